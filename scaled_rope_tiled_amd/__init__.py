@@ -1,0 +1,211 @@
+"""scaled_rope_tiled_amd: RoPE-scaled tiled causal attention for MI355X (gfx950).
+
+Thin Python binding over the C ABI of libsrt.so (include/srt.h).  Functions
+carry the same names as the C entry points without the ``srt_`` prefix and do
+argument marshalling only: torch tensors provide device memory and the current
+HIP stream; every step of the computation runs in the library's kernels.
+
+    rope_inv_freq(method, base, s, L, alpha, beta, D) -> (theta', mscale, band)
+    rope_cos_sin(theta', D, mscale, npos, device)     -> table [npos, D/2, 2] fp32
+    rope_apply(x, table, pos0=0, out=None)            -> rotated x
+    attn_prefill(q, k, v, ...)                        -> (out, lse)
+    attn_merge_states(o_a, lse_a, o_b, lse_b, ...)    -> (out, lse)
+    attn_decode_splitk(q, k_cache, v_cache, ...)      -> (out, lse)
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+
+import numpy as np
+import torch
+
+from . import _lib
+
+NONE, PI, NTK, YARN = 0, 1, 2, 3
+F32, BF16 = 0, 1
+ROTATE_Q, ROTATE_K = 1, 2
+BAND_LOW, BAND_MID, BAND_HIGH = 0, 1, 2
+
+__all__ = ["rope_inv_freq", "rope_cos_sin", "rope_apply", "attn_prefill", "attn_merge_states",
+           "attn_decode_splitk", "attn_decode_workspace_size", "NONE", "PI", "NTK", "YARN",
+           "ROTATE_Q", "ROTATE_K", "lib"]
+
+
+def lib():
+    return _lib.load()
+
+
+# Load at import: the binding has no fallback, a missing library is an error here.
+_lib.load()
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _tdt(code: int) -> torch.dtype:
+    return torch.float32 if code == F32 else torch.bfloat16
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _head_stride(t: torch.Tensor, name: str) -> int:
+    """Head stride of a [B][H][N][D] tensor whose rows are contiguous.
+
+    Allows views sliced along N (for ring chunks); requires D innermost,
+    rows D apart and batch stride = H * head stride."""
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, H, N, D]")
+    B, H, N, D = t.shape
+    sb, sh, sn, sd = t.stride()
+    if sd != 1 or (N > 1 and sn != D) or (B > 1 and sb != H * sh) or (H > 1 and sh < N * D):
+        raise ValueError(f"{name}: rows must be contiguous [B][H][N][D] (slices along N allowed)")
+    return sh if H > 1 else max(sh, N * D)
+
+
+def rope_inv_freq(method: int, base: float, s: float = 1.0, L: float = 0.0, alpha: float = 1.0,
+                  beta: float = 32.0, D: int = 128):
+    """Scaled RoPE frequencies (host, fp64).  Returns (theta' [D/2] float64, mscale, band [D/2] int8)."""
+    th = (C.c_double * (D // 2))()
+    ms = C.c_double()
+    band = (C.c_byte * (D // 2))()
+    _lib.check(lib().srt_rope_inv_freq(int(method), float(base), float(s), float(L), float(alpha),
+                                       float(beta), int(D), th, C.byref(ms), band), "rope_inv_freq")
+    return np.frombuffer(th, dtype=np.float64).copy(), ms.value, np.frombuffer(band, dtype=np.int8).copy()
+
+
+def rope_cos_sin(theta, D: int, mscale: float, npos: int, device="cuda") -> torch.Tensor:
+    """Device table [npos, D/2, 2] fp32 of mscale*(cos, sin)(p*theta'_i)."""
+    th = np.ascontiguousarray(np.asarray(theta, dtype=np.float64))
+    if th.shape != (D // 2,):
+        raise ValueError("theta must have D/2 entries")
+    dev = torch.device(device)
+    table = torch.empty((int(npos), D // 2, 2), dtype=torch.float32, device=dev)
+    _lib.check(lib().srt_rope_cos_sin(th.ctypes.data_as(C.POINTER(C.c_double)), int(D), float(mscale),
+                                      int(npos), _ptr(table), _stream(dev)), "rope_cos_sin")
+    return table
+
+
+def rope_apply(x: torch.Tensor, table: torch.Tensor, pos0: int = 0, out: torch.Tensor | None = None):
+    """Rotate every row of x [B, H, N, D] (row r at position pos0 + r).  out may be x."""
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    out = torch.empty_like(x) if out is None else out
+    if out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
+        raise ValueError("out must match x")
+    B, H, N, D = x.shape
+    _lib.check(lib().srt_rope_apply(_ptr(x), _ptr(out), _dt(x), B, H, N, D, int(pos0), _ptr(table),
+                                    table.shape[0], _stream(x.device)), "rope_apply")
+    return out
+
+
+def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, sm_scale: float | None = None,
+                 causal: bool = True, q_pos0: int = 0, k_pos0: int = 0, table: torch.Tensor | None = None,
+                 rope_flags: int | None = None, out: torch.Tensor | None = None,
+                 out_dtype: torch.dtype | None = None, lse: torch.Tensor | bool = True):
+    """Tiled causal attention with rotate-on-load RoPE.
+
+    q [B, Hq, Nq, D], k/v [B, Hkv, Nk, D] (views sliced along N allowed).
+    rope_flags defaults to ROTATE_Q|ROTATE_K when a table is given.
+    Returns (out [B, Hq, Nq, D], lse [B, Hq, Nq] fp32 or None)."""
+    B, Hq, Nq, D = q.shape
+    _, Hkv, Nk, _ = k.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("k and v must be [B, Hkv, Nk, D] matching q")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    qs, ks, vs = _head_stride(q, "q"), _head_stride(k, "k"), _head_stride(v, "v")
+    if ks != vs:
+        raise ValueError("k and v must have the same head stride")
+    if out is None:
+        out = torch.empty((B, Hq, Nq, D), dtype=out_dtype or q.dtype, device=q.device)
+    os_ = _head_stride(out, "out")
+    if lse is True:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    elif lse is False:
+        lse = None
+    ls = 0
+    if lse is not None:
+        if lse.dtype != torch.float32 or lse.stride(-1) != 1 or (Hq > 1 and lse.stride(1) < Nq):
+            raise ValueError("lse must be fp32 [B, Hq, Nq] with rows contiguous")
+        ls = lse.stride(1) if Hq > 1 else max(lse.stride(1), Nq)
+    if rope_flags is None:
+        rope_flags = (ROTATE_Q | ROTATE_K) if table is not None else 0
+    sm = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
+    _lib.check(lib().srt_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _dt(q), B, Hq, Hkv, Nq, Nk, D,
+                                      qs, ks, int(q_pos0), int(k_pos0), int(bool(causal)), sm,
+                                      _ptr(table), 0 if table is None else table.shape[0], int(rope_flags),
+                                      _ptr(out), _dt(out), os_, _ptr(lse), ls, _stream(q.device)),
+               "attn_prefill")
+    return out, lse
+
+
+def attn_merge_states(o_a, lse_a, o_b, lse_b, *, out=None, lse_out=None, out_dtype=None):
+    """Log-sum-exp merge of two partial states.  out may be o_a (in place)."""
+    B, H, N, D = o_a.shape
+    if o_b.shape != o_a.shape or o_b.dtype != o_a.dtype:
+        raise ValueError("o_a and o_b must match")
+    ia, ib = _head_stride(o_a, "o_a"), _head_stride(o_b, "o_b")
+    if ia != ib:
+        raise ValueError("o_a and o_b must have the same head stride")
+    for t in (lse_a, lse_b):
+        if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (B, H, N):
+            raise ValueError("lse_a / lse_b must be contiguous fp32 [B, H, N]")
+    if out is None:
+        out = torch.empty((B, H, N, D), dtype=out_dtype or o_a.dtype, device=o_a.device)
+    os_ = _head_stride(out, "out")
+    if lse_out is None:
+        lse_out = torch.empty((B, H, N), dtype=torch.float32, device=o_a.device)
+    ls = lse_out.stride(1) if H > 1 else max(lse_out.stride(1), N)
+    _lib.check(lib().srt_attn_merge_states(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _dt(o_a), ia,
+                                           _ptr(out), _dt(out), os_, _ptr(lse_out), ls, B, H, N, D,
+                                           _stream(o_a.device)), "attn_merge_states")
+    return out, lse_out
+
+
+def attn_decode_workspace_size(B: int, Hq: int, D: int, num_splits: int) -> int:
+    n = C.c_size_t()
+    _lib.check(lib().srt_attn_decode_workspace_size(B, Hq, D, num_splits, C.byref(n)),
+               "attn_decode_workspace_size")
+    return n.value
+
+
+def attn_decode_splitk(q, k_cache, v_cache, *, num_splits: int, sm_scale: float | None = None,
+                       table: torch.Tensor | None = None, seq_lens: torch.Tensor | None = None,
+                       workspace: torch.Tensor | None = None, out=None, lse=True):
+    """Split-K decode.  q [B, Hq, D] raw (rotated at seq_len-1 when a table is given);
+    k_cache/v_cache [B, Hkv, Nk, D] with rotated keys.  Returns (out [B, Hq, D], lse [B, Hq])."""
+    B, Hq, D = q.shape
+    _, Hkv, Nk, _ = k_cache.shape
+    for t in (q, k_cache, v_cache):
+        if not t.is_contiguous():
+            raise ValueError("decode tensors must be contiguous")
+    need = attn_decode_workspace_size(B, Hq, D, num_splits)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=q.dtype, device=q.device)
+    if lse is True:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    elif lse is False:
+        lse = None
+    if seq_lens is not None and (seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous()):
+        raise ValueError("seq_lens must be contiguous int32 [B]")
+    sm = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
+    _lib.check(lib().srt_attn_decode_splitk(_ptr(q), _ptr(k_cache), _ptr(v_cache), _dt(q), B, Hq, Hkv, Nk, D,
+                                            _ptr(seq_lens), int(num_splits), sm, _ptr(table),
+                                            0 if table is None else table.shape[0], _ptr(workspace),
+                                            workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
+                                            _stream(q.device)), "attn_decode_splitk")
+    return out, lse

@@ -1,0 +1,252 @@
+// C-ABI layer of libsrt: argument checks on the host, the fp64 frequency step,
+// and dispatch to the kernel launchers.  No exception crosses the ABI.
+#include "../../include/srt.h"
+#include "srt_internal.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return SRT_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SRT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool valid_dtype(int d) { return d == SRT_F32 || d == SRT_BF16; }
+
+bool misaligned16(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
+constexpr double kTwoPi = 6.283185307179586476925286766559;
+
+}  // namespace
+
+extern "C" {
+
+int srt_abi_version(void) { return 1; }
+
+const char* srt_status_string(int status) {
+  switch (status) {
+    case SRT_OK: return "ok";
+    case SRT_ERR_INVALID: return "invalid argument";
+    case SRT_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case SRT_ERR_HIP: return "HIP runtime error";
+    case SRT_ERR_WORKSPACE: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+const char* srt_last_error(void) { return g_err; }
+
+// Frequency step: "Long Context: RoPE / YaRN / NTK / MLA" §2.1 (base
+// frequencies), §4.2 (PI), §5.2 (NTK-aware base), §6.2-6.4 (NTK-by-parts ramp
+// and temperature); band labels from "8.3 长上下文技术" §8.3.3.
+int srt_rope_inv_freq(int method, double base, double s, double L, double alpha, double beta, int D,
+                      double* inv_freq_out, double* mscale_out, signed char* band_out) {
+  if (!inv_freq_out) return fail(SRT_ERR_INVALID, "rope_inv_freq: inv_freq_out is NULL");
+  if (D < 2 || D > 2 * srt::kMaxHalf || (D & 1))
+    return fail(SRT_ERR_INVALID, "rope_inv_freq: D=%d must be even and in [2, %d]", D, 2 * srt::kMaxHalf);
+  if (!(base > 0.0) || !std::isfinite(base)) return fail(SRT_ERR_INVALID, "rope_inv_freq: base must be > 0");
+  if (method < SRT_ROPE_NONE || method > SRT_ROPE_YARN)
+    return fail(SRT_ERR_INVALID, "rope_inv_freq: unknown method %d", method);
+  if (method != SRT_ROPE_NONE && (!(s > 0.0) || !std::isfinite(s)))
+    return fail(SRT_ERR_INVALID, "rope_inv_freq: scale s must be > 0");
+  if (method == SRT_ROPE_NTK && D <= 2) return fail(SRT_ERR_INVALID, "rope_inv_freq: NTK needs D > 2");
+  if (method == SRT_ROPE_YARN) {
+    if (!(L > 0.0) || !std::isfinite(L)) return fail(SRT_ERR_INVALID, "rope_inv_freq: YaRN needs L > 0");
+    if (!(beta > alpha)) return fail(SRT_ERR_INVALID, "rope_inv_freq: YaRN needs beta > alpha");
+  }
+  const int half = D / 2;
+  double mscale = 1.0;
+  // NTK-aware: new base b' = b * s^(D/(D-2)), exponent formed in fp64.
+  const double b_eff = (method == SRT_ROPE_NTK) ? base * std::pow(s, (double)D / (double)(D - 2)) : base;
+  for (int d = 0; d < half; ++d) {
+    const double th = std::pow(b_eff, -2.0 * (double)d / (double)D);
+    double out = th;
+    signed char band = SRT_BAND_HIGH;
+    switch (method) {
+      case SRT_ROPE_NONE: break;
+      case SRT_ROPE_PI: out = th / s; band = SRT_BAND_LOW; break;
+      case SRT_ROPE_NTK: band = SRT_BAND_MID; break;
+      case SRT_ROPE_YARN: {
+        const double r = L * th / kTwoPi;                 // turns within the training length
+        double w = (r - alpha) / (beta - alpha);          // ramp, clipped to [0, 1]
+        w = w < 0.0 ? 0.0 : (w > 1.0 ? 1.0 : w);
+        out = (1.0 - w) * (th / s) + w * th;
+        band = r > beta ? SRT_BAND_HIGH : (r < alpha ? SRT_BAND_LOW : SRT_BAND_MID);
+        break;
+      }
+    }
+    inv_freq_out[d] = out;
+    if (band_out) band_out[d] = band;
+  }
+  if (method == SRT_ROPE_YARN && s > 1.0) mscale = 0.1 * std::log(s) + 1.0;
+  if (mscale_out) *mscale_out = mscale;
+  return ok();
+}
+
+int srt_rope_cos_sin(const double* inv_freq_host, int D, double mscale, long long npos, float* table_dev,
+                     void* stream) {
+  if (!inv_freq_host || !table_dev) return fail(SRT_ERR_INVALID, "rope_cos_sin: NULL pointer");
+  if (D < 2 || D > 2 * srt::kMaxHalf || (D & 1)) return fail(SRT_ERR_INVALID, "rope_cos_sin: bad D=%d", D);
+  if (npos < 1 || npos > (1LL << 31)) return fail(SRT_ERR_INVALID, "rope_cos_sin: npos=%lld out of range", npos);
+  if (!std::isfinite(mscale)) return fail(SRT_ERR_INVALID, "rope_cos_sin: mscale not finite");
+  srt::Theta th{};
+  for (int i = 0; i < D / 2; ++i) {
+    if (!std::isfinite(inv_freq_host[i])) return fail(SRT_ERR_INVALID, "rope_cos_sin: theta[%d] not finite", i);
+    th.v[i] = inv_freq_host[i];
+  }
+  return hip_status(srt::launch_rope_table(th, D / 2, mscale, npos, table_dev, (hipStream_t)stream),
+                    "rope_cos_sin launch");
+}
+
+int srt_rope_apply(const void* x, void* y, int dtype, int B, int H, int N, int D, long long pos0,
+                   const float* table_dev, long long table_npos, void* stream) {
+  if (!valid_dtype(dtype)) return fail(SRT_ERR_INVALID, "rope_apply: bad dtype %d", dtype);
+  if (B < 0 || H < 0 || N < 0) return fail(SRT_ERR_INVALID, "rope_apply: negative size");
+  if ((long long)B * H * N == 0) return ok();   // nothing to rotate: pointers may be NULL
+  if (!x || !y || !table_dev) return fail(SRT_ERR_INVALID, "rope_apply: NULL pointer");
+  if (D < 2 || (D & 1) || D > 2 * srt::kMaxHalf) return fail(SRT_ERR_INVALID, "rope_apply: bad D=%d", D);
+  if (D % 8) return fail(SRT_ERR_UNSUPPORTED, "rope_apply: D=%d must be a multiple of 8", D);
+  if (pos0 < 0 || pos0 + N > table_npos)
+    return fail(SRT_ERR_INVALID, "rope_apply: positions [%lld, %lld) outside table [0, %lld)", pos0,
+                pos0 + N, table_npos);
+  if (misaligned16(x) || misaligned16(y) || misaligned16(table_dev))
+    return fail(SRT_ERR_INVALID, "rope_apply: pointers must be 16-byte aligned");
+  return hip_status(srt::launch_rope_apply(x, y, dtype == SRT_BF16, (long long)B * H, N, D, pos0, table_dev,
+                                           (hipStream_t)stream),
+                    "rope_apply launch");
+}
+
+int srt_attn_prefill(const void* q, const void* k, const void* v, int dtype, int B, int Hq, int Hkv, int Nq,
+                     int Nk, int D, long long q_hstride, long long kv_hstride, long long q_pos0,
+                     long long k_pos0, int causal, float sm_scale, const float* table_dev,
+                     long long table_npos, int rope_flags, void* out, int out_dtype, long long o_hstride,
+                     float* lse, long long lse_hstride, void* stream) {
+  if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return fail(SRT_ERR_INVALID, "attn_prefill: bad dtype");
+  if (B < 0 || Hq < 1 || Hkv < 1 || Nq < 0 || Nk < 0) return fail(SRT_ERR_INVALID, "attn_prefill: bad sizes");
+  if ((long long)B * Nq == 0) return ok();     // no query row: nothing to write, pointers may be NULL
+  if (!q || !out) return fail(SRT_ERR_INVALID, "attn_prefill: NULL q or out");
+  if (Nk > 0 && (!k || !v)) return fail(SRT_ERR_INVALID, "attn_prefill: NULL k or v");
+  if (Hq % Hkv) return fail(SRT_ERR_INVALID, "attn_prefill: Hq=%d not a multiple of Hkv=%d", Hq, Hkv);
+  if (D < 2 || (D & 1)) return fail(SRT_ERR_INVALID, "attn_prefill: D=%d must be even", D);
+  if (q_hstride < (long long)Nq * D || kv_hstride < (long long)Nk * D || o_hstride < (long long)Nq * D)
+    return fail(SRT_ERR_INVALID, "attn_prefill: head stride smaller than N*D");
+  if (lse && lse_hstride < Nq) return fail(SRT_ERR_INVALID, "attn_prefill: lse head stride smaller than Nq");
+  if (rope_flags & ~(SRT_ROTATE_Q | SRT_ROTATE_K)) return fail(SRT_ERR_INVALID, "attn_prefill: bad rope_flags");
+  if (rope_flags && !table_dev) return fail(SRT_ERR_INVALID, "attn_prefill: rope_flags set without a table");
+  if (q_pos0 < 0 || k_pos0 < 0) return fail(SRT_ERR_INVALID, "attn_prefill: negative position offset");
+  if ((rope_flags & SRT_ROTATE_Q) && q_pos0 + Nq > table_npos)
+    return fail(SRT_ERR_INVALID, "attn_prefill: q positions [%lld, %lld) outside table [0, %lld)", q_pos0,
+                q_pos0 + Nq, table_npos);
+  if ((rope_flags & SRT_ROTATE_K) && k_pos0 + Nk > table_npos)
+    return fail(SRT_ERR_INVALID, "attn_prefill: k positions [%lld, %lld) outside table [0, %lld)", k_pos0,
+                k_pos0 + Nk, table_npos);
+  if (!std::isfinite(sm_scale)) return fail(SRT_ERR_INVALID, "attn_prefill: sm_scale not finite");
+  if (Nq > (1 << 30) || Nk > (1 << 30)) return fail(SRT_ERR_UNSUPPORTED, "attn_prefill: N above 2^30");
+  srt::PrefillArgs a{};
+  a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.table = table_dev;
+  a.q_hstride = q_hstride; a.kv_hstride = kv_hstride; a.o_hstride = o_hstride; a.lse_hstride = lse_hstride;
+  a.q_pos0 = q_pos0; a.k_pos0 = k_pos0;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.D = D;
+  a.causal = causal ? 1 : 0; a.rope_flags = rope_flags; a.out_bf16 = out_dtype == SRT_BF16;
+  a.sm_scale = sm_scale;
+  if (dtype == SRT_BF16) {
+    if (D != 128) return fail(SRT_ERR_UNSUPPORTED, "attn_prefill: bf16 kernel needs D = 128 (got %d)", D);
+    return hip_status(srt::launch_prefill_bf16_d128(a, (hipStream_t)stream), "attn_prefill bf16 launch");
+  }
+  if (D != 64 && D != 128) return fail(SRT_ERR_UNSUPPORTED, "attn_prefill: fp32 kernel needs D in {64,128}");
+  return hip_status(srt::launch_prefill_f32(a, (hipStream_t)stream), "attn_prefill fp32 launch");
+}
+
+int srt_attn_merge_states(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                          int in_dtype, long long in_hstride, void* o_out, int out_dtype, long long out_hstride,
+                          float* lse_out, long long lse_out_hstride, int B, int H, int N, int D, void* stream) {
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return fail(SRT_ERR_INVALID, "attn_merge_states: bad dtype");
+  if (B < 0 || H < 0 || N < 0) return fail(SRT_ERR_INVALID, "attn_merge_states: negative size");
+  if ((long long)B * H * N == 0) return ok();  // nothing to merge: pointers may be NULL
+  if (!o_a || !lse_a || !o_b || !lse_b || !o_out) return fail(SRT_ERR_INVALID, "attn_merge_states: NULL pointer");
+  if (D < 8 || D > 512 || (D & (D - 1)))
+    return fail(SRT_ERR_UNSUPPORTED, "attn_merge_states: D=%d must be a power of two in [8, 512]", D);
+  if (in_hstride < (long long)N * D || out_hstride < (long long)N * D)
+    return fail(SRT_ERR_INVALID, "attn_merge_states: head stride smaller than N*D");
+  if (lse_out && lse_out_hstride < N) return fail(SRT_ERR_INVALID, "attn_merge_states: lse_out stride < N");
+  if (o_out == o_a && (out_dtype != in_dtype || out_hstride != in_hstride))
+    return fail(SRT_ERR_INVALID, "attn_merge_states: in-place merge needs equal dtype and stride");
+  if (misaligned16(o_a) || misaligned16(o_b) || misaligned16(o_out))
+    return fail(SRT_ERR_INVALID, "attn_merge_states: tensors must be 16-byte aligned");
+  if ((in_hstride % 8) || (out_hstride % 8))
+    return fail(SRT_ERR_INVALID, "attn_merge_states: head strides must be multiples of 8 elements");
+  srt::MergeArgs a{};
+  a.oa = o_a; a.la = lse_a; a.ob = o_b; a.lb = lse_b; a.oo = o_out; a.lo = lse_out;
+  a.in_hstride = in_hstride; a.out_hstride = out_hstride; a.lse_out_hstride = lse_out_hstride;
+  a.BH = B * H; a.N = N; a.D = D; a.in_bf16 = in_dtype == SRT_BF16; a.out_bf16 = out_dtype == SRT_BF16;
+  return hip_status(srt::launch_merge(a, (hipStream_t)stream), "attn_merge_states launch");
+}
+
+int srt_attn_decode_workspace_size(int B, int Hq, int D, int num_splits, size_t* bytes_out) {
+  if (!bytes_out) return fail(SRT_ERR_INVALID, "attn_decode_workspace_size: NULL output");
+  if (B < 0 || Hq < 1 || D < 2 || num_splits < 1 || num_splits > 1024)
+    return fail(SRT_ERR_INVALID, "attn_decode_workspace_size: bad sizes");
+  *bytes_out = srt::decode_workspace_bytes(B, Hq, D, num_splits);
+  return ok();
+}
+
+int srt_attn_decode_splitk(const void* q, const void* k_cache, const void* v_cache, int dtype, int B, int Hq,
+                           int Hkv, int Nk, int D, const int* seq_lens_dev, int num_splits, float sm_scale,
+                           const float* table_dev, long long table_npos, void* workspace,
+                           size_t workspace_bytes, void* out, float* lse, void* stream) {
+  if (!valid_dtype(dtype)) return fail(SRT_ERR_INVALID, "attn_decode_splitk: bad dtype");
+  if (B < 0 || Hq < 1 || Hkv < 1 || Nk < 0) return fail(SRT_ERR_INVALID, "attn_decode_splitk: bad sizes");
+  if (B == 0) return ok();                     // no sequence: pointers may be NULL
+  if (!q || !out) return fail(SRT_ERR_INVALID, "attn_decode_splitk: NULL q or out");
+  if (Nk > 0 && (!k_cache || !v_cache)) return fail(SRT_ERR_INVALID, "attn_decode_splitk: NULL cache pointer");
+  if (Hq % Hkv) return fail(SRT_ERR_INVALID, "attn_decode_splitk: Hq not a multiple of Hkv");
+  if (num_splits < 1 || num_splits > 1024) return fail(SRT_ERR_INVALID, "attn_decode_splitk: num_splits out of [1,1024]");
+  if (D < 2 || (D & 1)) return fail(SRT_ERR_INVALID, "attn_decode_splitk: D must be even");
+  if (table_dev && table_npos < Nk)
+    return fail(SRT_ERR_INVALID, "attn_decode_splitk: table has %lld positions, query may sit at %d", table_npos, Nk - 1);
+  if (!std::isfinite(sm_scale)) return fail(SRT_ERR_INVALID, "attn_decode_splitk: sm_scale not finite");
+  if (dtype != SRT_BF16 || D != 128)
+    return fail(SRT_ERR_UNSUPPORTED, "attn_decode_splitk: kernel needs bf16 and D = 128");
+  {
+    const int g = Hq / Hkv;
+    if (g != 1 && g != 2 && g != 4 && g != 8)
+      return fail(SRT_ERR_UNSUPPORTED, "attn_decode_splitk: Hq/Hkv=%d must be 1, 2, 4 or 8", g);
+  }
+  if (misaligned16(q) || misaligned16(k_cache) || misaligned16(v_cache) || misaligned16(table_dev))
+    return fail(SRT_ERR_INVALID, "attn_decode_splitk: tensors must be 16-byte aligned");
+  const size_t need = srt::decode_workspace_bytes(B, Hq, D, num_splits);
+  if (B > 0 && (!workspace || workspace_bytes < need))
+    return fail(SRT_ERR_WORKSPACE, "attn_decode_splitk: workspace %zu bytes, need %zu", workspace_bytes, need);
+  if (((uintptr_t)workspace) & 15) return fail(SRT_ERR_INVALID, "attn_decode_splitk: workspace not 16-byte aligned");
+  if (B == 0) return ok();
+  srt::DecodeArgs a{};
+  a.q = q; a.k = k_cache; a.v = v_cache; a.seq_lens = seq_lens_dev; a.table = table_dev;
+  a.ws_o = (float*)workspace;
+  a.ws_lse = (float*)((char*)workspace + (size_t)B * Hq * num_splits * D * sizeof(float));
+  a.out = out; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nk = Nk; a.D = D; a.splits = num_splits;
+  a.split_len = Nk > 0 ? (Nk + num_splits - 1) / num_splits : 0;
+  a.sm_scale = sm_scale;
+  return hip_status(srt::launch_decode(a, (hipStream_t)stream), "attn_decode_splitk launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,253 @@
+// Split-K decode: one new query token per sequence against a rotated bf16
+// KV cache [B][Hkv][Nk][128].
+//
+// Every decode step streams the whole K/V cache from HBM ("Long Context: RoPE
+// / YaRN / NTK / MLA" §12.3), so the kernel is bound by HBM bandwidth.  The
+// cache rows [0, seq_len) of a sequence are cut into `splits` blocks; one
+// workgroup reads one block of one KV head exactly once (K and V in the same
+// pass) and serves all query heads of that GQA group from registers.  The
+// partial results (O_s, lse_s) are merged by a second, tiny kernel with the
+// log-sum-exp rule, the same online-softmax combination the pages use for
+// Ring / Star Attention partial results ("8.3 长上下文技术" §8.3.5-8.3.6).
+//
+// Lane layout: 8 lanes share one cache row.  Lane `sub` of a row loads the
+// 16-byte chunks sub and sub+8 (dims 8*sub..8*sub+7 and 64+8*sub..), so each
+// load instruction of a wave reads 8 whole 128-byte row halves.  The q.k dot
+// is 4 bf16 dot2 instructions per chunk and head, finished by a 3-step
+// butterfly inside the 8 lanes.  Each lane keeps a private online softmax over
+// its rows (running max m, sum l, accumulator of its 16 dims per head) and only
+// rescales when a score exceeds its running max by more than 2^8 (the result is
+// exact for any choice of m; the bound only keeps e^(s-m) <= 2^8).  Partial
+// states are merged across lanes and waves once at the end.
+#include "srt_internal.h"
+
+namespace srt {
+namespace {
+
+constexpr int kD = 128;
+constexpr int kThreads = 256;
+constexpr int kLanesPerRow = 8;
+constexpr int kRowsPerIter = kThreads / kLanesPerRow;   // 32
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.0f;                           // rescale threshold in log2 units
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+
+__device__ inline float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float hi_f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ inline uint32_t pack2(float a, float b) {
+  return (uint32_t)__bfloat16_as_ushort(__float2bfloat16(a)) |
+         ((uint32_t)__bfloat16_as_ushort(__float2bfloat16(b)) << 16);
+}
+
+__device__ inline float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                         false);
+}
+
+template <int G>
+__global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a) {
+  const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sub = tid & (kLanesPerRow - 1);
+  const int rgroup = tid / kLanesPerRow;                 // 0..31
+  int seq = a.seq_lens ? a.seq_lens[b] : a.Nk;
+  seq = seq < 0 ? 0 : (seq > a.Nk ? a.Nk : seq);
+  const int lo = split * a.split_len;
+  const int hi = min(seq, lo + a.split_len);
+  const int h0 = hk * G;
+  float* ws_o = a.ws_o + (((long long)b * a.Hq + h0) * a.splits + split) * kD;
+  float* ws_l = a.ws_lse + ((long long)b * a.Hq + h0) * a.splits + split;
+
+  __shared__ float red_m[4][G];
+  __shared__ float red_l[4][G];
+  __shared__ float red_o[4][G][kD];
+
+  if (lo >= hi) {   // empty block of this sequence: identity state
+    for (int e = tid; e < G * kD; e += kThreads) ws_o[(long long)(e / kD) * a.splits * kD + e % kD] = 0.f;
+    if (tid < G) ws_l[(long long)tid * a.splits] = -INFINITY;
+    return;
+  }
+
+  // ---- q of the G heads: rotate at position seq-1, fold sm_scale*log2(e), pack to bf16 pairs
+  const long long qpos = seq - 1;
+  const float qs = a.sm_scale * kLog2e;
+  uint32_t qp[G][8];       // [head][chunk c (0: dims 8sub.., 1: dims 64+8sub..) * 4 + pair-in-chunk]
+  const uint4* qg = reinterpret_cast<const uint4*>(a.q);
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int chunk = sub + 8 * c;                     // 16-byte chunk index within the row
+      const uint4 w = qg[((long long)b * a.Hq + h0 + j) * (kD / 8) + chunk];
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        float x0 = lo_f(ww[p]), x1 = hi_f(ww[p]);
+        if (a.table) {
+          const float2 cs = reinterpret_cast<const float2*>(a.table)[qpos * (kD / 2) + chunk * 4 + p];
+          const float t0 = x0 * cs.x - x1 * cs.y, t1 = x0 * cs.y + x1 * cs.x;
+          x0 = t0; x1 = t1;
+        }
+        qp[j][c * 4 + p] = pack2(x0 * qs, x1 * qs);
+      }
+    }
+  }
+
+  float m[G], l[G], acc[G][16];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    m[j] = -INFINITY; l[j] = 0.f;
+#pragma unroll
+    for (int d = 0; d < 16; ++d) acc[j][d] = 0.f;
+  }
+
+  const long long row_base = ((long long)b * a.Hkv + hk) * a.Nk;
+  const uint4* kg = reinterpret_cast<const uint4*>(a.k) + row_base * (kD / 8);
+  const uint4* vg = reinterpret_cast<const uint4*>(a.v) + row_base * (kD / 8);
+
+  constexpr int kUnroll = 2;
+  for (int r0 = lo; r0 < hi; r0 += kRowsPerIter * kUnroll) {
+    uint4 kw[kUnroll][2], vw[kUnroll][2];
+    bool valid[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int row = r0 + u * kRowsPerIter + rgroup;
+      valid[u] = row < hi;
+      const long long off = (long long)(valid[u] ? row : lo) * (kD / 8);
+      kw[u][0] = kg[off + sub];
+      kw[u][1] = kg[off + sub + 8];
+      vw[u][0] = vg[off + sub];
+      vw[u][1] = vg[off + sub + 8];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t kk[8] = {kw[u][0].x, kw[u][0].y, kw[u][0].z, kw[u][0].w,
+                              kw[u][1].x, kw[u][1].y, kw[u][1].z, kw[u][1].w};
+      float s[G];
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        float t = 0.f;
+#pragma unroll
+        for (int p = 0; p < 8; ++p) t = dot2(qp[j][p], kk[p], t);
+        t += __shfl_xor(t, 1, 8);
+        t += __shfl_xor(t, 2, 8);
+        t += __shfl_xor(t, 4, 8);
+        s[j] = valid[u] ? t : -INFINITY;
+      }
+      const uint32_t vv[8] = {vw[u][0].x, vw[u][0].y, vw[u][0].z, vw[u][0].w,
+                              vw[u][1].x, vw[u][1].y, vw[u][1].z, vw[u][1].w};
+      float vf[16];
+#pragma unroll
+      for (int p = 0; p < 8; ++p) { vf[2 * p] = lo_f(vv[p]); vf[2 * p + 1] = hi_f(vv[p]); }
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        if (s[j] > m[j] + kLazy) {          // rare: raise the running max
+          const float sc = exp2f(m[j] - s[j]);
+          l[j] *= sc;
+#pragma unroll
+          for (int d = 0; d < 16; ++d) acc[j][d] *= sc;
+          m[j] = s[j];
+        }
+        const float p = valid[u] ? exp2f(s[j] - m[j]) : 0.f;
+        l[j] += p;
+#pragma unroll
+        for (int d = 0; d < 16; ++d) acc[j][d] = fmaf(p, vf[d], acc[j][d]);
+      }
+    }
+  }
+
+  // ---- merge the per-lane states: lanes of one row group hold the same (m, l);
+  // reduce over the 8 row groups of a wave, then over the 4 waves.
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    float M = m[j];
+    M = fmaxf(M, __shfl_xor(M, 8));
+    M = fmaxf(M, __shfl_xor(M, 16));
+    M = fmaxf(M, __shfl_xor(M, 32));
+    const float sc = (m[j] == -INFINITY) ? 0.f : exp2f(m[j] - M);
+    float L = l[j] * sc;
+    L += __shfl_xor(L, 8);
+    L += __shfl_xor(L, 16);
+    L += __shfl_xor(L, 32);
+#pragma unroll
+    for (int d = 0; d < 16; ++d) {
+      float x = acc[j][d] * sc;
+      x += __shfl_xor(x, 8);
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      acc[j][d] = x;
+    }
+    if (lane < kLanesPerRow) {
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        red_o[wave][j][8 * sub + d] = acc[j][d];
+        red_o[wave][j][64 + 8 * sub + d] = acc[j][8 + d];
+      }
+    }
+    if (lane == 0) { red_m[wave][j] = M; red_l[wave][j] = L; }
+  }
+  __syncthreads();
+  for (int e = tid; e < G * kD; e += kThreads) {
+    const int j = e / kD, d = e % kD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w][j]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float sc = red_m[w][j] == -INFINITY ? 0.f : exp2f(red_m[w][j] - M);
+      L += red_l[w][j] * sc;
+      O += red_o[w][j][d] * sc;
+    }
+    ws_o[(long long)j * a.splits * kD + d] = L > 0.f ? O / L : 0.f;
+    if (d == 0) ws_l[(long long)j * a.splits] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  }
+}
+
+// Merge the `splits` partial states of one (b, h): lse-weighted average.
+__global__ void __launch_bounds__(128) decode_combine_kernel(DecodeArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const long long bh = (long long)b * a.Hq + h;
+  const float* pl = a.ws_lse + bh * a.splits;
+  const float* po = a.ws_o + bh * a.splits * kD;
+  float M = -INFINITY;
+  for (int s = 0; s < a.splits; ++s) M = fmaxf(M, pl[s]);
+  float L = 0.f, O = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < a.splits; ++s) {
+      const float w = __expf(pl[s] - M);
+      L += w;
+      O = fmaf(w, po[(long long)s * kD + d], O);
+    }
+  }
+  reinterpret_cast<__hip_bfloat16*>(a.out)[bh * kD + d] = __float2bfloat16(L > 0.f ? O / L : 0.f);
+  if (a.lse && d == 0) a.lse[bh] = L > 0.f ? M + __logf(L) : -INFINITY;
+}
+
+}  // namespace
+
+size_t decode_workspace_bytes(int B, int Hq, int D, int splits) {
+  return (size_t)B * Hq * splits * (size_t)(D + 1) * sizeof(float);
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  if (a.D != kD) return hipErrorInvalidValue;
+  const int G = a.Hq / a.Hkv;
+  const dim3 grid(a.splits, a.Hkv, a.B), block(kThreads);
+  switch (G) {
+    case 1: hipLaunchKernelGGL(decode_split_kernel<1>, grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(decode_split_kernel<2>, grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(decode_split_kernel<4>, grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL(decode_split_kernel<8>, grid, block, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(a.Hq, a.B), dim3(kD), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace srt

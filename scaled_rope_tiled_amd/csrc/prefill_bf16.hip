@@ -1,0 +1,357 @@
+// bf16 tiled online-softmax attention, D = 128, on the gfx950 matrix cores.
+//
+// What it computes is FlashAttention's exact tiled softmax ("8.3 长上下文技术"
+// §8.3.4: tiles of Q, K, V in on-chip memory, per-block max and exp-sum, the
+// earlier accumulator rescaled; the N x N matrix never exists), with RoPE
+// applied to q and k as they are loaded ("Long Context: RoPE / YaRN / NTK /
+// MLA" §2.4 rope_attention; the YaRN temperature travels in the table, §6.4).
+//
+// Work decomposition (one workgroup = 4 waves = 256 threads)
+//   * A workgroup owns one KV head and 64 * (4 / HPW) query rows of HPW query
+//     heads of its GQA group (HPW = min(Hq/Hkv, 4)): the K/V tiles staged in
+//     LDS are shared by all four waves, i.e. by up to four query heads.
+//   * Wave w owns 64 query rows of one head and keeps them in registers:
+//     rotated q as the B operand of S^T = K Q^T, the output as O^T (fp32).
+//   * The grid's x index is the KV head (fastest), so consecutive workgroups,
+//     which the dispatcher spreads round-robin over the 8 XCDs, keep one head
+//     per XCD L2; the y index walks query tiles from the last (most keys under
+//     the causal mask) to the first, so the long tiles start first.
+//   * Key tiles wholly above the causal diagonal are never visited; only tiles
+//     that cross the diagonal (or the ragged end of K) evaluate the mask.
+//
+// Matrix-core mapping (v_mfma_f32_32x32x16_bf16, wave64)
+//   S^T[keys][queries] = K[keys][d] Q^T[d][queries]: A = 32x16 block of K read
+//   from LDS (16 bytes per lane), B = Q^T from registers; the accumulator puts
+//   one query per lane (lane & 31) with 16 of its keys, so the row max and row
+//   sum of the softmax are in-lane, plus one exchange with lane ^ 32.
+//   O^T[d][queries] = V^T[d][keys] P^T[keys][queries]: B = P^T comes straight
+//   from the S^T accumulator (converted to bf16) because the contraction over
+//   keys may use any key order as long as A uses the same one; A = V^T is read
+//   from the row-major V tile with the gfx950 transposing LDS read
+//   ds_read_b64_tr_b16, four consecutive keys of one d column per read.
+//   The O^T accumulator again holds one query per lane, so the online-softmax
+//   rescale is a per-lane multiply.  The rescale runs only when a row maximum
+//   grows by more than 2^8 (exact for any reference maximum; the bound keeps
+//   e^(s - m) <= 2^8 so bf16/fp32 stay far from overflow).
+//
+// Staging: each thread moves four 16-byte chunks of K and of V per 64-key
+// tile (16 threads per 256-byte row: fully coalesced), rotating K in fp32 on
+// the way when asked.  LDS is double-buffered: the next tile's global loads are
+// issued before the current tile's matrix work and stored after it, one
+// barrier per tile.  Row strides are padded (K: 272 B, V: 320 B) so the 16-byte
+// K reads and the transposing V reads of a wave hit distinct LDS banks.
+#include "srt_internal.h"
+
+namespace srt {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kD = 128;
+constexpr int kBM = 64;           // query rows per wave
+constexpr int kBN = 64;           // keys per tile
+constexpr int kKStr = kD + 8;     // K tile row stride (bf16 elements) = 272 B
+constexpr int kVStr = kD + 32;    // V tile row stride (bf16 elements) = 320 B
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.0f;     // rescale threshold (log2 units)
+
+struct Smem {
+  __hip_bfloat16 k[2][kBN * kKStr];
+  __hip_bfloat16 v[2][kBN * kVStr];
+};
+
+__device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ inline uint32_t pack2(float a, float b) {
+  return (uint32_t)__bfloat16_as_ushort(__float2bfloat16(a)) |
+         ((uint32_t)__bfloat16_as_ushort(__float2bfloat16(b)) << 16);
+}
+
+// Rotate the 4 pairs of a 16-byte bf16 chunk with 4 (cos, sin) table entries.
+__device__ inline uint4 rotate_chunk(uint4 w, float4 t0, float4 t1) {
+  const uint32_t in[4] = {w.x, w.y, w.z, w.w};
+  const float c[4] = {t0.x, t0.z, t1.x, t1.z};
+  const float s[4] = {t0.y, t0.w, t1.y, t1.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float x0 = bf_lo(in[i]), x1 = bf_hi(in[i]);
+    o[i] = pack2(x0 * c[i] - x1 * s[i], x0 * s[i] + x1 * c[i]);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+__device__ inline bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(bf16x8, w); }
+
+// gfx950 transposing LDS read: each lane fetches 8 bytes at its address, then
+// within every 16 lanes, lane i receives element (i & 3) of the values fetched
+// by lanes 4t + (i >> 2), t = 0..3.
+__device__ inline i16x4 ds_read_tr(const __hip_bfloat16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+template <bool ROT_K>
+__global__ void __launch_bounds__(256, 1) prefill_bf16_kernel(PrefillArgs a) {
+  __shared__ Smem sm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int G = a.Hq / a.Hkv;
+  const int HPW = G < 4 ? G : 4;                 // query heads per workgroup
+  const int RB = 4 / HPW;                        // 64-row blocks per workgroup
+  const int quads = G > 4 ? G / 4 : 1;
+  const int hk = blockIdx.x / quads;
+  const int quad = blockIdx.x - hk * quads;
+  const int b = blockIdx.z;
+  const int ntiles_q = gridDim.y;
+  const int qt = a.causal ? (ntiles_q - 1 - (int)blockIdx.y) : (int)blockIdx.y;
+  const int hq = hk * G + quad * 4 + (wave % HPW);
+  const int wrow0 = qt * (kBM * RB) + (wave / HPW) * kBM;     // first query row of this wave
+  const int wg_row_last = min(a.Nq, (qt + 1) * kBM * RB) - 1;  // last valid row of the workgroup
+
+  const __hip_bfloat16* qg = reinterpret_cast<const __hip_bfloat16*>(a.q) + ((long long)b * a.Hq + hq) * a.q_hstride;
+  const __hip_bfloat16* kg = reinterpret_cast<const __hip_bfloat16*>(a.k) + ((long long)b * a.Hkv + hk) * a.kv_hstride;
+  const __hip_bfloat16* vg = reinterpret_cast<const __hip_bfloat16*>(a.v) + ((long long)b * a.Hkv + hk) * a.kv_hstride;
+  const float4* tab4 = reinterpret_cast<const float4*>(a.table);
+
+  const int l32 = lane & 31;
+  const int hl = lane >> 5;                      // lane half: 0 or 1
+
+  // ---- Q^T operand: query (qb*32 + l32), d = ks*16 + hl*8 + 0..7, rotated on load
+  bf16x8 qreg[2][8];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = wrow0 + qb * 32 + l32;
+    const bool ok = row < a.Nq;
+    const long long qpos = a.q_pos0 + row;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const int d0 = ks * 16 + hl * 8;
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (ok) {
+        w = *reinterpret_cast<const uint4*>(qg + (long long)row * kD + d0);
+        if (a.rope_flags & 1) {
+          const float4* t = tab4 + (qpos * (kD / 2) + d0 / 2) / 2;
+          w = rotate_chunk(w, t[0], t[1]);
+        }
+      }
+      qreg[qb][ks] = as_bf16x8(w);
+    }
+  }
+
+  // ---- key range of the workgroup (causal: up to its last query position)
+  int kend = a.Nk;
+  if (a.causal) {
+    const long long lim = a.q_pos0 + wg_row_last - a.k_pos0 + 1;
+    kend = (int)max(0LL, min((long long)a.Nk, lim));
+  }
+  const int ntiles = (kend + kBN - 1) / kBN;
+
+  // ---- staging assignment: chunk c (16 bytes = dims 8c..8c+7) of rows r0s + 16 i
+  const int sc = tid & 15;
+  const int sr = tid >> 4;
+  uint4 kbuf[4], vbuf[4];
+  float4 tbuf[4][2];
+
+  auto issue_loads = [&](int key0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = key0 + sr + 16 * i;
+      if (key < a.Nk) {
+        kbuf[i] = *reinterpret_cast<const uint4*>(kg + (long long)key * kD + sc * 8);
+        vbuf[i] = *reinterpret_cast<const uint4*>(vg + (long long)key * kD + sc * 8);
+        if (ROT_K) {
+          const float4* t = tab4 + ((a.k_pos0 + key) * (kD / 2) + sc * 4) / 2;
+          tbuf[i][0] = t[0];
+          tbuf[i][1] = t[1];
+        }
+      } else {
+        kbuf[i] = make_uint4(0, 0, 0, 0);
+        vbuf[i] = make_uint4(0, 0, 0, 0);
+        if (ROT_K) {
+          tbuf[i][0] = make_float4(0.f, 0.f, 0.f, 0.f);
+          tbuf[i][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+    }
+  };
+  auto store_lds = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = sr + 16 * i;
+      uint4 kw = kbuf[i];
+      if (ROT_K) kw = rotate_chunk(kw, tbuf[i][0], tbuf[i][1]);
+      *reinterpret_cast<uint4*>(&sm.k[buf][r * kKStr + sc * 8]) = kw;
+      *reinterpret_cast<uint4*>(&sm.v[buf][r * kVStr + sc * 8]) = vbuf[i];
+    }
+  };
+
+  f32x16 oacc[4][2];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) oacc[db][qb][j] = 0.f;
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.f, 0.f};
+  const float cscale = a.sm_scale * kLog2e;
+
+  if (ntiles > 0) {
+    issue_loads(0);
+    store_lds(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    const int key0 = t * kBN;
+    if (t + 1 < ntiles) issue_loads(key0 + kBN);
+
+    const __hip_bfloat16* kl = sm.k[buf];
+    const __hip_bfloat16* vl = sm.v[buf];
+    const bool ragged = key0 + kBN > a.Nk;
+    const bool diag = a.causal && (a.k_pos0 + key0 + kBN - 1 > a.q_pos0 + wrow0);
+    const int gj = lane & 15;
+    const int gd = ((lane >> 4) & 1) * 16 + 4 * (gj & 3);    // d offset inside a 32-wide block
+
+    // the 64-key tile is processed as two 32-key halves to bound register use
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      // ---- S^T = K Q^T : 32 keys x 2 query blocks x 8 d-steps
+      f32x16 sacc[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sacc[qb][j] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 ka =
+            as_bf16x8(*reinterpret_cast<const uint4*>(&kl[(kb * 32 + l32) * kKStr + ks * 16 + hl * 8]));
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[qb][ks], sacc[qb], 0, 0, 0);
+      }
+
+      // ---- mask (diagonal or ragged tiles only), online softmax, P^T operands
+      bf16x8 pb[2][2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const long long qpos = a.q_pos0 + wrow0 + qb * 32 + l32;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          float s = sacc[qb][j] * cscale;
+          if (ragged || diag) {
+            const int key = key0 + kb * 32 + (j >> 2) * 8 + hl * 4 + (j & 3);
+            const bool vis = key < a.Nk && (!a.causal || a.k_pos0 + key <= qpos);
+            s = vis ? s : -INFINITY;
+          }
+          sacc[qb][j] = s;
+          mx = fmaxf(mx, s);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // lazy rescale: only when some lane's maximum grew by more than 2^kLazy
+        const bool grow = mx > m_run[qb] + kLazy;
+        if (__any(grow)) {
+          const float mnew = fmaxf(m_run[qb], mx);
+          const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(m_run[qb] - mnew);
+          l_run[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) oacc[db][qb][j] *= alpha;
+          m_run[qb] = mnew;
+        }
+        const float mref = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+        float lsum = 0.f;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          uint32_t w[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p0 = exp2f(sacc[qb][half * 8 + 2 * i] - mref);
+            const float p1 = exp2f(sacc[qb][half * 8 + 2 * i + 1] - mref);
+            lsum += p0 + p1;
+            w[i] = pack2(p0, p1);
+          }
+          pb[half][qb] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+        }
+        l_run[qb] += lsum;
+      }
+
+      // ---- O^T += V^T P^T : 4 d blocks x 2 query blocks x 2 key steps of 16
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const int col = db * 32 + gd;
+          const int r1 = kb * 32 + half * 16 + hl * 4 + (gj >> 2);
+          const i16x4 lo = ds_read_tr(&vl[r1 * kVStr + col]);
+          const i16x4 hi = ds_read_tr(&vl[(r1 + 8) * kVStr + col]);
+          const bf16x8 va = __builtin_bit_cast(
+              bf16x8, (__attribute__((__vector_size__(8 * sizeof(short)))) short){lo[0], lo[1], lo[2], lo[3],
+                                                                                 hi[0], hi[1], hi[2], hi[3]});
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[half][qb], oacc[db][qb], 0, 0, 0);
+        }
+      }
+    }
+
+    if (t + 1 < ntiles) store_lds(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: combine the two lane halves' sums, normalise, write O and lse
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32);
+    const int row = wrow0 + qb * 32 + l32;
+    if (row >= a.Nq) continue;
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    const long long obase = ((long long)b * a.Hq + hq) * a.o_hstride + (long long)row * kD;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = db * 32 + g4 * 8 + hl * 4;
+        const float o0 = oacc[db][qb][g4 * 4 + 0] * inv, o1 = oacc[db][qb][g4 * 4 + 1] * inv;
+        const float o2 = oacc[db][qb][g4 * 4 + 2] * inv, o3 = oacc[db][qb][g4 * 4 + 3] * inv;
+        if (a.out_bf16) {
+          *reinterpret_cast<uint2*>(reinterpret_cast<__hip_bfloat16*>(a.out) + obase + d) =
+              make_uint2(pack2(o0, o1), pack2(o2, o3));
+        } else {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + obase + d) = make_float4(o0, o1, o2, o3);
+        }
+      }
+    }
+    if (a.lse && hl == 0)
+      a.lse[((long long)b * a.Hq + hq) * a.lse_hstride + row] =
+          lt > 0.f ? (m_run[qb] + log2f(lt)) * kLn2 : -INFINITY;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_bf16_d128(const PrefillArgs& a, hipStream_t stream) {
+  const int G = a.Hq / a.Hkv;
+  if (a.D != kD || !(G == 1 || G == 2 || G % 4 == 0)) return hipErrorInvalidValue;
+  const int HPW = G < 4 ? G : 4;
+  const int rows_per_wg = kBM * (4 / HPW);
+  const int quads = G > 4 ? G / 4 : 1;
+  const dim3 grid(a.Hkv * quads, (a.Nq + rows_per_wg - 1) / rows_per_wg, a.B), block(256);
+  if (a.rope_flags & 2)
+    hipLaunchKernelGGL(prefill_bf16_kernel<true>, grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(prefill_bf16_kernel<false>, grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace srt

@@ -1,0 +1,116 @@
+// RoPE kernels: the cos/sin table and the standalone rotation.
+//
+// Table: entry (p, i) = mscale * (cos, sin)(p * theta'_i).  The angle is formed
+// and the trigonometric functions evaluated in fp64, then rounded to fp32 once,
+// so positions up to 2^31 keep full fp32 accuracy ("Long Context: RoPE / YaRN /
+// NTK / MLA" §A.1 recommends computing cos/sin in fp32 or better and casting;
+// §6.4 folds the YaRN temperature into the cached cos/sin).
+//
+// Rotation: interleaved pairs (x_{2i}, x_{2i+1}) turned counter-clockwise by
+// the table angle ("Long Context..." §2.2; "长上下文外推" §4.2).  HBM-bound:
+// each thread moves 8 elements (one 16-byte bf16 vector or two fp32 vectors)
+// and reads the matching 4 table entries (32 bytes, L2-resident across heads).
+#include "srt_internal.h"
+
+namespace srt {
+namespace {
+
+__global__ void __launch_bounds__(256) rope_table_kernel(Theta th, int half, double mscale, long long npos,
+                                                          float2* __restrict__ table) {
+  const long long total = npos * half;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (long long)gridDim.x * blockDim.x) {
+    const long long p = e / half;
+    const int i = (int)(e - p * half);
+    double s, c;
+    sincos((double)p * th.v[i], &s, &c);
+    table[e] = make_float2((float)(mscale * c), (float)(mscale * s));
+  }
+}
+
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// round-to-nearest-even fp32 -> bf16 pair packed in one dword (lo = a, hi = b)
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  __hip_bfloat16 x = __float2bfloat16(a), y = __float2bfloat16(b);
+  return (uint32_t)__bfloat16_as_ushort(x) | ((uint32_t)__bfloat16_as_ushort(y) << 16);
+}
+
+// One thread = 8 consecutive elements of one row = 4 pairs.
+template <bool BF16>
+__global__ void __launch_bounds__(256) rope_apply_kernel(const void* __restrict__ x, void* y, long long groups,
+                                                         int N, int D, long long pos0,
+                                                         const float4* __restrict__ table) {
+  const int vec_per_row = D / 8;
+  const long long total = groups * (long long)N * vec_per_row;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (long long)gridDim.x * blockDim.x) {
+    const long long row = e / vec_per_row;
+    const int j = (int)(e - row * vec_per_row);        // which 8-element chunk of the row
+    const long long n = row % N;
+    const long long p = pos0 + n;
+    // table row p, pairs 4j .. 4j+3 = two float4 of (cos, sin, cos, sin)
+    const float4* trow = table + (p * (D / 2) + 4 * j) / 2;
+    const float4 t0 = trow[0], t1 = trow[1];
+    const float c[4] = {t0.x, t0.z, t1.x, t1.z};
+    const float s[4] = {t0.y, t0.w, t1.y, t1.w};
+    float v[8];
+    if (BF16) {
+      const uint4 w = reinterpret_cast<const uint4*>(x)[e];
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { v[2 * i] = bf16_lo(ww[i]); v[2 * i + 1] = bf16_hi(ww[i]); }
+    } else {
+      const float4 a = reinterpret_cast<const float4*>(x)[2 * e];
+      const float4 b = reinterpret_cast<const float4*>(x)[2 * e + 1];
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    float o[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = v[2 * i] * c[i] - v[2 * i + 1] * s[i];
+      o[2 * i + 1] = v[2 * i] * s[i] + v[2 * i + 1] * c[i];
+    }
+    if (BF16) {
+      uint4 w;
+      w.x = pack_bf16x2(o[0], o[1]); w.y = pack_bf16x2(o[2], o[3]);
+      w.z = pack_bf16x2(o[4], o[5]); w.w = pack_bf16x2(o[6], o[7]);
+      reinterpret_cast<uint4*>(y)[e] = w;
+    } else {
+      reinterpret_cast<float4*>(y)[2 * e] = make_float4(o[0], o[1], o[2], o[3]);
+      reinterpret_cast<float4*>(y)[2 * e + 1] = make_float4(o[4], o[5], o[6], o[7]);
+    }
+  }
+}
+
+inline unsigned grid_for(long long work, int block) {
+  long long g = (work + block - 1) / block;
+  const long long cap = 256LL * 64;   // enough waves in flight on 256 CUs; the loops stride beyond
+  return (unsigned)(g < 1 ? 1 : (g > cap ? cap : g));
+}
+
+}  // namespace
+
+hipError_t launch_rope_table(const Theta& th, int half, double mscale, long long npos, float* table,
+                             hipStream_t stream) {
+  const long long work = npos * half;
+  hipLaunchKernelGGL(rope_table_kernel, dim3(grid_for(work, 256)), dim3(256), 0, stream, th, half, mscale, npos,
+                     reinterpret_cast<float2*>(table));
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_apply(const void* x, void* y, bool bf16, long long groups, int N, int D, long long pos0,
+                             const float* table, hipStream_t stream) {
+  const long long work = groups * (long long)N * (D / 8);
+  const float4* t = reinterpret_cast<const float4*>(table);
+  if (bf16)
+    hipLaunchKernelGGL(rope_apply_kernel<true>, dim3(grid_for(work, 256)), dim3(256), 0, stream, x, y, groups, N,
+                       D, pos0, t);
+  else
+    hipLaunchKernelGGL(rope_apply_kernel<false>, dim3(grid_for(work, 256)), dim3(256), 0, stream, x, y, groups,
+                       N, D, pos0, t);
+  return hipGetLastError();
+}
+
+}  // namespace srt

@@ -1,0 +1,79 @@
+// Internal declarations shared by the C-ABI layer (abi.cpp) and the kernel
+// translation units.  Nothing here is part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+#include <cstdint>
+
+namespace srt {
+
+constexpr int kMaxHalf = 128;  // D <= 256
+
+// Scaled frequencies passed by value as a kernel argument (1 KiB).
+struct Theta {
+  double v[kMaxHalf];
+};
+
+// ---------------------------------------------------------------- rope
+hipError_t launch_rope_table(const Theta& th, int half, double mscale, long long npos, float* table,
+                             hipStream_t stream);
+
+// rows = B*H rows-groups of N rows each; row r of a group sits at position pos0 + r.
+hipError_t launch_rope_apply(const void* x, void* y, bool bf16, long long groups, int N, int D,
+                             long long pos0, const float* table, hipStream_t stream);
+
+// ---------------------------------------------------------------- prefill
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  const float* table;   // [npos][D/2] float2 or nullptr
+  long long q_hstride, kv_hstride, o_hstride, lse_hstride;  // elements
+  long long q_pos0, k_pos0;
+  int B, Hq, Hkv, Nq, Nk, D;
+  int causal;
+  int rope_flags;       // bit0: rotate q, bit1: rotate k
+  int out_bf16;         // 1: out is bf16, 0: fp32
+  float sm_scale;
+};
+
+hipError_t launch_prefill_bf16_d128(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- merge
+struct MergeArgs {
+  const void* oa;
+  const float* la;
+  const void* ob;
+  const float* lb;
+  void* oo;
+  float* lo;
+  long long in_hstride, out_hstride, lse_out_hstride;
+  int BH, N, D;
+  int in_bf16, out_bf16;
+};
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- decode
+struct DecodeArgs {
+  const void* q;          // [B][Hq][D] bf16
+  const void* k;          // [B][Hkv][Nk][D] bf16, rotated
+  const void* v;          // [B][Hkv][Nk][D] bf16
+  const int* seq_lens;    // [B] or nullptr
+  const float* table;     // or nullptr
+  float* ws_o;            // [B][Hq][splits][D] fp32
+  float* ws_lse;          // [B][Hq][splits] fp32
+  void* out;              // [B][Hq][D] bf16
+  float* lse;             // [B][Hq] or nullptr
+  int B, Hq, Hkv, Nk, D, splits, split_len;
+  float sm_scale;
+};
+
+size_t decode_workspace_bytes(int B, int Hq, int D, int splits);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace srt

@@ -1,0 +1,135 @@
+"""Host-side checks of libsrt.so (no GPU): exported symbols, the fp64
+frequency step against the oracle, and argument validation that returns
+before anything is enqueued."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import rope as orope
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def srt():
+    from scaled_rope_tiled_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from scaled_rope_tiled_amd.build import build
+        build()
+    import scaled_rope_tiled_amd as m
+    return m
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "srt.h"), encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(srt_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(srt):
+    names = _declared()
+    assert len(names) >= 9
+    lib = srt.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    from scaled_rope_tiled_amd._lib import SIGNATURES
+    assert sorted(SIGNATURES) == names
+
+
+def test_status_strings(srt):
+    lib = srt.lib()
+    assert lib.srt_abi_version() == 1
+    for s in range(5):
+        assert lib.srt_status_string(s)
+    assert lib.srt_status_string(99) == b"unknown status"
+
+
+CASES = [
+    (orope.NONE, 10000.0, 1.0, 0.0, 1.0, 32.0, 64),
+    (orope.NONE, 500000.0, 1.0, 0.0, 1.0, 32.0, 128),
+    (orope.PI, 10000.0, 16.0, 0.0, 1.0, 32.0, 128),
+    (orope.NTK, 10000.0, 16.0, 0.0, 1.0, 32.0, 128),
+    (orope.NTK, 1e6, 4.0, 0.0, 1.0, 32.0, 64),
+    (orope.YARN, 10000.0, 16.0, 2048.0, 1.0, 32.0, 128),
+    (orope.YARN, 10000.0, 8.0, 4096.0, 1.0, 32.0, 64),
+    (orope.YARN, 500000.0, 0.5, 8192.0, 2.0, 16.0, 128),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_inv_freq_matches_oracle(srt, case):
+    """Bands exact; theta' within 1e-15 relative; mscale exact to 1e-15."""
+    th, ms, band = srt.rope_inv_freq(*case)
+    oth, oms, oband = orope.inv_freq(*case)
+    np.testing.assert_array_equal(band, oband)
+    np.testing.assert_allclose(th, oth, rtol=1e-15, atol=0)
+    assert abs(ms - oms) <= 1e-15
+
+
+def test_c3_band_classification_exact(srt):
+    _, _, band = srt.rope_inv_freq(srt.YARN, 10000.0, 16.0, 2048.0, 1.0, 32.0, 128)
+    assert list(np.flatnonzero(band == 2)) == list(range(17))
+    assert list(np.flatnonzero(band == 1)) == list(range(17, 41))
+    assert list(np.flatnonzero(band == 0)) == list(range(41, 64))
+
+
+@pytest.mark.parametrize("args,frag", [
+    ((3, 1e4, 16.0, 2048.0, 32.0, 1.0, 128), "beta > alpha"),
+    ((0, 1e4, 1.0, 0.0, 1.0, 32.0, 63), "even"),
+    ((0, -1.0, 1.0, 0.0, 1.0, 32.0, 64), "base"),
+    ((9, 1e4, 1.0, 0.0, 1.0, 32.0, 64), "unknown method"),
+    ((1, 1e4, 0.0, 0.0, 1.0, 32.0, 64), "scale"),
+    ((3, 1e4, 16.0, 0.0, 1.0, 32.0, 64), "L > 0"),
+])
+def test_inv_freq_validation(srt, args, frag):
+    from scaled_rope_tiled_amd._lib import SrtError
+    with pytest.raises(SrtError, match=frag) as e:
+        srt.rope_inv_freq(*args)
+    assert e.value.status == 1
+
+
+def test_abi_rejects_before_launch(srt):
+    """Argument errors return SRT_ERR_INVALID / UNSUPPORTED with no GPU call."""
+    lib = srt.lib()
+    fake = C.c_void_p(0x100000)      # never dereferenced: every call below fails validation first
+    st = lib.srt_attn_prefill(None, fake, fake, 1, 1, 4, 2, 8, 8, 128, 1024, 1024, 0, 0, 1, 0.1,
+                              None, 0, 0, fake, 1, 1024, None, 0, None)
+    assert st == 1 and b"NULL" in lib.srt_last_error()
+    st = lib.srt_attn_prefill(fake, fake, fake, 1, 1, 4, 3, 8, 8, 128, 1024, 1024, 0, 0, 1, 0.1,
+                              None, 0, 0, fake, 1, 1024, None, 0, None)
+    assert st == 1 and b"multiple" in lib.srt_last_error()
+    st = lib.srt_attn_prefill(fake, fake, fake, 1, 1, 4, 2, 8, 8, 96, 768, 768, 0, 0, 1, 0.1,
+                              None, 0, 0, fake, 1, 768, None, 0, None)
+    assert st == 2
+    st = lib.srt_attn_prefill(fake, fake, fake, 1, 1, 4, 2, 8, 8, 128, 1024, 1024, 0, 0, 1, 0.1,
+                              None, 0, 3, fake, 1, 1024, None, 0, None)
+    assert st == 1 and b"table" in lib.srt_last_error()
+    st = lib.srt_attn_prefill(fake, fake, fake, 1, 1, 4, 2, 8, 8, 128, 1024, 1024, 0, 0, 1, 0.1,
+                              fake, 4, 3, fake, 1, 1024, None, 0, None)
+    assert st == 1 and b"outside table" in lib.srt_last_error()
+    st = lib.srt_rope_apply(fake, fake, 1, 1, 1, 8, 128, 5, fake, 10, None)
+    assert st == 1 and b"outside table" in lib.srt_last_error()
+    st = lib.srt_rope_apply(fake, fake, 7, 1, 1, 8, 128, 0, fake, 10, None)
+    assert st == 1
+    n = C.c_size_t()
+    assert lib.srt_attn_decode_workspace_size(16, 32, 128, 64, C.byref(n)) == 0
+    assert n.value == 16 * 32 * 64 * 129 * 4
+    st = lib.srt_attn_decode_splitk(fake, fake, fake, 1, 16, 32, 8, 1024, 128, None, 64, 0.1, None, 0,
+                                    fake, n.value - 1, fake, None, None)
+    assert st == 4
+    st = lib.srt_attn_decode_splitk(fake, fake, fake, 1, 16, 24, 8, 1024, 128, None, 64, 0.1, None, 0,
+                                    fake, n.value, fake, None, None)
+    assert st == 2
+    st = lib.srt_attn_decode_splitk(fake, fake, fake, 1, 16, 32, 8, 1024, 128, None, 0, 0.1, None, 0,
+                                    fake, n.value, fake, None, None)
+    assert st == 1
+    st = lib.srt_attn_merge_states(fake, fake, fake, fake, 0, 64, fake, 1, 128, None, 0, 1, 1, 1, 128, None)
+    assert st == 1 and b"stride" in lib.srt_last_error()
+    st = lib.srt_attn_merge_states(fake, fake, fake, fake, 0, 96, fake, 0, 96, None, 0, 1, 1, 1, 96, None)
+    assert st == 2
+    th = (C.c_double * 4)(1.0, 0.1, 0.01, float("inf"))
+    st = lib.srt_rope_cos_sin(th, 8, 1.0, 16, fake, None)
+    assert st == 1 and b"finite" in lib.srt_last_error()
