@@ -1,0 +1,375 @@
+#!/usr/bin/env python3
+"""Benchmark of the RoPE-scaled tiled attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
+
+Prints ONE JSON line.  The headline ``value`` is causal prefill TFLOP/s on the
+YaRN 32K workload (B=1, 32 query / 8 KV heads, D=128, N=32768, bf16, base
+1e4, L=2048, s=16, alpha=1, beta=32); a step is one pass of the prefill path
+over that input: the cos/sin table for the 32768 positions, then the fused
+kernel that rotates q and k on load and runs the tiled online softmax.  Inputs
+are resident in HBM before timing starts.  The same line carries:
+
+  * ``roofline``: the prefill kernel's algorithmic flops / its mean launch
+    time (HIP events on the launch stream) against the bf16 dense MFMA peak,
+    plus HBM traffic from committed rocprofv3 counters when they were taken
+    on the current kernel source (else null);
+  * ``decode``: 128K split-K decode (B=16, GQA 32/8, PI s=16, 64 splits):
+    algorithmic bytes / time against the 8 TB/s HBM peak;
+  * ``ring``: the 128K NTK prefill as 8 K/V chunks of 16384 merged by
+    log-sum-exp (one device's ring step), TFLOP/s;
+  * ``cpu_baseline``: the fp64 oracle on the host cores, on a bounded sample.
+
+FLOPs count only (query, key) pairs the causal mask keeps, 4*D per pair per
+query head.  Decode bytes count K and V once plus q, out, lse and the split-K
+workspace written and read back.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "causal prefill attn TFLOP/s + 128K decode GB/s, % of MI355X roofline"
+PEAK_BF16_TFLOPS = 2516.6       # 256 CU x 2.4 GHz x 4096 flop/clk/CU, dense
+PEAK_HBM_GBS = 8000.0
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_c3_yarn32k_counters.json")
+PREFILL_SRC = os.path.join(ROOT, "scaled_rope_tiled_amd", "csrc", "prefill_bf16.hip")
+
+
+def causal_pairs(Nq: int, Nk: int, q_pos0: int = 0, k_pos0: int = 0) -> int:
+    """Number of (query, key) pairs with k_pos0 + c <= q_pos0 + r (exact integer count)."""
+    total = 0
+    # row r sees clamp(q_pos0 - k_pos0 + r + 1, 0, Nk) keys
+    off = q_pos0 - k_pos0 + 1
+    r_lo = max(0, -off)                 # first row with a positive count
+    r_full = max(0, Nk - off)           # first row that sees all Nk keys
+    a, b = min(r_lo, Nq), min(max(r_full, r_lo), Nq)
+    if b > a:                           # ramp rows: off + r keys
+        total += (b - a) * off + (a + b - 1) * (b - a) // 2
+    if Nq > b:
+        total += (Nq - b) * Nk
+    return total
+
+
+def prefill_flops(B, Hq, Nq, Nk, D, q_pos0=0, k_pos0=0, causal=True) -> float:
+    pairs = causal_pairs(Nq, Nk, q_pos0, k_pos0) if causal else Nq * Nk
+    return 4.0 * D * B * Hq * pairs
+
+
+def _sha(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _ensure_built():
+    from scaled_rope_tiled_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from scaled_rope_tiled_amd.build import build
+        build()
+
+
+class Timer:
+    """HIP events on the current stream around a callable, averaged over calls."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def run(self, fn):
+        t = self.torch
+        e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        e0.record()
+        r = fn()
+        e1.record()
+        self.pairs.append((e0, e1))
+        return r
+
+    def mean_ms(self):
+        return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
+
+
+# ----------------------------------------------------------------------------- prefill (headline)
+
+def bench_prefill(srt, torch, w, steps, warmup, prerotate_k=False):
+    import synth
+    D = w.D
+    q = synth.randn((w.B, w.Hq, w.N, D), torch.bfloat16, w.seed, synth.Q_ID, "cuda")
+    k = synth.randn((w.B, w.Hkv, w.N, D), torch.bfloat16, w.seed, synth.K_ID, "cuda")
+    v = synth.randn((w.B, w.Hkv, w.N, D), torch.bfloat16, w.seed, synth.V_ID, "cuda")
+    rp = w.rope
+    th, ms, _ = srt.rope_inv_freq(rp.method, rp.base, rp.s, rp.L, rp.alpha, rp.beta, D)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device="cuda")
+    table = torch.empty((w.N, D // 2, 2), dtype=torch.float32, device="cuda")
+    krot = torch.empty_like(k) if prerotate_k else None
+    kt = Timer(torch)
+
+    import ctypes as C
+    import numpy as np
+    thc = np.ascontiguousarray(th)
+    lib = srt.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(timed):
+        from scaled_rope_tiled_amd import _lib as L
+        L.check(lib.srt_rope_cos_sin(thc.ctypes.data_as(C.POINTER(C.c_double)), D, ms, w.N,
+                                     C.c_void_p(table.data_ptr()), stream), "rope_cos_sin")
+        if prerotate_k:
+            srt.rope_apply(k, table, out=krot)
+            fn = lambda: srt.attn_prefill(q, krot, v, table=table, rope_flags=srt.ROTATE_Q, out=out, lse=lse)
+        else:
+            fn = lambda: srt.attn_prefill(q, k, v, table=table, out=out, lse=lse)
+        if timed:
+            kt.run(fn)
+        else:
+            fn()
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    flops = prefill_flops(w.B, w.Hq, w.N, w.N, D)
+    kernel_ms = kt.mean_ms()
+    return {"flops": flops, "ms_per_step": ms_step, "kernel_ms": kernel_ms,
+            "tflops_step": flops / (ms_step * 1e-3) / 1e12, "tflops_kernel": flops / (kernel_ms * 1e-3) / 1e12}
+
+
+def traffic_from_counters(flops_unit_note=None):
+    """HBM bytes per launch from committed rocprofv3 counters, if taken on this kernel source."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None, "no counter file"
+    with open(COUNTERS_FILE) as f:
+        c = json.load(f)
+    if c.get("source_sha256") != _sha(PREFILL_SRC):
+        return None, "kernel changed since the counters were taken"
+    fetch = c["fetch_kib_per_dispatch"] * 1024.0 * c["fetch_scale"]
+    write = c["write_kib_per_dispatch"] * 1024.0 * c["write_scale"]
+    return fetch + write, "rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated"
+
+
+# ----------------------------------------------------------------------------- decode
+
+def bench_decode(srt, torch, w, steps, warmup):
+    import synth
+    D = w.D
+    N = w.N
+    q = synth.randn((w.B, w.Hq, D), torch.bfloat16, w.seed, synth.Q_ID, "cuda")
+    k = synth.randn((w.B, w.Hkv, N, D), torch.bfloat16, w.seed, synth.K_ID, "cuda")
+    v = synth.randn((w.B, w.Hkv, N, D), torch.bfloat16, w.seed, synth.V_ID, "cuda")
+    rp = w.rope
+    th, ms, _ = srt.rope_inv_freq(rp.method, rp.base, rp.s, rp.L, rp.alpha, rp.beta, D)
+    table = srt.rope_cos_sin(th, D, ms, N, "cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    srt.rope_apply(k, table, out=k)                 # rotated cache, in place (setup, not timed in the step)
+    torch.cuda.synchronize()
+    cache_ms = (time.perf_counter() - t0) * 1e3
+    ws = torch.empty(srt.attn_decode_workspace_size(w.B, w.Hq, D, w.splits), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.B, w.Hq, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
+    kt = Timer(torch)
+    fn = lambda: srt.attn_decode_splitk(q, k, v, num_splits=w.splits, table=table, workspace=ws, out=out, lse=lse)
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        kt.run(fn)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    kv = 2.0 * w.B * w.Hkv * N * D * 2
+    ws_bytes = w.B * w.Hq * w.splits * (D + 1) * 4.0
+    alg = kv + w.B * w.Hq * D * 2 * 2 + w.B * w.Hq * 4 + 2 * ws_bytes
+    kernel_ms = kt.mean_ms()
+    gbs = alg / (kernel_ms * 1e-3) / 1e9
+    del k, v
+    return {"workload": w.name, "unit": "GB/s", "value": round(gbs, 1), "ms_per_step": round(ms_step, 4),
+            "kernel_ms": round(kernel_ms, 4), "alg_bytes": alg,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4)},
+            "cache_build_ms": round(cache_ms, 3)}
+
+
+# ----------------------------------------------------------------------------- ring step on one GPU
+
+def bench_ring(srt, torch, w, steps, warmup):
+    import synth
+    D, N, C = w.D, w.N, w.N // w.chunks
+    q = synth.randn((w.B, w.Hq, N, D), torch.bfloat16, w.seed, synth.Q_ID, "cuda")
+    k = synth.randn((w.B, w.Hkv, N, D), torch.bfloat16, w.seed, synth.K_ID, "cuda")
+    v = synth.randn((w.B, w.Hkv, N, D), torch.bfloat16, w.seed, synth.V_ID, "cuda")
+    rp = w.rope
+    th, ms, _ = srt.rope_inv_freq(rp.method, rp.base, rp.s, rp.L, rp.alpha, rp.beta, D)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, N), dtype=torch.float32, device="cuda")
+    acc = torch.empty((w.B, w.Hq, C, D), dtype=torch.float32, device="cuda")
+    acc_l = torch.empty((w.B, w.Hq, C), dtype=torch.float32, device="cuda")
+    tmp = torch.empty_like(acc)
+    tmp_l = torch.empty_like(acc_l)
+
+    def step():
+        table = srt.rope_cos_sin(th, D, ms, N, "cuda")
+        ring_step(srt, q, k, v, table, out, lse, acc, acc_l, tmp, tmp_l, w.chunks)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    flops = prefill_flops(w.B, w.Hq, N, N, D)
+    tf = flops / (ms_step * 1e-3) / 1e12
+    return {"workload": w.name, "unit": "TFLOP/s", "value": round(tf, 2), "ms_per_step": round(ms_step, 3),
+            "chunks": w.chunks, "launches": {"prefill": w.chunks * (w.chunks + 1) // 2,
+                                             "merge": w.chunks * (w.chunks - 1) // 2},
+            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
+def ring_step(srt, q, k, v, table, out, lse, acc, acc_l, tmp, tmp_l, chunks):
+    """Query chunk i attends K/V chunks 0..i at their absolute offsets; partial
+    states (fp32) are merged by log-sum-exp; the last merge writes bf16 output."""
+    N = q.shape[2]
+    C = N // chunks
+    for i in range(chunks):
+        qi = q[:, :, i * C:(i + 1) * C]
+        oi, li = out[:, :, i * C:(i + 1) * C], lse[:, :, i * C:(i + 1) * C]
+        if i == 0:
+            srt.attn_prefill(qi, k[:, :, :C], v[:, :, :C], q_pos0=0, k_pos0=0, table=table, out=oi, lse=li)
+            continue
+        for j in range(i + 1):
+            kj, vj = k[:, :, j * C:(j + 1) * C], v[:, :, j * C:(j + 1) * C]
+            dst, dst_l = (acc, acc_l) if j == 0 else (tmp, tmp_l)
+            srt.attn_prefill(qi, kj, vj, q_pos0=i * C, k_pos0=j * C, table=table, out=dst, lse=dst_l)
+            if j == 0:
+                continue
+            if j < i:
+                srt.attn_merge_states(acc, acc_l, tmp, tmp_l, out=acc, lse_out=acc_l)
+            else:
+                srt.attn_merge_states(acc, acc_l, tmp, tmp_l, out=oi, lse_out=li)
+
+
+# ----------------------------------------------------------------------------- CPU baseline (oracle)
+
+def cpu_baseline(w, budget_s: float):
+    """The fp64 oracle on the host cores over a bounded sample of the prefill
+    workload: query rows taken from the end of the sequence (the longest rows),
+    one KV group of 4 query heads at a time, until the time budget is spent.
+    Inputs are drawn on the CPU with the same recipe (values differ from the
+    GPU draw; the rate does not depend on them)."""
+    import numpy as np
+    import torch
+    import synth
+    from oracle import attention as OA
+    from oracle import rope as OR
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count()
+    D, N = w.D, w.N
+    rp = w.rope
+    th, ms, _ = OR.inv_freq(rp.method, rp.base, rp.s, rp.L, rp.alpha, rp.beta, D)
+    G = w.Hq // w.Hkv
+    block = 256
+    t0 = time.perf_counter()
+    flops = 0.0
+    rows_done = 0
+    hk = 0
+    k = synth.randn((1, 1, N, D), torch.bfloat16, w.seed, synth.K_ID).float().numpy()
+    v = synth.randn((1, 1, N, D), torch.bfloat16, w.seed, synth.V_ID).float().numpy()
+    q = synth.randn((1, G, N, D), torch.bfloat16, w.seed, synth.Q_ID).float().numpy()
+    r_hi = N
+    while time.perf_counter() - t0 < budget_s and r_hi > 0:
+        rows = np.arange(max(0, r_hi - block), r_hi)
+        OA.attention(q, k, v, sm_scale=w.sm_scale, causal=True, theta=th, mscale=ms, rows=rows, block=block)
+        flops += 4.0 * D * G * float(np.sum(rows + 1))
+        rows_done += G * len(rows)
+        r_hi -= block
+    el = time.perf_counter() - t0
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{rows_done} query rows (the last {N - r_hi} rows of {G} heads of one KV group, "
+                      f"each against all its visible keys) of {w.name}, {el:.1f} s, fp64 numpy"}
+
+
+# ----------------------------------------------------------------------------- copy calibration
+
+def copy_calibration(torch, nbytes: int, reps: int):
+    """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE."""
+    x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c3", choices=["c2", "c3"])
+    ap.add_argument("--prerotate-k", action="store_true", help="rotate K once with rope_apply, q on load")
+    ap.add_argument("--no-extras", action="store_true", help="skip the decode and ring legs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (multi-GPU sharding is "
+                                   "described in DESIGN.md, not built)"}))
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration:
+        copy_calibration(torch, args.copy_calibration, 5)
+        return
+    _ensure_built()
+    import scaled_rope_tiled_amd as srt
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    p = bench_prefill(srt, torch, w, args.steps, args.warmup, args.prerotate_k)
+    traffic, traffic_note = traffic_from_counters()
+    roof = {"bound": "mfma", "achieved": round(p["tflops_kernel"], 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(p["tflops_kernel"] / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic, "traffic_note": traffic_note,
+            "kernel": "prefill_bf16_kernel", "kernel_ms": round(p["kernel_ms"], 4),
+            "alg_flops_per_launch": p["flops"]}
+    line = {"metric": METRIC, "value": round(p["tflops_step"], 2), "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(p["ms_per_step"], 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "D": w.D,
+                       "causal": True, "rope": w.note, "step": ("cos/sin table + prefill (K pre-rotated)"
+                                                               if args.prerotate_k else
+                                                               "cos/sin table + prefill rotating q,k on load")},
+            "roofline": roof}
+    if not args.no_extras:
+        torch.cuda.empty_cache()
+        line["decode"] = bench_decode(srt, torch, synth.WORKLOADS["c5"], max(5, args.steps), args.warmup)
+        torch.cuda.empty_cache()
+        line["ring"] = bench_ring(srt, torch, synth.WORKLOADS["c4"], max(2, args.steps // 5), 1)
+        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

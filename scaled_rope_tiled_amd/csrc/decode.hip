@@ -38,8 +38,10 @@ __device__ inline float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float hi_f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 __device__ inline uint32_t pack2(float a, float b) {
-  return (uint32_t)__bfloat16_as_ushort(__float2bfloat16(a)) |
-         ((uint32_t)__bfloat16_as_ushort(__float2bfloat16(b)) << 16);
+  // one v_cvt_pk_bf16_f32: both values rounded to nearest even
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){a, b}, b2_t));
 }
 
 __device__ inline float dot2(uint32_t a, uint32_t b, float c) {

@@ -30,8 +30,10 @@ __device__ inline void load8(const void* base, long long off, bool bf16, float v
 }
 
 __device__ inline uint32_t pack2(float a, float b) {
-  return (uint32_t)__bfloat16_as_ushort(__float2bfloat16(a)) |
-         ((uint32_t)__bfloat16_as_ushort(__float2bfloat16(b)) << 16);
+  // one v_cvt_pk_bf16_f32: both values rounded to nearest even
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){a, b}, b2_t));
 }
 
 __device__ inline void store8(void* base, long long off, bool bf16, const float v[8]) {

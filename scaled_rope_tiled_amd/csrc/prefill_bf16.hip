@@ -51,13 +51,16 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kD = 128;
-constexpr int kBM = 64;           // query rows per wave
+constexpr int kWaves = 8;         // waves per workgroup (two per SIMD)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 32;           // query rows per wave
 constexpr int kBN = 64;           // keys per tile
 constexpr int kKStr = kD + 8;     // K tile row stride (bf16 elements) = 272 B
 constexpr int kVStr = kD + 32;    // V tile row stride (bf16 elements) = 320 B
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;     // rescale threshold (log2 units)
+constexpr int kStageRows = kBN * 16 / kThreads;   // 16-byte chunks per thread per tile and tensor
 
 struct Smem {
   __hip_bfloat16 k[2][kBN * kKStr];
@@ -68,8 +71,10 @@ __device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 __device__ inline uint32_t pack2(float a, float b) {
-  return (uint32_t)__bfloat16_as_ushort(__float2bfloat16(a)) |
-         ((uint32_t)__bfloat16_as_ushort(__float2bfloat16(b)) << 16);
+  // one v_cvt_pk_bf16_f32: both values rounded to nearest even
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){a, b}, b2_t));
 }
 
 // Rotate the 4 pairs of a 16-byte bf16 chunk with 4 (cos, sin) table entries.
@@ -96,15 +101,15 @@ __device__ inline i16x4 ds_read_tr(const __hip_bfloat16* p) {
 }
 
 template <bool ROT_K>
-__global__ void __launch_bounds__(256, 1) prefill_bf16_kernel(PrefillArgs a) {
+__global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a) {
   __shared__ Smem sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = a.Hq / a.Hkv;
   const int HPW = G < 4 ? G : 4;                 // query heads per workgroup
-  const int RB = 4 / HPW;                        // 64-row blocks per workgroup
+  const int RB = kWaves / HPW;                   // 32-row blocks per workgroup
   const int quads = G > 4 ? G / 4 : 1;
   const int hk = blockIdx.x / quads;
   const int quad = blockIdx.x - hk * quads;
@@ -123,11 +128,10 @@ __global__ void __launch_bounds__(256, 1) prefill_bf16_kernel(PrefillArgs a) {
   const int l32 = lane & 31;
   const int hl = lane >> 5;                      // lane half: 0 or 1
 
-  // ---- Q^T operand: query (qb*32 + l32), d = ks*16 + hl*8 + 0..7, rotated on load
-  bf16x8 qreg[2][8];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int row = wrow0 + qb * 32 + l32;
+  // ---- Q^T operand: query wrow0 + l32, d = ks*16 + hl*8 + 0..7, rotated on load
+  bf16x8 qreg[8];
+  {
+    const int row = wrow0 + l32;
     const bool ok = row < a.Nq;
     const long long qpos = a.q_pos0 + row;
 #pragma unroll
@@ -141,7 +145,7 @@ __global__ void __launch_bounds__(256, 1) prefill_bf16_kernel(PrefillArgs a) {
           w = rotate_chunk(w, t[0], t[1]);
         }
       }
-      qreg[qb][ks] = as_bf16x8(w);
+      qreg[ks] = as_bf16x8(w);
     }
   }
 
@@ -152,17 +156,20 @@ __global__ void __launch_bounds__(256, 1) prefill_bf16_kernel(PrefillArgs a) {
     kend = (int)max(0LL, min((long long)a.Nk, lim));
   }
   const int ntiles = (kend + kBN - 1) / kBN;
+  // keys of a tile starting at key0 are all visible to every row of this wave iff
+  // key0 + kBN <= Nk and k_pos0 + key0 + kBN - 1 <= q_pos0 + wrow0
+  const long long wave_free_lim = a.causal ? (a.q_pos0 + wrow0 - a.k_pos0 + 1) : (long long)a.Nk;
 
-  // ---- staging assignment: chunk c (16 bytes = dims 8c..8c+7) of rows r0s + 16 i
+  // ---- staging assignment: chunk sc (16 bytes = dims 8sc..8sc+7) of rows sr and sr + 32
   const int sc = tid & 15;
   const int sr = tid >> 4;
-  uint4 kbuf[4], vbuf[4];
-  float4 tbuf[4][2];
+  uint4 kbuf[kStageRows], vbuf[kStageRows];
+  float4 tbuf[kStageRows][2];
 
   auto issue_loads = [&](int key0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = key0 + sr + 16 * i;
+    for (int i = 0; i < kStageRows; ++i) {
+      const int key = key0 + sr + (kThreads / 16) * i;
       if (key < a.Nk) {
         kbuf[i] = *reinterpret_cast<const uint4*>(kg + (long long)key * kD + sc * 8);
         vbuf[i] = *reinterpret_cast<const uint4*>(vg + (long long)key * kD + sc * 8);
@@ -183,8 +190,8 @@ __global__ void __launch_bounds__(256, 1) prefill_bf16_kernel(PrefillArgs a) {
   };
   auto store_lds = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = sr + 16 * i;
+    for (int i = 0; i < kStageRows; ++i) {
+      const int r = sr + (kThreads / 16) * i;
       uint4 kw = kbuf[i];
       if (ROT_K) kw = rotate_chunk(kw, tbuf[i][0], tbuf[i][1]);
       *reinterpret_cast<uint4*>(&sm.k[buf][r * kKStr + sc * 8]) = kw;
@@ -192,16 +199,24 @@ __global__ void __launch_bounds__(256, 1) prefill_bf16_kernel(PrefillArgs a) {
     }
   };
 
-  f32x16 oacc[4][2];
+  f32x16 oacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) oacc[db][qb][j] = 0.f;
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
+    for (int j = 0; j < 16; ++j) oacc[db][j] = 0.f;
+  float m_run = -INFINITY;       // running max of this lane's query, in scaled log2 units
+  float l_run = 0.f;             // this lane's partial sum (its 16 keys of every 32)
   const float cscale = a.sm_scale * kLog2e;
+  // Mask as one integer compare per score: key index c is visible to this
+  // lane's query iff c <= klim (causal: k_pos0 + c <= q_pos0 + wrow0 + l32; and c < Nk).
+  int klim;
+  {
+    long long lim = a.causal ? (a.q_pos0 + wrow0 + l32 - a.k_pos0) : (long long)a.Nk - 1;
+    lim = lim < (long long)a.Nk - 1 ? lim : (long long)a.Nk - 1;
+    klim = (int)(lim < -1 ? -1 : lim);
+  }
+  const int gj = lane & 15;
+  const int gd = ((lane >> 4) & 1) * 16 + 4 * (gj & 3);    // d offset inside a 32-wide block
 
   if (ntiles > 0) {
     issue_loads(0);
@@ -213,80 +228,65 @@ __global__ void __launch_bounds__(256, 1) prefill_bf16_kernel(PrefillArgs a) {
     const int buf = t & 1;
     const int key0 = t * kBN;
     if (t + 1 < ntiles) issue_loads(key0 + kBN);
-
     const __hip_bfloat16* kl = sm.k[buf];
     const __hip_bfloat16* vl = sm.v[buf];
-    const bool ragged = key0 + kBN > a.Nk;
-    const bool diag = a.causal && (a.k_pos0 + key0 + kBN - 1 > a.q_pos0 + wrow0);
-    const int gj = lane & 15;
-    const int gd = ((lane >> 4) & 1) * 16 + 4 * (gj & 3);    // d offset inside a 32-wide block
+    // wave-uniform: does any key of this tile need the mask for this wave?
+    const bool masked = (long long)key0 + kBN > wave_free_lim || key0 + kBN > a.Nk;
 
-    // the 64-key tile is processed as two 32-key halves to bound register use
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      // ---- S^T = K Q^T : 32 keys x 2 query blocks x 8 d-steps
-      f32x16 sacc[2];
+      // ---- S^T = K Q^T for 32 keys: 8 d-steps
+      f32x16 sacc;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) sacc[qb][j] = 0.f;
+      for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const bf16x8 ka =
             as_bf16x8(*reinterpret_cast<const uint4*>(&kl[(kb * 32 + l32) * kKStr + ks * 16 + hl * 8]));
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[qb][ks], sacc[qb], 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], sacc, 0, 0, 0);
       }
 
-      // ---- mask (diagonal or ragged tiles only), online softmax, P^T operands
-      bf16x8 pb[2][2];
+      // ---- causal / ragged mask (uniform branch), row max
+      if (masked) {
+        const int rel = klim - (key0 + kb * 32 + hl * 4);
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const long long qpos = a.q_pos0 + wrow0 + qb * 32 + l32;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          float s = sacc[qb][j] * cscale;
-          if (ragged || diag) {
-            const int key = key0 + kb * 32 + (j >> 2) * 8 + hl * 4 + (j & 3);
-            const bool vis = key < a.Nk && (!a.causal || a.k_pos0 + key <= qpos);
-            s = vis ? s : -INFINITY;
-          }
-          sacc[qb][j] = s;
-          mx = fmaxf(mx, s);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        // lazy rescale: only when some lane's maximum grew by more than 2^kLazy
-        const bool grow = mx > m_run[qb] + kLazy;
-        if (__any(grow)) {
-          const float mnew = fmaxf(m_run[qb], mx);
-          const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(m_run[qb] - mnew);
-          l_run[qb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) oacc[db][qb][j] *= alpha;
-          m_run[qb] = mnew;
-        }
-        const float mref = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
-        float lsum = 0.f;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          uint32_t w[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p0 = exp2f(sacc[qb][half * 8 + 2 * i] - mref);
-            const float p1 = exp2f(sacc[qb][half * 8 + 2 * i + 1] - mref);
-            lsum += p0 + p1;
-            w[i] = pack2(p0, p1);
-          }
-          pb[half][qb] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
-        }
-        l_run[qb] += lsum;
+        for (int j = 0; j < 16; ++j) sacc[j] = ((j >> 2) * 8 + (j & 3)) <= rel ? sacc[j] : -INFINITY;
       }
+      float mx = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
+#pragma unroll
+      for (int j = 3; j < 15; j += 2) mx = fmaxf(fmaxf(mx, sacc[j]), sacc[j + 1]);
+      mx = fmaxf(mx, sacc[15]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * cscale;
+      // lazy rescale: only when some lane's maximum grew by more than 2^kLazy
+      if (__any(mx > m_run + kLazy)) {
+        const float mnew = fmaxf(m_run, mx);
+        const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - mnew);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
+        m_run = mnew;
+      }
+      const float mref = m_run == -INFINITY ? 0.f : m_run;
+      // ---- P = exp2(s * c - m), packed as the P^T operand of two 16-key steps
+      bf16x8 pb[2];
+      float lsum = 0.f;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[half * 8 + 2 * i], cscale, -mref));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[half * 8 + 2 * i + 1], cscale, -mref));
+          lsum += p0 + p1;
+          w[i] = pack2(p0, p1);
+        }
+        pb[half] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+      }
+      l_run += lsum;
 
-      // ---- O^T += V^T P^T : 4 d blocks x 2 query blocks x 2 key steps of 16
+      // ---- O^T += V^T P^T : 4 d blocks x 2 key steps of 16
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
 #pragma unroll
@@ -298,9 +298,7 @@ __global__ void __launch_bounds__(256, 1) prefill_bf16_kernel(PrefillArgs a) {
           const bf16x8 va = __builtin_bit_cast(
               bf16x8, (__attribute__((__vector_size__(8 * sizeof(short)))) short){lo[0], lo[1], lo[2], lo[3],
                                                                                  hi[0], hi[1], hi[2], hi[3]});
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[half][qb], oacc[db][qb], 0, 0, 0);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[half], oacc[db], 0, 0, 0);
         }
       }
     }
@@ -310,11 +308,9 @@ __global__ void __launch_bounds__(256, 1) prefill_bf16_kernel(PrefillArgs a) {
   }
 
   // ---- epilogue: combine the two lane halves' sums, normalise, write O and lse
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32);
-    const int row = wrow0 + qb * 32 + l32;
-    if (row >= a.Nq) continue;
+  const float lt = l_run + __shfl_xor(l_run, 32);
+  const int row = wrow0 + l32;
+  if (row < a.Nq) {
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
     const long long obase = ((long long)b * a.Hq + hq) * a.o_hstride + (long long)row * kD;
 #pragma unroll
@@ -322,8 +318,8 @@ __global__ void __launch_bounds__(256, 1) prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d = db * 32 + g4 * 8 + hl * 4;
-        const float o0 = oacc[db][qb][g4 * 4 + 0] * inv, o1 = oacc[db][qb][g4 * 4 + 1] * inv;
-        const float o2 = oacc[db][qb][g4 * 4 + 2] * inv, o3 = oacc[db][qb][g4 * 4 + 3] * inv;
+        const float o0 = oacc[db][g4 * 4 + 0] * inv, o1 = oacc[db][g4 * 4 + 1] * inv;
+        const float o2 = oacc[db][g4 * 4 + 2] * inv, o3 = oacc[db][g4 * 4 + 3] * inv;
         if (a.out_bf16) {
           *reinterpret_cast<uint2*>(reinterpret_cast<__hip_bfloat16*>(a.out) + obase + d) =
               make_uint2(pack2(o0, o1), pack2(o2, o3));
@@ -333,8 +329,7 @@ __global__ void __launch_bounds__(256, 1) prefill_bf16_kernel(PrefillArgs a) {
       }
     }
     if (a.lse && hl == 0)
-      a.lse[((long long)b * a.Hq + hq) * a.lse_hstride + row] =
-          lt > 0.f ? (m_run[qb] + log2f(lt)) * kLn2 : -INFINITY;
+      a.lse[((long long)b * a.Hq + hq) * a.lse_hstride + row] = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -INFINITY;
   }
 }
 
@@ -344,9 +339,9 @@ hipError_t launch_prefill_bf16_d128(const PrefillArgs& a, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
   if (a.D != kD || !(G == 1 || G == 2 || G % 4 == 0)) return hipErrorInvalidValue;
   const int HPW = G < 4 ? G : 4;
-  const int rows_per_wg = kBM * (4 / HPW);
+  const int rows_per_wg = kBM * (kWaves / HPW);
   const int quads = G > 4 ? G / 4 : 1;
-  const dim3 grid(a.Hkv * quads, (a.Nq + rows_per_wg - 1) / rows_per_wg, a.B), block(256);
+  const dim3 grid(a.Hkv * quads, (a.Nq + rows_per_wg - 1) / rows_per_wg, a.B), block(kThreads);
   if (a.rope_flags & 2)
     hipLaunchKernelGGL(prefill_bf16_kernel<true>, grid, block, 0, stream, a);
   else

@@ -31,10 +31,12 @@ __global__ void __launch_bounds__(256) rope_table_kernel(Theta th, int half, dou
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// round-to-nearest-even fp32 -> bf16 pair packed in one dword (lo = a, hi = b)
+// fp32 pair -> packed bf16 pair (lo = a, hi = b), round to nearest even
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
-  __hip_bfloat16 x = __float2bfloat16(a), y = __float2bfloat16(b);
-  return (uint32_t)__bfloat16_as_ushort(x) | ((uint32_t)__bfloat16_as_ushort(y) << 16);
+  // one v_cvt_pk_bf16_f32: both values rounded to nearest even
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){a, b}, b2_t));
 }
 
 // One thread = 8 consecutive elements of one row = 4 pairs.

@@ -1,0 +1,126 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration
+the benchmark times, on sampled output rows the oracle computes one by one.
+
+Row samples per head: the first and last rows, both sides of every 64-row
+kernel tile edge near the sample points, both sides of every ring chunk edge,
+and seeded random rows.  Bar: max-abs <= 1e-4 (fp32) / 2e-2 (bf16) on O and lse."""
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_helpers import device_table, f64, max_abs, need_gpu, oracle_freq
+from oracle import attention as A
+from oracle import rope as orope
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _row_ranges(N, seed, chunk=None, n_random=24):
+    rng = np.random.default_rng(seed)
+    ranges = [(0, 8), (N - 8, N), (63, 66), (N // 2 - 1, N // 2 + 1)]
+    if chunk:
+        for j in range(1, N // chunk):
+            ranges.append((j * chunk - 2, j * chunk + 2))
+    for r in rng.integers(0, N - 2, n_random):
+        ranges.append((int(r), int(r) + 2))
+    return sorted(set(ranges))
+
+
+def _inputs(w, device="cuda"):
+    D = w.D
+    q = synth.randn((w.B, w.Hq, w.N, D), w.dtype, w.seed, synth.Q_ID, device)
+    k = synth.randn((w.B, w.Hkv, w.N, D), w.dtype, w.seed, synth.K_ID, device)
+    v = synth.randn((w.B, w.Hkv, w.N, D), w.dtype, w.seed, synth.V_ID, device)
+    return q, k, v
+
+
+def _check_rows(w, q, k, v, o, l, ranges):
+    """Oracle on the sampled rows: rotate each KV head once (fp64), then plain
+    softmax attention for each contiguous row range at its absolute position."""
+    th, ms, _ = oracle_freq(w.rope, w.D)
+    G = w.Hq // w.Hkv
+    worst_o = worst_l = 0.0
+    for b in range(w.B):
+        for hk in range(w.Hkv):
+            kr = orope.rotate(f64(k[b, hk]), np.arange(w.N), th, ms)[None, None]
+            vv = f64(v[b, hk])[None, None]
+            for h in range(hk * G, (hk + 1) * G):
+                for a, e in ranges:
+                    qr = orope.rotate(f64(q[b, h, a:e]), np.arange(a, e), th, ms)[None, None]
+                    ro, rl = A.attention(qr, kr[:, :, :e], vv[:, :, :e], sm_scale=w.sm_scale, causal=True,
+                                         q_pos0=a, k_pos0=0, theta=None)
+                    worst_o = max(worst_o, max_abs(f64(o[b, h, a:e]), ro[0, 0]))
+                    worst_l = max(worst_l, max_abs(f64(l[b, h, a:e]), rl[0, 0]))
+    return worst_o, worst_l
+
+
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_prefill_full_size(name):
+    srt = need_gpu()
+    w = synth.WORKLOADS[name]
+    q, k, v = _inputs(w)
+    table, _ = device_table(srt, w.rope, w.D, w.N)
+    o, l = srt.attn_prefill(q, k, v, table=table)            # same launch as the benchmark step
+    torch.cuda.synchronize()
+    wo, wl = _check_rows(w, q, k, v, o, l, _row_ranges(w.N, w.seed))
+    print(f"{name}: max|dO|={wo:.3g} max|dlse|={wl:.3g}", flush=True)
+    assert wo <= TOL and wl <= TOL
+    # K pre-rotated by rope_apply + q rotated on load gives the same rows
+    kr = srt.rope_apply(k, table)
+    o2, l2 = srt.attn_prefill(q, kr, v, table=table, rope_flags=srt.ROTATE_Q)
+    assert max_abs(f64(o2[:, :, -64:]), f64(o[:, :, -64:])) <= 1e-2
+
+
+def test_ring_128k_full_size():
+    """NTK 128K as 8 K/V chunks of 16384 merged by log-sum-exp (the benchmark's ring leg)."""
+    srt = need_gpu()
+    sys.path.insert(0, ROOT)
+    from bench import ring_step
+    w = synth.WORKLOADS["c4"]
+    q, k, v = _inputs(w)
+    table, _ = device_table(srt, w.rope, w.D, w.N)
+    C = w.N // w.chunks
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device="cuda")
+    acc = torch.empty((w.B, w.Hq, C, w.D), dtype=torch.float32, device="cuda")
+    accl = torch.empty((w.B, w.Hq, C), dtype=torch.float32, device="cuda")
+    tmp, tmpl = torch.empty_like(acc), torch.empty_like(accl)
+    ring_step(srt, q, k, v, table, out, lse, acc, accl, tmp, tmpl, w.chunks)
+    torch.cuda.synchronize()
+    ranges = _row_ranges(w.N, w.seed, chunk=C, n_random=8)
+    wo, wl = _check_rows(w, q, k, v, out, lse, ranges)
+    print(f"c4 ring: max|dO|={wo:.3g} max|dlse|={wl:.3g}", flush=True)
+    assert wo <= TOL and wl <= TOL
+
+
+def test_decode_full_size():
+    """B=16 sequences, 131072-position rotated cache (PI s=16), 64 splits; sampled (b, kv head) groups."""
+    srt = need_gpu()
+    w = synth.WORKLOADS["c5"]
+    D, N = w.D, w.N
+    q = synth.randn((w.B, w.Hq, D), w.dtype, w.seed, synth.Q_ID, "cuda")
+    k = synth.randn((w.B, w.Hkv, N, D), w.dtype, w.seed, synth.K_ID, "cuda")
+    v = synth.randn((w.B, w.Hkv, N, D), w.dtype, w.seed, synth.V_ID, "cuda")
+    table, _ = device_table(srt, w.rope, D, N)
+    kc = srt.rope_apply(k, table)
+    o, l = srt.attn_decode_splitk(q, kc, v, num_splits=w.splits, table=table)
+    torch.cuda.synchronize()
+    th, ms, _ = oracle_freq(w.rope, D)
+    G = w.Hq // w.Hkv
+    worst_o = worst_l = 0.0
+    for b, hk in ((0, 0), (7, 3), (15, 7)):
+        kr = orope.rotate(f64(k[b, hk]), np.arange(N), th, ms)
+        hs = slice(hk * G, (hk + 1) * G)
+        ro, rl = A.decode(f64(q[b:b + 1, hs]), kr[None, None], f64(v[b, hk])[None, None],
+                          sm_scale=w.sm_scale, theta=th, mscale=ms)
+        worst_o = max(worst_o, max_abs(f64(o[b, hs]), ro[0]))
+        worst_l = max(worst_l, max_abs(f64(l[b, hs]), rl[0]))
+    print(f"c5 decode: max|dO|={worst_o:.3g} max|dlse|={worst_l:.3g}", flush=True)
+    assert worst_o <= TOL and worst_l <= TOL
