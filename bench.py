@@ -6,9 +6,11 @@
 Prints ONE JSON line.  The headline ``value`` is causal prefill TFLOP/s on the
 YaRN 32K workload (B=1, 32 query / 8 KV heads, D=128, N=32768, bf16, base
 1e4, L=2048, s=16, alpha=1, beta=32); a step is one pass of the prefill path
-over that input: the cos/sin table for the 32768 positions, then the fused
-kernel that rotates q and k on load and runs the tiled online softmax.  Inputs
-are resident in HBM before timing starts.  The same line carries:
+over that input: the cos/sin table for the 32768 positions, K rotated once
+(rope_apply into a scratch buffer), then the fused kernel that rotates q on
+load and runs the tiled online softmax (--rotate-k-on-load rotates K inside
+the kernel instead).  Inputs are resident in HBM before timing starts.  The
+same line carries:
 
   * ``roofline``: the prefill kernel's algorithmic flops / its mean launch
     time (HIP events on the launch stream) against the bf16 dense MFMA peak,
@@ -219,9 +221,12 @@ def bench_ring(srt, torch, w, steps, warmup):
     tmp = torch.empty_like(acc)
     tmp_l = torch.empty_like(acc_l)
 
+    krot = torch.empty_like(k)
+
     def step():
         table = srt.rope_cos_sin(th, D, ms, N, "cuda")
-        ring_step(srt, q, k, v, table, out, lse, acc, acc_l, tmp, tmp_l, w.chunks)
+        srt.rope_apply(k, table, out=krot)             # K rotated once at its absolute positions
+        ring_step(srt, q, krot, v, table, out, lse, acc, acc_l, tmp, tmp_l, w.chunks, srt.ROTATE_Q)
 
     for _ in range(warmup):
         step()
@@ -239,21 +244,24 @@ def bench_ring(srt, torch, w, steps, warmup):
             "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
 
 
-def ring_step(srt, q, k, v, table, out, lse, acc, acc_l, tmp, tmp_l, chunks):
+def ring_step(srt, q, k, v, table, out, lse, acc, acc_l, tmp, tmp_l, chunks, rope_flags=None):
     """Query chunk i attends K/V chunks 0..i at their absolute offsets; partial
-    states (fp32) are merged by log-sum-exp; the last merge writes bf16 output."""
+    states (fp32) are merged by log-sum-exp; the last merge writes bf16 output.
+    rope_flags=ROTATE_Q when k is already rotated; None rotates q and k on load."""
     N = q.shape[2]
     C = N // chunks
     for i in range(chunks):
         qi = q[:, :, i * C:(i + 1) * C]
         oi, li = out[:, :, i * C:(i + 1) * C], lse[:, :, i * C:(i + 1) * C]
         if i == 0:
-            srt.attn_prefill(qi, k[:, :, :C], v[:, :, :C], q_pos0=0, k_pos0=0, table=table, out=oi, lse=li)
+            srt.attn_prefill(qi, k[:, :, :C], v[:, :, :C], q_pos0=0, k_pos0=0, table=table, out=oi, lse=li,
+                             rope_flags=rope_flags)
             continue
         for j in range(i + 1):
             kj, vj = k[:, :, j * C:(j + 1) * C], v[:, :, j * C:(j + 1) * C]
             dst, dst_l = (acc, acc_l) if j == 0 else (tmp, tmp_l)
-            srt.attn_prefill(qi, kj, vj, q_pos0=i * C, k_pos0=j * C, table=table, out=dst, lse=dst_l)
+            srt.attn_prefill(qi, kj, vj, q_pos0=i * C, k_pos0=j * C, table=table, out=dst, lse=dst_l,
+                             rope_flags=rope_flags)
             if j == 0:
                 continue
             if j < i:
@@ -323,7 +331,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c3", choices=["c2", "c3"])
-    ap.add_argument("--prerotate-k", action="store_true", help="rotate K once with rope_apply, q on load")
+    ap.add_argument("--rotate-k-on-load", action="store_true",
+                    help="rotate K inside the prefill kernel at every tile load (default: once, with rope_apply)")
     ap.add_argument("--no-extras", action="store_true", help="skip the decode and ring legs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -344,7 +353,7 @@ def main():
     import synth
 
     w = synth.WORKLOADS[args.workload]
-    p = bench_prefill(srt, torch, w, args.steps, args.warmup, args.prerotate_k)
+    p = bench_prefill(srt, torch, w, args.steps, args.warmup, not args.rotate_k_on_load)
     traffic, traffic_note = traffic_from_counters()
     roof = {"bound": "mfma", "achieved": round(p["tflops_kernel"], 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(p["tflops_kernel"] / PEAK_BF16_TFLOPS, 4),
@@ -356,9 +365,9 @@ def main():
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic",
             "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "D": w.D,
-                       "causal": True, "rope": w.note, "step": ("cos/sin table + prefill (K pre-rotated)"
-                                                               if args.prerotate_k else
-                                                               "cos/sin table + prefill rotating q,k on load")},
+                       "causal": True, "rope": w.note, "step": ("cos/sin table + prefill rotating q and k on load"
+                                                               if args.rotate_k_on_load else
+                                                               "cos/sin table + rope_apply(k) + prefill rotating q on load")},
             "roofline": roof}
     if not args.no_extras:
         torch.cuda.empty_cache()

@@ -100,6 +100,19 @@ __device__ inline i16x4 ds_read_tr(const __hip_bfloat16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
 }
 
+// Lanes l and l ^ 32 hold the same query (different keys).  v_permlane32_swap
+// of a value with itself leaves the lower half's values in the first result and
+// the upper half's in the second, in every lane, so their max / sum combines
+// the pair without a trip through LDS.
+__device__ inline float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <bool ROT_K>
 __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a) {
   __shared__ Smem sm;
@@ -256,7 +269,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
 #pragma unroll
       for (int j = 3; j < 15; j += 2) mx = fmaxf(fmaxf(mx, sacc[j]), sacc[j + 1]);
       mx = fmaxf(mx, sacc[15]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * cscale;
+      mx = pair_max(mx) * cscale;
       // lazy rescale: only when some lane's maximum grew by more than 2^kLazy
       if (__any(mx > m_run + kLazy)) {
         const float mnew = fmaxf(m_run, mx);
@@ -308,7 +321,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   }
 
   // ---- epilogue: combine the two lane halves' sums, normalise, write O and lse
-  const float lt = l_run + __shfl_xor(l_run, 32);
+  const float lt = pair_sum(l_run);
   const int row = wrow0 + l32;
   if (row < a.Nq) {
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
