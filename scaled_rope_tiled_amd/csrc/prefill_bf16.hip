@@ -6,24 +6,25 @@
 // applied to q and k as they are loaded ("Long Context: RoPE / YaRN / NTK /
 // MLA" §2.4 rope_attention; the YaRN temperature travels in the table, §6.4).
 //
-// Work decomposition (one workgroup = 4 waves = 256 threads)
-//   * A workgroup owns one KV head and 64 * (4 / HPW) query rows of HPW query
-//     heads of its GQA group (HPW = min(Hq/Hkv, 4)): the K/V tiles staged in
-//     LDS are shared by all four waves, i.e. by up to four query heads.
-//   * Wave w owns 64 query rows of one head and keeps them in registers:
+// Work decomposition (one workgroup = 8 waves = 512 threads, two per SIMD)
+//   * A workgroup owns one KV head and 32 * (8 / HPW) query rows of HPW query
+//     heads of its GQA group (HPW = min(Hq/Hkv, 4)): every K/V tile staged in
+//     LDS serves all eight waves, i.e. up to four query heads.
+//   * Wave w owns 32 query rows of one head and keeps them in registers:
 //     rotated q as the B operand of S^T = K Q^T, the output as O^T (fp32).
 //   * The grid's x index is the KV head (fastest), so consecutive workgroups,
 //     which the dispatcher spreads round-robin over the 8 XCDs, keep one head
 //     per XCD L2; the y index walks query tiles from the last (most keys under
 //     the causal mask) to the first, so the long tiles start first.
-//   * Key tiles wholly above the causal diagonal are never visited; only tiles
-//     that cross the diagonal (or the ragged end of K) evaluate the mask.
+//   * Key tiles wholly above the causal diagonal are never visited; only the
+//     32-key halves that cross the diagonal (or the ragged end of K) evaluate
+//     the mask, one integer compare per score.
 //
 // Matrix-core mapping (v_mfma_f32_32x32x16_bf16, wave64)
 //   S^T[keys][queries] = K[keys][d] Q^T[d][queries]: A = 32x16 block of K read
 //   from LDS (16 bytes per lane), B = Q^T from registers; the accumulator puts
 //   one query per lane (lane & 31) with 16 of its keys, so the row max and row
-//   sum of the softmax are in-lane, plus one exchange with lane ^ 32.
+//   sum of the softmax are in-lane, plus one v_permlane32_swap with lane ^ 32.
 //   O^T[d][queries] = V^T[d][keys] P^T[keys][queries]: B = P^T comes straight
 //   from the S^T accumulator (converted to bf16) because the contraction over
 //   keys may use any key order as long as A uses the same one; A = V^T is read
@@ -34,13 +35,20 @@
 //   grows by more than 2^8 (exact for any reference maximum; the bound keeps
 //   e^(s - m) <= 2^8 so bf16/fp32 stay far from overflow).
 //
-// Staging: each thread moves four 16-byte chunks of K and of V per 64-key
-// tile (16 threads per 256-byte row: fully coalesced), rotating K in fp32 on
-// the way when asked.  LDS is double-buffered: the next tile's global loads are
-// issued before the current tile's matrix work and stored after it, one
-// barrier per tile.  Row strides are padded (K: 272 B, V: 320 B) so the 16-byte
-// K reads and the transposing V reads of a wave hit distinct LDS banks.
+// Pipeline: the key range is walked in 32-key halves.  Step h issues PV of
+// half h-1 and QK of half h+1 (matrix work) next to the softmax of half h
+// (VALU work that depends on neither), as one basic block, so a wave's
+// exponentials overlap its own MFMAs as well as the other wave's on the SIMD.
+//
+// Staging: each thread moves two 16-byte chunks of K and of V per 64-key tile
+// (16 threads per 256-byte row: fully coalesced), rotating K in fp32 on the
+// way when asked.  Tiles rotate through three LDS buffers with one barrier per
+// tile; the next tile's global loads are in flight during two steps.  Row
+// strides are padded (K: 272 B, V: 320 B) so the 16-byte K reads and the
+// transposing V reads of a wave hit distinct LDS banks.
 #include "srt_internal.h"
+
+#include <type_traits>
 
 namespace srt {
 namespace {
@@ -63,8 +71,8 @@ constexpr float kLazy = 8.0f;     // rescale threshold (log2 units)
 constexpr int kStageRows = kBN * 16 / kThreads;   // 16-byte chunks per thread per tile and tensor
 
 struct Smem {
-  __hip_bfloat16 k[2][kBN * kKStr];
-  __hip_bfloat16 v[2][kBN * kVStr];
+  __hip_bfloat16 k[3][kBN * kKStr];
+  __hip_bfloat16 v[3][kBN * kVStr];
 };
 
 __device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -93,11 +101,24 @@ __device__ inline uint4 rotate_chunk(uint4 w, float4 t0, float4 t1) {
 
 __device__ inline bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(bf16x8, w); }
 
+// LDS operands are addressed with 32-bit LDS byte addresses.  `opaque` hides a
+// step's base address from the loop optimisers, so every read of the step is
+// that one base register plus an immediate offset (no per-read arithmetic).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const u32x4_t lds_u4;
+__device__ inline uint32_t lds_off(const void* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
+}
+__device__ inline uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+__device__ inline bf16x8 lds_read16(uint32_t addr) { return __builtin_bit_cast(bf16x8, *(lds_u4*)(uintptr_t)addr); }
 // gfx950 transposing LDS read: each lane fetches 8 bytes at its address, then
 // within every 16 lanes, lane i receives element (i & 3) of the values fetched
 // by lanes 4t + (i >> 2), t = 0..3.
-__device__ inline i16x4 ds_read_tr(const __hip_bfloat16* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+__device__ inline i16x4 lds_read_tr(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)addr);
 }
 
 // Lanes l and l ^ 32 hold the same query (different keys).  v_permlane32_swap
@@ -179,25 +200,21 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   uint4 kbuf[kStageRows], vbuf[kStageRows];
   float4 tbuf[kStageRows][2];
 
+  // Branch-free: rows past Nk read row Nk-1 (always valid when a tile exists) and are zeroed.
   auto issue_loads = [&](int key0) {
 #pragma unroll
     for (int i = 0; i < kStageRows; ++i) {
       const int key = key0 + sr + (kThreads / 16) * i;
-      if (key < a.Nk) {
-        kbuf[i] = *reinterpret_cast<const uint4*>(kg + (long long)key * kD + sc * 8);
-        vbuf[i] = *reinterpret_cast<const uint4*>(vg + (long long)key * kD + sc * 8);
-        if (ROT_K) {
-          const float4* t = tab4 + ((a.k_pos0 + key) * (kD / 2) + sc * 4) / 2;
-          tbuf[i][0] = t[0];
-          tbuf[i][1] = t[1];
-        }
-      } else {
-        kbuf[i] = make_uint4(0, 0, 0, 0);
-        vbuf[i] = make_uint4(0, 0, 0, 0);
-        if (ROT_K) {
-          tbuf[i][0] = make_float4(0.f, 0.f, 0.f, 0.f);
-          tbuf[i][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+      const bool in = key < a.Nk;
+      const int kc = in ? key : a.Nk - 1;
+      const uint4 kw = *reinterpret_cast<const uint4*>(kg + (long long)kc * kD + sc * 8);
+      const uint4 vw = *reinterpret_cast<const uint4*>(vg + (long long)kc * kD + sc * 8);
+      kbuf[i] = in ? kw : make_uint4(0, 0, 0, 0);
+      vbuf[i] = in ? vw : make_uint4(0, 0, 0, 0);
+      if (ROT_K) {
+        const float4* t = tab4 + ((a.k_pos0 + kc) * (kD / 2) + sc * 4) / 2;
+        tbuf[i][0] = t[0];
+        tbuf[i][1] = t[1];
       }
     }
   };
@@ -231,93 +248,139 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   const int gj = lane & 15;
   const int gd = ((lane >> 4) & 1) * 16 + 4 * (gj & 3);    // d offset inside a 32-wide block
 
+  // ---- building blocks on one 32-key half of a K/V tile in LDS.  Buffer
+  // index and half are compile-time constants, so every LDS address is a
+  // per-lane base plus an immediate offset.
+  const uint32_t k_lane = lds_off(&sm.k[0][l32 * kKStr + hl * 8]);
+  const uint32_t v_lane = lds_off(&sm.v[0][(hl * 4 + (gj >> 2)) * kVStr + gd]);
+  // S^T = K Q^T: 8 d-steps of one 32x32x16 MFMA
+  auto qk = [&](int buf, auto kb, f32x16& acc) {
+    constexpr int KB = decltype(kb)::value;
+    const uint32_t kl = opaque(k_lane + buf * (kBN * kKStr * 2)) + KB * 32 * kKStr * 2;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 ka = lds_read16(kl + ks * 32);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], acc, 0, 0, 0);
+    }
+  };
+  // O^T += V^T P^T: 4 d blocks x 2 key steps of 16
+  auto pv = [&](const bf16x8 (&pb)[2], int buf, auto kb) {
+    constexpr int KB = decltype(kb)::value;
+    const uint32_t vl = opaque(v_lane + buf * (kBN * kVStr * 2)) + KB * 32 * kVStr * 2;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const i16x4 lo = lds_read_tr(vl + ((half * 16) * kVStr + db * 32) * 2);
+        const i16x4 hi = lds_read_tr(vl + ((half * 16 + 8) * kVStr + db * 32) * 2);
+        const bf16x8 va = __builtin_bit_cast(
+            bf16x8, (__attribute__((__vector_size__(8 * sizeof(short)))) short){lo[0], lo[1], lo[2], lo[3], hi[0],
+                                                                               hi[1], hi[2], hi[3]});
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[half], oacc[db], 0, 0, 0);
+      }
+    }
+  };
+
+  f32x16 s_a, s_b;
+  bf16x8 p_a[2], p_b[2];
+  float alpha_prev = 1.f;
+  bool need_prev = false;
+
+  // One pipeline step on half h = 2t + kb: scores of half h arrive in s_in,
+  // the step computes QK(h+1) into s_out and PV(h-1) from p_in while the
+  // softmax of half h writes p_out.  The matrix work does not depend on the
+  // softmax, so with no branch in between the scheduler interleaves the wave's
+  // MFMAs with its VALU softmax.  A rescale of O decided by the softmax of half
+  // h is applied at the start of step h+1, after PV(h-1) and before PV(h).
+  auto step = [&](auto has_pv, int qbuf, auto qkb, int pbuf, auto pkb, int h, f32x16& s_in, f32x16& s_out,
+                  const bf16x8 (&p_in)[2], bf16x8 (&p_out)[2]) {
+    constexpr bool HAS_PV = decltype(has_pv)::value;
+    if (HAS_PV && need_prev) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha_prev;
+    }
+    const int key0h = h * 32;
+    if ((long long)key0h + 32 > wave_free_lim || key0h + 32 > a.Nk) {
+      const int rel = klim - (key0h + hl * 4);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s_in[j] = ((j >> 2) * 8 + (j & 3)) <= rel ? s_in[j] : -INFINITY;
+    }
+
+    // matrix work of this step (the QK of the half after the last one reads a
+    // buffer holding stale data; its result is never used)
+    qk(qbuf, qkb, s_out);
+    if (HAS_PV) pv(p_in, pbuf, pkb);
+
+    // online softmax of half h (branch-free)
+    float mx = fmaxf(fmaxf(s_in[0], s_in[1]), s_in[2]);
+#pragma unroll
+    for (int j = 3; j < 15; j += 2) mx = fmaxf(fmaxf(mx, s_in[j]), s_in[j + 1]);
+    mx = pair_max(fmaxf(mx, s_in[15])) * cscale;
+    const bool need = __any(mx > m_run + kLazy);
+    const float mnew = need ? fmaxf(m_run, mx) : m_run;
+    const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - mnew);
+    m_run = mnew;
+    const float mref = m_run == -INFINITY ? 0.f : m_run;
+    float lsum = 0.f;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s_in[half * 8 + 2 * i], cscale, -mref));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s_in[half * 8 + 2 * i + 1], cscale, -mref));
+        lsum += p0 + p1;
+        w[i] = pack2(p0, p1);
+      }
+      p_out[half] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+    }
+    l_run = fmaf(l_run, alpha, lsum);
+    alpha_prev = alpha;
+    need_prev = need;
+  };
+  // Tile t+1 goes into LDS buffer (t+1) % 3 at the end of step 2t; that buffer
+  // last served tile t-2, whose last reader (PV of step 2t-2) every wave has
+  // passed at the barrier closing step 2t-2.  Past the last tile the store
+  // writes stale registers into an unused buffer and the loads re-read row Nk-1.
+  auto tile_io = [&](int next_buf, int t) {
+    store_lds(next_buf);
+    __syncthreads();
+    issue_loads((t + 2) * kBN);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  using K0 = std::integral_constant<int, 0>;
+  using K1 = std::integral_constant<int, 1>;
+
   if (ntiles > 0) {
     issue_loads(0);
     store_lds(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const int key0 = t * kBN;
-    if (t + 1 < ntiles) issue_loads(key0 + kBN);
-    const __hip_bfloat16* kl = sm.k[buf];
-    const __hip_bfloat16* vl = sm.v[buf];
-    // wave-uniform: does any key of this tile need the mask for this wave?
-    const bool masked = (long long)key0 + kBN > wave_free_lim || key0 + kBN > a.Nk;
-
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      // ---- S^T = K Q^T for 32 keys: 8 d-steps
-      f32x16 sacc;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 ka =
-            as_bf16x8(*reinterpret_cast<const uint4*>(&kl[(kb * 32 + l32) * kKStr + ks * 16 + hl * 8]));
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], sacc, 0, 0, 0);
-      }
-
-      // ---- causal / ragged mask (uniform branch), row max
-      if (masked) {
-        const int rel = klim - (key0 + kb * 32 + hl * 4);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) sacc[j] = ((j >> 2) * 8 + (j & 3)) <= rel ? sacc[j] : -INFINITY;
-      }
-      float mx = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
-#pragma unroll
-      for (int j = 3; j < 15; j += 2) mx = fmaxf(fmaxf(mx, sacc[j]), sacc[j + 1]);
-      mx = fmaxf(mx, sacc[15]);
-      mx = pair_max(mx) * cscale;
-      // lazy rescale: only when some lane's maximum grew by more than 2^kLazy
-      if (__any(mx > m_run + kLazy)) {
-        const float mnew = fmaxf(m_run, mx);
-        const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - mnew);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
-        m_run = mnew;
-      }
-      const float mref = m_run == -INFINITY ? 0.f : m_run;
-      // ---- P = exp2(s * c - m), packed as the P^T operand of two 16-key steps
-      bf16x8 pb[2];
-      float lsum = 0.f;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        uint32_t w[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[half * 8 + 2 * i], cscale, -mref));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[half * 8 + 2 * i + 1], cscale, -mref));
-          lsum += p0 + p1;
-          w[i] = pack2(p0, p1);
-        }
-        pb[half] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
-      }
-      l_run += lsum;
-
-      // ---- O^T += V^T P^T : 4 d blocks x 2 key steps of 16
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int col = db * 32 + gd;
-          const int r1 = kb * 32 + half * 16 + hl * 4 + (gj >> 2);
-          const i16x4 lo = ds_read_tr(&vl[r1 * kVStr + col]);
-          const i16x4 hi = ds_read_tr(&vl[(r1 + 8) * kVStr + col]);
-          const bf16x8 va = __builtin_bit_cast(
-              bf16x8, (__attribute__((__vector_size__(8 * sizeof(short)))) short){lo[0], lo[1], lo[2], lo[3],
-                                                                                 hi[0], hi[1], hi[2], hi[3]});
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[half], oacc[db], 0, 0, 0);
-        }
-      }
-    }
-
-    if (t + 1 < ntiles) store_lds(buf ^ 1);
     __syncthreads();
+    issue_loads(kBN);
+    qk(0, K0{}, s_a);
+    step(F{}, 0, K1{}, 0, K0{}, 0, s_a, s_b, p_b, p_a);
+    tile_io(1, 0);
+    step(T{}, 1, K0{}, 0, K0{}, 1, s_b, s_a, p_a, p_b);
+    int cur = 1;                           // buffer of tile t = t % 3
+    for (int t = 1; t < ntiles; ++t) {
+      const int prev = cur == 0 ? 2 : cur - 1, next = cur == 2 ? 0 : cur + 1;
+      step(T{}, cur, K1{}, prev, K1{}, 2 * t, s_a, s_b, p_b, p_a);
+      tile_io(next, t);
+      step(T{}, next, K0{}, cur, K0{}, 2 * t + 1, s_b, s_a, p_a, p_b);
+      cur = next;
+    }
+    if (need_prev) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha_prev;
+    }
+    // the last step, 2(ntiles-1)+1, left P of the last half in p_b
+    pv(p_b, cur == 0 ? 2 : cur - 1, K1{});
   }
 
   // ---- epilogue: combine the two lane halves' sums, normalise, write O and lse
