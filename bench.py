@@ -72,10 +72,11 @@ def _sha(path: str) -> str:
 
 
 def _ensure_built():
-    from scaled_rope_tiled_amd import _lib
-    if not os.path.exists(_lib.LIB_PATH):
-        from scaled_rope_tiled_amd.build import build
-        build()
+    """Build libsrt.so only when it is absent (a built library is used as is)."""
+    lib = os.environ.get("SRT_LIB", os.path.join(ROOT, "scaled_rope_tiled_amd", "libsrt.so"))
+    if not os.path.exists(lib):
+        import __graft_entry__
+        __graft_entry__.build()
 
 
 class Timer:

@@ -20,7 +20,9 @@
  *     (b*H + h) * hstride.
  *   - dtype codes: SRT_F32 (float) or SRT_BF16 (bfloat16, round-to-nearest-even).
  *     Arithmetic is fp32 inside every kernel; bf16 is a storage type.
- *   - Pairing is interleaved: pair i is (x[2i], x[2i+1]) ([LC] §2.1, [NB] §5.1).
+ *   - Pairing is interleaved by default: pair i is (x[2i], x[2i+1]) ([LC] §2.1,
+ *     [NB] §5.1).  Half-split pairing, pair i = (x[i], x[i + D/2]) ([LC] §2.4
+ *     code), is selected per call (SRT_PAIR_HALF); the table is the same.
  *   - The cos/sin table (srt_rope_cos_sin) holds, for position p and pair i,
  *     the two floats mscale*cos(p*theta'_i), mscale*sin(p*theta'_i) at
  *     table[(p*(D/2) + i)*2 + {0,1}].  A row at absolute position p uses table
@@ -64,6 +66,11 @@ typedef enum { SRT_F32 = 0, SRT_BF16 = 1 } srt_dtype;
 /* rope_flags of srt_attn_prefill */
 #define SRT_ROTATE_Q 1      /* rotate q rows on load with table rows q_pos0 + r */
 #define SRT_ROTATE_K 2      /* rotate k rows on load with table rows k_pos0 + c */
+#define SRT_PAIR_HALF 4     /* half-split pairs (x[i], x[i + D/2]) instead of interleaved */
+
+/* pairing argument of srt_rope_apply and srt_attn_decode_splitk */
+#define SRT_PAIRING_INTERLEAVED 0
+#define SRT_PAIRING_HALF 1
 
 /* band labels written by srt_rope_inv_freq ([BK] §8.3.3) */
 #define SRT_BAND_LOW 0      /* r(d) <  alpha : gamma = 1/s (interpolated)  */
@@ -102,6 +109,27 @@ int srt_rope_inv_freq(int method, double base, double s, double L, double alpha,
                       double* inv_freq_out_host, double* mscale_out_host, signed char* band_out_host);
 
 /*
+ * srt_rope_inv_freq_dynamic_ntk - NTK-aware frequencies with the scale taken
+ * from the actual sequence length (host only, fp64).
+ *
+ * Dynamic NTK adjusts the base from the length seen at inference ("AI Day 9:
+ * 长上下文技术", Dynamic NTK).  Reading: s = max(1, seq_len / L), then
+ * theta'_d = b'^(-2d/D) with b' = base * s^(D/(D-2)) as in srt_rope_inv_freq
+ * (NTK); a sequence no longer than L keeps the original frequencies.
+ * base > 0; seq_len >= 0; L > 0; D even, 4 <= D <= 256.  inv_freq_out_host:
+ * D/2 doubles (required); s_out_host: optional.
+ */
+int srt_rope_inv_freq_dynamic_ntk(double base, long long seq_len, double L, int D, double* inv_freq_out_host,
+                                  double* s_out_host);
+
+/*
+ * srt_rope_inv_freq_factors - per-pair factors: theta'_d = base^(-2d/D) / lambda_d
+ * ([LC] §7.3, the LongRoPE search space; the search itself is out of scope).
+ * lambda_host: D/2 positive finite doubles.  inv_freq_out_host: D/2 doubles.
+ */
+int srt_rope_inv_freq_factors(double base, const double* lambda_host, int D, double* inv_freq_out_host);
+
+/*
  * srt_rope_cos_sin - cos/sin table for positions [0, npos) (GPU kernel).
  *
  * table_dev[(p*(D/2) + i)*2 + 0] = mscale*cos(p*theta'_i),
@@ -121,12 +149,14 @@ int srt_rope_cos_sin(const double* inv_freq_host, int D, double mscale, long lon
  *
  * y_{2i} = x_{2i} c - x_{2i+1} s,  y_{2i+1} = x_{2i} s + x_{2i+1} c with (c, s)
  * the table entry of row r's position pos0 + r ([LC] §2.2, [NB] §4.2); the
- * table already carries mscale.  Used to build a rotated KV cache and to
- * pre-rotate K.  x, y: device, contiguous, dtype; y may equal x (in place).
+ * table already carries mscale.  With pairing = SRT_PAIRING_HALF the pair is
+ * (x_i, x_{i+D/2}) instead ([LC] §2.4).  Used to build a rotated KV cache and
+ * to pre-rotate K.  x, y: device, contiguous, 16-byte aligned, dtype; y may
+ * equal x (in place).  D a multiple of 8 (of 16 for half-split).
  * Requires 0 <= pos0 and pos0 + N <= table_npos.
  */
 int srt_rope_apply(const void* x, void* y, int dtype, int B, int H, int N, int D, long long pos0,
-                   const float* table_dev, long long table_npos, void* stream);
+                   const float* table_dev, long long table_npos, int pairing, void* stream);
 
 /*
  * srt_attn_prefill - tiled online-softmax attention with rotate-on-load RoPE.
@@ -136,7 +166,8 @@ int srt_rope_apply(const void* x, void* y, int dtype, int B, int H, int N, int D
  * position k_pos0 + c <= q_pos0 + r (all keys if causal == 0);
  * O_r = softmax(s) V, lse_r = log sum exp(s) ([LC] §2.4).  q~ / k~ are the
  * rows rotated with the table (carrying the YaRN mscale) when rope_flags has
- * SRT_ROTATE_Q / SRT_ROTATE_K, else used as given.  Scores are produced tile by
+ * SRT_ROTATE_Q / SRT_ROTATE_K, else used as given; SRT_PAIR_HALF selects the
+ * half-split pairing for both.  Scores are produced tile by
  * tile with the online softmax (running max and sum, rescaled accumulator:
  * [BK] §8.3.4 (1)-(2)); tiles wholly above the causal diagonal are skipped.
  *
@@ -183,7 +214,8 @@ int srt_attn_decode_workspace_size(int B, int Hq, int D, int num_splits, size_t*
  *
  * Every decode step reads the whole K/V cache ([LC] §12.3; [PL] KV-cache
  * notes).  Query q[b][h] (raw, [B][Hq][D]) is rotated at position
- * seq_len_b - 1 with the table (skipped if table_dev is NULL); the cache holds
+ * seq_len_b - 1 with the table (skipped if table_dev is NULL), pairs chosen by
+ * `pairing` (SRT_PAIRING_INTERLEAVED or SRT_PAIRING_HALF); the cache holds
  * keys already rotated at their positions (built with srt_rope_apply).  The
  * keys [0, seq_len_b) are cut into num_splits blocks of ceil(Nk/num_splits);
  * a first kernel computes each block's partial (O, lse) into the workspace,
@@ -198,7 +230,7 @@ int srt_attn_decode_workspace_size(int B, int Hq, int D, int num_splits, size_t*
 int srt_attn_decode_splitk(const void* q, const void* k_cache, const void* v_cache, int dtype,
                            int B, int Hq, int Hkv, int Nk, int D, const int* seq_lens_dev,
                            int num_splits, float sm_scale, const float* table_dev, long long table_npos,
-                           void* workspace, size_t workspace_bytes,
+                           int pairing, void* workspace, size_t workspace_bytes,
                            void* out, float* lse, void* stream);
 
 #ifdef __cplusplus

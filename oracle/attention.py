@@ -35,14 +35,24 @@ def _f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
+def _rotator(pairing: str):
+    if pairing == "interleaved":
+        return _rope.rotate
+    if pairing == "half":
+        return _rope.rotate_half
+    raise ValueError(f"unknown pairing {pairing}")
+
+
 def attention(q, k, v, *, sm_scale: float, causal: bool = True, q_pos0: int = 0, k_pos0: int = 0,
-              theta=None, mscale: float = 1.0, rows=None, block: int = 256):
+              theta=None, mscale: float = 1.0, rows=None, block: int = 256, pairing: str = "interleaved"):
     """Softmax attention with RoPE applied to q and k.
 
     q: [B, Hq, Nq, D]; k, v: [B, Hkv, Nk, D].  theta=None means q and k are
     used as given (already rotated).  ``rows`` (optional int array) restricts
-    the computation to those query rows.  Returns (O [B, Hq, R, D], lse [B, Hq, R]).
+    the computation to those query rows.  ``pairing`` picks interleaved pairs
+    (default) or half-split pairs.  Returns (O [B, Hq, R, D], lse [B, Hq, R]).
     """
+    rot = _rotator(pairing)
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, Hq, Nq, D = q.shape
     _, Hkv, Nk, _ = k.shape
@@ -56,13 +66,13 @@ def attention(q, k, v, *, sm_scale: float, causal: bool = True, q_pos0: int = 0,
     kpos = k_pos0 + np.arange(Nk)
     for b in range(B):
         for hk in range(Hkv):
-            kt = k[b, hk] if theta is None else _rope.rotate(k[b, hk], kpos, theta, mscale)
+            kt = k[b, hk] if theta is None else rot(k[b, hk], kpos, theta, mscale)
             vv = v[b, hk]
             for h in range(hk * g, (hk + 1) * g):
                 for r0 in range(0, R, block):
                     rr = rows[r0:r0 + block]
                     qpos = q_pos0 + rr
-                    qt = q[b, h, rr] if theta is None else _rope.rotate(q[b, h, rr], qpos, theta, mscale)
+                    qt = q[b, h, rr] if theta is None else rot(q[b, h, rr], qpos, theta, mscale)
                     s = sm_scale * (qt @ kt.T)                              # [r, Nk]
                     if causal:
                         s = np.where(kpos[None, :] <= qpos[:, None], s, -np.inf)
@@ -148,7 +158,8 @@ def merge(o_a, lse_a, o_b, lse_b):
     return wa[..., None] * o_a + wb[..., None] * o_b, lse
 
 
-def decode(q, k_cache_rotated, v_cache, *, sm_scale: float, seq_lens=None, theta=None, mscale: float = 1.0):
+def decode(q, k_cache_rotated, v_cache, *, sm_scale: float, seq_lens=None, theta=None, mscale: float = 1.0,
+           pairing: str = "interleaved"):
     """One new query per sequence against its cache (already rotated keys).
 
     q: [B, Hq, D] raw, rotated at position seq_len - 1 (the new token's own
@@ -168,7 +179,7 @@ def decode(q, k_cache_rotated, v_cache, *, sm_scale: float, seq_lens=None, theta
             continue
         qb = q[b][:, None, :]                                   # [Hq, 1, D]
         if theta is not None:
-            qb = _rope.rotate(qb, np.array([n - 1]), theta, mscale)
+            qb = _rotator(pairing)(qb, np.array([n - 1]), theta, mscale)
         o, l = attention(qb[None], kc[b:b + 1, :, :n], vc[b:b + 1, :, :n], sm_scale=sm_scale,
                          causal=False, theta=None)
         out[b] = o[0, :, 0]

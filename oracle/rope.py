@@ -152,3 +152,50 @@ def over_extrapolated_range(D: int, L: float, s: float, base: float = 10000.0):
     lower = D / 2.0 * math.log(L / (2.0 * math.pi)) / math.log(base)
     upper = (D - 2) / 2.0 * math.log((Lp - 1.0) / (L - 1.0)) / math.log(s)
     return lower, upper
+
+
+# --------------------------------------------------------------------------- frequency-step variants
+
+def rotate_half(x: np.ndarray, pos, theta: np.ndarray, mscale: float = 1.0) -> np.ndarray:
+    """Half-split pairing: pair i is (x_i, x_{i+D/2}), turned by p * theta_i.
+
+    "Long Context: RoPE / YaRN / NTK / MLA" §2.4 (apply_rope: the first and the
+    second half of the row form the real and imaginary parts; the page notes it
+    is the interleaved rule up to a permutation of the dimensions).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    h = x.shape[-1] // 2
+    pos = np.asarray(pos, dtype=np.float64)
+    a = pos[:, None] * np.asarray(theta, dtype=np.float64)[None, :]
+    c, s = np.cos(a), np.sin(a)
+    x1, x2 = x[..., :h], x[..., h:]
+    return mscale * np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c], axis=-1)
+
+
+def dynamic_ntk_scale(seq_len: float, L: float) -> float:
+    """Dynamic NTK: the scale follows the actual sequence length at inference.
+
+    "AI Day 9: 长上下文技术" (Dynamic NTK: the base is adjusted from the actual
+    length; short sequences lose nothing).  Reading: s = max(1, N / L) fed to
+    the NTK-aware base change, so N <= L keeps the original base.
+    """
+    return max(1.0, float(seq_len) / float(L))
+
+
+def inv_freq_dynamic_ntk(base: float, seq_len: float, L: float, D: int) -> np.ndarray:
+    s = dynamic_ntk_scale(seq_len, L)
+    return base_inv_freq(D, ntk_base(base, s, D))
+
+
+def inv_freq_factors(base: float, lambdas, D: int) -> np.ndarray:
+    """Per-dimension factors: theta'_i = theta_i / lambda_i.
+
+    "Long Context: RoPE / YaRN / NTK / MLA" §7.3 (LongRoPE's search space; the
+    search itself needs a trained model and is not part of this oracle).
+    """
+    lam = np.asarray(lambdas, dtype=np.float64)
+    if lam.shape != (D // 2,):
+        raise ValueError("one factor per pair")
+    if not (lam > 0).all():
+        raise ValueError("factors must be positive")
+    return base_inv_freq(D, base) / lam

@@ -6,8 +6,10 @@ argument marshalling only: torch tensors provide device memory and the current
 HIP stream; every step of the computation runs in the library's kernels.
 
     rope_inv_freq(method, base, s, L, alpha, beta, D) -> (theta', mscale, band)
+    rope_inv_freq_dynamic_ntk(base, seq_len, L, D)    -> (theta', s)
+    rope_inv_freq_factors(base, lambdas, D)           -> theta'
     rope_cos_sin(theta', D, mscale, npos, device)     -> table [npos, D/2, 2] fp32
-    rope_apply(x, table, pos0=0, out=None)            -> rotated x
+    rope_apply(x, table, pos0=0, out=None, pairing=) -> rotated x
     attn_prefill(q, k, v, ...)                        -> (out, lse)
     attn_merge_states(o_a, lse_a, o_b, lse_b, ...)    -> (out, lse)
     attn_decode_splitk(q, k_cache, v_cache, ...)      -> (out, lse)
@@ -24,12 +26,13 @@ from . import _lib
 
 NONE, PI, NTK, YARN = 0, 1, 2, 3
 F32, BF16 = 0, 1
-ROTATE_Q, ROTATE_K = 1, 2
+ROTATE_Q, ROTATE_K, PAIR_HALF = 1, 2, 4
+PAIRING_INTERLEAVED, PAIRING_HALF = 0, 1
 BAND_LOW, BAND_MID, BAND_HIGH = 0, 1, 2
 
-__all__ = ["rope_inv_freq", "rope_cos_sin", "rope_apply", "attn_prefill", "attn_merge_states",
+__all__ = ["rope_inv_freq", "rope_inv_freq_dynamic_ntk", "rope_inv_freq_factors", "rope_cos_sin", "rope_apply", "attn_prefill", "attn_merge_states",
            "attn_decode_splitk", "attn_decode_workspace_size", "NONE", "PI", "NTK", "YARN",
-           "ROTATE_Q", "ROTATE_K", "lib"]
+           "ROTATE_Q", "ROTATE_K", "PAIR_HALF", "PAIRING_INTERLEAVED", "PAIRING_HALF", "lib"]
 
 
 def lib():
@@ -85,6 +88,34 @@ def rope_inv_freq(method: int, base: float, s: float = 1.0, L: float = 0.0, alph
     return np.frombuffer(th, dtype=np.float64).copy(), ms.value, np.frombuffer(band, dtype=np.int8).copy()
 
 
+def rope_inv_freq_dynamic_ntk(base: float, seq_len: int, L: float, D: int = 128):
+    """NTK-aware frequencies with s = max(1, seq_len / L).  Returns (theta' [D/2] float64, s)."""
+    th = (C.c_double * (D // 2))()
+    s = C.c_double()
+    _lib.check(lib().srt_rope_inv_freq_dynamic_ntk(float(base), int(seq_len), float(L), int(D), th, C.byref(s)),
+               "rope_inv_freq_dynamic_ntk")
+    return np.frombuffer(th, dtype=np.float64).copy(), s.value
+
+
+def rope_inv_freq_factors(base: float, lambdas, D: int = 128):
+    """theta'_d = base^(-2d/D) / lambda_d.  Returns theta' [D/2] float64."""
+    lam = np.ascontiguousarray(np.asarray(lambdas, dtype=np.float64))
+    if lam.shape != (D // 2,):
+        raise ValueError("one factor per pair (D/2 entries)")
+    th = (C.c_double * (D // 2))()
+    _lib.check(lib().srt_rope_inv_freq_factors(float(base), lam.ctypes.data_as(C.POINTER(C.c_double)), int(D), th),
+               "rope_inv_freq_factors")
+    return np.frombuffer(th, dtype=np.float64).copy()
+
+
+def _pairing(p) -> int:
+    if p in (PAIRING_INTERLEAVED, "interleaved"):
+        return PAIRING_INTERLEAVED
+    if p in (PAIRING_HALF, "half"):
+        return PAIRING_HALF
+    raise ValueError(f"unknown pairing {p!r}")
+
+
 def rope_cos_sin(theta, D: int, mscale: float, npos: int, device="cuda") -> torch.Tensor:
     """Device table [npos, D/2, 2] fp32 of mscale*(cos, sin)(p*theta'_i)."""
     th = np.ascontiguousarray(np.asarray(theta, dtype=np.float64))
@@ -97,8 +128,10 @@ def rope_cos_sin(theta, D: int, mscale: float, npos: int, device="cuda") -> torc
     return table
 
 
-def rope_apply(x: torch.Tensor, table: torch.Tensor, pos0: int = 0, out: torch.Tensor | None = None):
-    """Rotate every row of x [B, H, N, D] (row r at position pos0 + r).  out may be x."""
+def rope_apply(x: torch.Tensor, table: torch.Tensor, pos0: int = 0, out: torch.Tensor | None = None,
+               pairing="interleaved"):
+    """Rotate every row of x [B, H, N, D] (row r at position pos0 + r).  out may be x.
+    pairing: "interleaved" (x_2i, x_2i+1) or "half" (x_i, x_i+D/2)."""
     if not x.is_contiguous():
         raise ValueError("x must be contiguous")
     out = torch.empty_like(x) if out is None else out
@@ -106,7 +139,7 @@ def rope_apply(x: torch.Tensor, table: torch.Tensor, pos0: int = 0, out: torch.T
         raise ValueError("out must match x")
     B, H, N, D = x.shape
     _lib.check(lib().srt_rope_apply(_ptr(x), _ptr(out), _dt(x), B, H, N, D, int(pos0), _ptr(table),
-                                    table.shape[0], _stream(x.device)), "rope_apply")
+                                    table.shape[0], _pairing(pairing), _stream(x.device)), "rope_apply")
     return out
 
 
@@ -117,7 +150,8 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, sm_scale:
     """Tiled causal attention with rotate-on-load RoPE.
 
     q [B, Hq, Nq, D], k/v [B, Hkv, Nk, D] (views sliced along N allowed).
-    rope_flags defaults to ROTATE_Q|ROTATE_K when a table is given.
+    rope_flags defaults to ROTATE_Q|ROTATE_K when a table is given; add
+    PAIR_HALF for half-split pairs.
     Returns (out [B, Hq, Nq, D], lse [B, Hq, Nq] fp32 or None)."""
     B, Hq, Nq, D = q.shape
     _, Hkv, Nk, _ = k.shape
@@ -183,7 +217,7 @@ def attn_decode_workspace_size(B: int, Hq: int, D: int, num_splits: int) -> int:
 
 def attn_decode_splitk(q, k_cache, v_cache, *, num_splits: int, sm_scale: float | None = None,
                        table: torch.Tensor | None = None, seq_lens: torch.Tensor | None = None,
-                       workspace: torch.Tensor | None = None, out=None, lse=True):
+                       workspace: torch.Tensor | None = None, out=None, lse=True, pairing="interleaved"):
     """Split-K decode.  q [B, Hq, D] raw (rotated at seq_len-1 when a table is given);
     k_cache/v_cache [B, Hkv, Nk, D] with rotated keys.  Returns (out [B, Hq, D], lse [B, Hq])."""
     B, Hq, D = q.shape
@@ -205,7 +239,8 @@ def attn_decode_splitk(q, k_cache, v_cache, *, num_splits: int, sm_scale: float 
     sm = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
     _lib.check(lib().srt_attn_decode_splitk(_ptr(q), _ptr(k_cache), _ptr(v_cache), _dt(q), B, Hq, Hkv, Nk, D,
                                             _ptr(seq_lens), int(num_splits), sm, _ptr(table),
-                                            0 if table is None else table.shape[0], _ptr(workspace),
+                                            0 if table is None else table.shape[0], _pairing(pairing),
+                                            _ptr(workspace),
                                             workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
                                             _stream(q.device)), "attn_decode_splitk")
     return out, lse

@@ -22,8 +22,11 @@ SIGNATURES = {
     "srt_last_error": [],
     "srt_rope_inv_freq": [c_int, c_double, c_double, c_double, c_double, c_double, c_int,
                           C.POINTER(c_double), C.POINTER(c_double), C.POINTER(C.c_byte)],
+    "srt_rope_inv_freq_dynamic_ntk": [c_double, c_ll, c_double, c_int, C.POINTER(c_double), C.POINTER(c_double)],
+    "srt_rope_inv_freq_factors": [c_double, C.POINTER(c_double), c_int, C.POINTER(c_double)],
     "srt_rope_cos_sin": [C.POINTER(c_double), c_int, c_double, c_ll, c_void_p, c_void_p],
-    "srt_rope_apply": [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_ll, c_void_p, c_ll, c_void_p],
+    "srt_rope_apply": [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_ll, c_void_p, c_ll, c_int,
+                       c_void_p],
     "srt_attn_prefill": [c_void_p, c_void_p, c_void_p, c_int,
                          c_int, c_int, c_int, c_int, c_int, c_int,
                          c_ll, c_ll, c_ll, c_ll, c_int, c_float,
@@ -35,7 +38,7 @@ SIGNATURES = {
     "srt_attn_decode_workspace_size": [c_int, c_int, c_int, c_int, C.POINTER(c_size_t)],
     "srt_attn_decode_splitk": [c_void_p, c_void_p, c_void_p, c_int,
                                c_int, c_int, c_int, c_int, c_int, c_void_p,
-                               c_int, c_float, c_void_p, c_ll,
+                               c_int, c_float, c_void_p, c_ll, c_int,
                                c_void_p, c_size_t, c_void_p, c_void_p, c_void_p],
 }
 
@@ -48,7 +51,7 @@ def load(path: str = LIB_PATH):
     if _lib is not None:
         return _lib
     if not os.path.exists(path):
-        raise ImportError(f"libsrt.so not built at {path}: run `python -m scaled_rope_tiled_amd.build`")
+        raise ImportError(f"libsrt.so not built at {path}: run `python scaled_rope_tiled_amd/build.py`")
     lib = C.CDLL(path)
     for name, args in SIGNATURES.items():
         fn = getattr(lib, name)

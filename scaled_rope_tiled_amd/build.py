@@ -1,6 +1,8 @@
 """Build libsrt.so (the C-ABI library) in-tree for gfx950 with hipcc.
 
-Usage: python -m scaled_rope_tiled_amd.build   (or build() from Python).
+Usage: python scaled_rope_tiled_amd/build.py   (or build() from Python).
+Run it as a script (or load it by path): importing the package first would
+load the library that is about to be replaced.
 Each translation unit compiles to _build/<name>.o in parallel, then one
 shared library is linked next to this file.
 """

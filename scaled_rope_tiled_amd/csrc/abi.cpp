@@ -102,6 +102,30 @@ int srt_rope_inv_freq(int method, double base, double s, double L, double alpha,
   return ok();
 }
 
+int srt_rope_inv_freq_dynamic_ntk(double base, long long seq_len, double L, int D, double* inv_freq_out,
+                                  double* s_out) {
+  if (!inv_freq_out) return fail(SRT_ERR_INVALID, "rope_inv_freq_dynamic_ntk: inv_freq_out is NULL");
+  if (seq_len < 0) return fail(SRT_ERR_INVALID, "rope_inv_freq_dynamic_ntk: seq_len < 0");
+  if (!(L > 0.0) || !std::isfinite(L)) return fail(SRT_ERR_INVALID, "rope_inv_freq_dynamic_ntk: L must be > 0");
+  if (D < 4) return fail(SRT_ERR_INVALID, "rope_inv_freq_dynamic_ntk: D must be >= 4");
+  // Dynamic NTK: the scale follows the length actually seen, never below 1.
+  const double s = (double)seq_len > L ? (double)seq_len / L : 1.0;
+  if (s_out) *s_out = s;
+  return srt_rope_inv_freq(SRT_ROPE_NTK, base, s, 0.0, 1.0, 2.0, D, inv_freq_out, nullptr, nullptr);
+}
+
+int srt_rope_inv_freq_factors(double base, const double* lambda, int D, double* inv_freq_out) {
+  if (!lambda || !inv_freq_out) return fail(SRT_ERR_INVALID, "rope_inv_freq_factors: NULL pointer");
+  if (D < 2 || D > 2 * srt::kMaxHalf || (D & 1))
+    return fail(SRT_ERR_INVALID, "rope_inv_freq_factors: D=%d must be even and in [2, %d]", D, 2 * srt::kMaxHalf);
+  if (!(base > 0.0) || !std::isfinite(base)) return fail(SRT_ERR_INVALID, "rope_inv_freq_factors: base must be > 0");
+  for (int d = 0; d < D / 2; ++d)
+    if (!(lambda[d] > 0.0) || !std::isfinite(lambda[d]))
+      return fail(SRT_ERR_INVALID, "rope_inv_freq_factors: lambda[%d] must be positive and finite", d);
+  for (int d = 0; d < D / 2; ++d) inv_freq_out[d] = std::pow(base, -2.0 * (double)d / (double)D) / lambda[d];
+  return ok();
+}
+
 int srt_rope_cos_sin(const double* inv_freq_host, int D, double mscale, long long npos, float* table_dev,
                      void* stream) {
   if (!inv_freq_host || !table_dev) return fail(SRT_ERR_INVALID, "rope_cos_sin: NULL pointer");
@@ -118,20 +142,24 @@ int srt_rope_cos_sin(const double* inv_freq_host, int D, double mscale, long lon
 }
 
 int srt_rope_apply(const void* x, void* y, int dtype, int B, int H, int N, int D, long long pos0,
-                   const float* table_dev, long long table_npos, void* stream) {
+                   const float* table_dev, long long table_npos, int pairing, void* stream) {
   if (!valid_dtype(dtype)) return fail(SRT_ERR_INVALID, "rope_apply: bad dtype %d", dtype);
   if (B < 0 || H < 0 || N < 0) return fail(SRT_ERR_INVALID, "rope_apply: negative size");
   if ((long long)B * H * N == 0) return ok();   // nothing to rotate: pointers may be NULL
   if (!x || !y || !table_dev) return fail(SRT_ERR_INVALID, "rope_apply: NULL pointer");
   if (D < 2 || (D & 1) || D > 2 * srt::kMaxHalf) return fail(SRT_ERR_INVALID, "rope_apply: bad D=%d", D);
+  if (pairing != SRT_PAIRING_INTERLEAVED && pairing != SRT_PAIRING_HALF)
+    return fail(SRT_ERR_INVALID, "rope_apply: bad pairing %d", pairing);
   if (D % 8) return fail(SRT_ERR_UNSUPPORTED, "rope_apply: D=%d must be a multiple of 8", D);
+  if (pairing == SRT_PAIRING_HALF && D % 16)
+    return fail(SRT_ERR_UNSUPPORTED, "rope_apply: half-split pairing needs D a multiple of 16 (D=%d)", D);
   if (pos0 < 0 || pos0 + N > table_npos)
     return fail(SRT_ERR_INVALID, "rope_apply: positions [%lld, %lld) outside table [0, %lld)", pos0,
                 pos0 + N, table_npos);
   if (misaligned16(x) || misaligned16(y) || misaligned16(table_dev))
     return fail(SRT_ERR_INVALID, "rope_apply: pointers must be 16-byte aligned");
-  return hip_status(srt::launch_rope_apply(x, y, dtype == SRT_BF16, (long long)B * H, N, D, pos0, table_dev,
-                                           (hipStream_t)stream),
+  return hip_status(srt::launch_rope_apply(x, y, dtype == SRT_BF16, pairing == SRT_PAIRING_HALF, (long long)B * H,
+                                           N, D, pos0, table_dev, (hipStream_t)stream),
                     "rope_apply launch");
 }
 
@@ -150,8 +178,10 @@ int srt_attn_prefill(const void* q, const void* k, const void* v, int dtype, int
   if (q_hstride < (long long)Nq * D || kv_hstride < (long long)Nk * D || o_hstride < (long long)Nq * D)
     return fail(SRT_ERR_INVALID, "attn_prefill: head stride smaller than N*D");
   if (lse && lse_hstride < Nq) return fail(SRT_ERR_INVALID, "attn_prefill: lse head stride smaller than Nq");
-  if (rope_flags & ~(SRT_ROTATE_Q | SRT_ROTATE_K)) return fail(SRT_ERR_INVALID, "attn_prefill: bad rope_flags");
-  if (rope_flags && !table_dev) return fail(SRT_ERR_INVALID, "attn_prefill: rope_flags set without a table");
+  if (rope_flags & ~(SRT_ROTATE_Q | SRT_ROTATE_K | SRT_PAIR_HALF))
+    return fail(SRT_ERR_INVALID, "attn_prefill: bad rope_flags");
+  if ((rope_flags & (SRT_ROTATE_Q | SRT_ROTATE_K)) && !table_dev)
+    return fail(SRT_ERR_INVALID, "attn_prefill: rope_flags set without a table");
   if (q_pos0 < 0 || k_pos0 < 0) return fail(SRT_ERR_INVALID, "attn_prefill: negative position offset");
   if ((rope_flags & SRT_ROTATE_Q) && q_pos0 + Nq > table_npos)
     return fail(SRT_ERR_INVALID, "attn_prefill: q positions [%lld, %lld) outside table [0, %lld)", q_pos0,
@@ -211,7 +241,7 @@ int srt_attn_decode_workspace_size(int B, int Hq, int D, int num_splits, size_t*
 
 int srt_attn_decode_splitk(const void* q, const void* k_cache, const void* v_cache, int dtype, int B, int Hq,
                            int Hkv, int Nk, int D, const int* seq_lens_dev, int num_splits, float sm_scale,
-                           const float* table_dev, long long table_npos, void* workspace,
+                           const float* table_dev, long long table_npos, int pairing, void* workspace,
                            size_t workspace_bytes, void* out, float* lse, void* stream) {
   if (!valid_dtype(dtype)) return fail(SRT_ERR_INVALID, "attn_decode_splitk: bad dtype");
   if (B < 0 || Hq < 1 || Hkv < 1 || Nk < 0) return fail(SRT_ERR_INVALID, "attn_decode_splitk: bad sizes");
@@ -221,6 +251,8 @@ int srt_attn_decode_splitk(const void* q, const void* k_cache, const void* v_cac
   if (Hq % Hkv) return fail(SRT_ERR_INVALID, "attn_decode_splitk: Hq not a multiple of Hkv");
   if (num_splits < 1 || num_splits > 1024) return fail(SRT_ERR_INVALID, "attn_decode_splitk: num_splits out of [1,1024]");
   if (D < 2 || (D & 1)) return fail(SRT_ERR_INVALID, "attn_decode_splitk: D must be even");
+  if (pairing != SRT_PAIRING_INTERLEAVED && pairing != SRT_PAIRING_HALF)
+    return fail(SRT_ERR_INVALID, "attn_decode_splitk: bad pairing %d", pairing);
   if (table_dev && table_npos < Nk)
     return fail(SRT_ERR_INVALID, "attn_decode_splitk: table has %lld positions, query may sit at %d", table_npos, Nk - 1);
   if (!std::isfinite(sm_scale)) return fail(SRT_ERR_INVALID, "attn_decode_splitk: sm_scale not finite");
@@ -240,6 +272,7 @@ int srt_attn_decode_splitk(const void* q, const void* k_cache, const void* v_cac
   if (B == 0) return ok();
   srt::DecodeArgs a{};
   a.q = q; a.k = k_cache; a.v = v_cache; a.seq_lens = seq_lens_dev; a.table = table_dev;
+  a.half_pairs = pairing == SRT_PAIRING_HALF;
   a.ws_o = (float*)workspace;
   a.ws_lse = (float*)((char*)workspace + (size_t)B * Hq * num_splits * D * sizeof(float));
   a.out = out; a.lse = lse;

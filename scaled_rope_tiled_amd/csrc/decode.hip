@@ -80,22 +80,41 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
   const uint4* qg = reinterpret_cast<const uint4*>(a.q);
 #pragma unroll
   for (int j = 0; j < G; ++j) {
+    const uint4 w0 = qg[((long long)b * a.Hq + h0 + j) * (kD / 8) + sub];
+    const uint4 w1 = qg[((long long)b * a.Hq + h0 + j) * (kD / 8) + sub + 8];
+    const uint32_t ww[2][4] = {{w0.x, w0.y, w0.z, w0.w}, {w1.x, w1.y, w1.z, w1.w}};
+    float x[2][8];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int chunk = sub + 8 * c;                     // 16-byte chunk index within the row
-      const uint4 w = qg[((long long)b * a.Hq + h0 + j) * (kD / 8) + chunk];
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        float x0 = lo_f(ww[p]), x1 = hi_f(ww[p]);
-        if (a.table) {
-          const float2 cs = reinterpret_cast<const float2*>(a.table)[qpos * (kD / 2) + chunk * 4 + p];
-          const float t0 = x0 * cs.x - x1 * cs.y, t1 = x0 * cs.y + x1 * cs.x;
-          x0 = t0; x1 = t1;
+      for (int p = 0; p < 4; ++p) { x[c][2 * p] = lo_f(ww[c][p]); x[c][2 * p + 1] = hi_f(ww[c][p]); }
+    if (a.table) {
+      const float2* tab = reinterpret_cast<const float2*>(a.table) + qpos * (kD / 2);
+      if (a.half_pairs) {
+        // pair 8*sub + e is (element e of chunk sub, element e of chunk sub + 8)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float2 cs = tab[8 * sub + e];
+          const float t0 = x[0][e] * cs.x - x[1][e] * cs.y, t1 = x[0][e] * cs.y + x[1][e] * cs.x;
+          x[0][e] = t0; x[1][e] = t1;
         }
-        qp[j][c * 4 + p] = pack2(x0 * qs, x1 * qs);
+      } else {
+        // pair (chunk * 4 + p) is elements 2p, 2p+1 of one chunk
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const float2 cs = tab[(sub + 8 * c) * 4 + p];
+            const float x0 = x[c][2 * p], x1 = x[c][2 * p + 1];
+            x[c][2 * p] = x0 * cs.x - x1 * cs.y;
+            x[c][2 * p + 1] = x0 * cs.y + x1 * cs.x;
+          }
       }
     }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) qp[j][c * 4 + p] = pack2(x[c][2 * p] * qs, x[c][2 * p + 1] * qs);
   }
 
   float m[G], l[G], acc[G][16];

@@ -99,6 +99,23 @@ __device__ inline uint4 rotate_chunk(uint4 w, float4 t0, float4 t1) {
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+// Half-split pairs: chunk w1 holds dims i..i+7 of the first half, w2 the same
+// dims of the second half; pair (w1[e], w2[e]) turns by table entry i + e.
+__device__ inline void rotate_chunk_pair(uint4& w1, uint4& w2, const float4 (&t)[4]) {
+  const uint32_t a[4] = {w1.x, w1.y, w1.z, w1.w};
+  const uint32_t b[4] = {w2.x, w2.y, w2.z, w2.w};
+  uint32_t o1[4], o2[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    // elements 2q, 2q+1 of each chunk: pairs i+2q (t[q].x, t[q].y) and i+2q+1 (t[q].z, t[q].w)
+    const float a0 = bf_lo(a[q]), a1 = bf_hi(a[q]), b0 = bf_lo(b[q]), b1 = bf_hi(b[q]);
+    o1[q] = pack2(a0 * t[q].x - b0 * t[q].y, a1 * t[q].z - b1 * t[q].w);
+    o2[q] = pack2(a0 * t[q].y + b0 * t[q].x, a1 * t[q].w + b1 * t[q].z);
+  }
+  w1 = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+  w2 = make_uint4(o2[0], o2[1], o2[2], o2[3]);
+}
+
 __device__ inline bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(bf16x8, w); }
 
 // LDS operands are addressed with 32-bit LDS byte addresses.  `opaque` hides a
@@ -134,7 +151,7 @@ __device__ inline float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <bool ROT_K>
+template <bool ROT_K, bool HALF>
 __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a) {
   __shared__ Smem sm;
 
@@ -163,23 +180,44 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   const int hl = lane >> 5;                      // lane half: 0 or 1
 
   // ---- Q^T operand: query wrow0 + l32, d = ks*16 + hl*8 + 0..7, rotated on load
+  // With half-split pairs, dims d and d + 64 pair up; chunks ks and ks + 4
+  // of the same lane hold exactly those, so the rotation stays in-lane.
   bf16x8 qreg[8];
   {
     const int row = wrow0 + l32;
     const bool ok = row < a.Nq;
     const long long qpos = a.q_pos0 + row;
+    if constexpr (HALF) {
+      uint4 w[8];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const int d0 = ks * 16 + hl * 8;
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (ok) {
-        w = *reinterpret_cast<const uint4*>(qg + (long long)row * kD + d0);
-        if (a.rope_flags & 1) {
-          const float4* t = tab4 + (qpos * (kD / 2) + d0 / 2) / 2;
-          w = rotate_chunk(w, t[0], t[1]);
+      for (int ks = 0; ks < 8; ++ks)
+        w[ks] = ok ? *reinterpret_cast<const uint4*>(qg + (long long)row * kD + ks * 16 + hl * 8)
+                   : make_uint4(0, 0, 0, 0);
+      if (ok && (a.rope_flags & 1)) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int d0 = ks * 16 + hl * 8;                  // first-half dims d0..d0+7 = pairs d0..d0+7
+          const float4* t = tab4 + (qpos * (kD / 2) + d0) / 2;
+          const float4 tt[4] = {t[0], t[1], t[2], t[3]};
+          rotate_chunk_pair(w[ks], w[ks + 4], tt);
         }
       }
-      qreg[ks] = as_bf16x8(w);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) qreg[ks] = as_bf16x8(w[ks]);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int d0 = ks * 16 + hl * 8;
+        uint4 w = make_uint4(0, 0, 0, 0);
+        if (ok) {
+          w = *reinterpret_cast<const uint4*>(qg + (long long)row * kD + d0);
+          if (a.rope_flags & 1) {
+            const float4* t = tab4 + (qpos * (kD / 2) + d0 / 2) / 2;
+            w = rotate_chunk(w, t[0], t[1]);
+          }
+        }
+        qreg[ks] = as_bf16x8(w);
+      }
     }
   }
 
@@ -201,31 +239,60 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   float4 tbuf[kStageRows][2];
 
   // Branch-free: rows past Nk read row Nk-1 (always valid when a tile exists) and are zeroed.
+  // K rotated on load with half-split pairs needs chunks c and c + 8 of one
+  // row in one thread: then thread t takes chunks (t & 7) and (t & 7) + 8 of
+  // row t >> 3 (8 threads per 256-byte row, still coalesced).
+  static_assert(kStageRows == 2 && kThreads / 8 == kBN, "half-split K staging covers one row per thread");
+  const int hr = tid >> 3, hc = tid & 7;
   auto issue_loads = [&](int key0) {
 #pragma unroll
     for (int i = 0; i < kStageRows; ++i) {
       const int key = key0 + sr + (kThreads / 16) * i;
       const bool in = key < a.Nk;
       const int kc = in ? key : a.Nk - 1;
-      const uint4 kw = *reinterpret_cast<const uint4*>(kg + (long long)kc * kD + sc * 8);
       const uint4 vw = *reinterpret_cast<const uint4*>(vg + (long long)kc * kD + sc * 8);
-      kbuf[i] = in ? kw : make_uint4(0, 0, 0, 0);
       vbuf[i] = in ? vw : make_uint4(0, 0, 0, 0);
-      if (ROT_K) {
-        const float4* t = tab4 + ((a.k_pos0 + kc) * (kD / 2) + sc * 4) / 2;
-        tbuf[i][0] = t[0];
-        tbuf[i][1] = t[1];
+      if (!(ROT_K && HALF)) {
+        const uint4 kw = *reinterpret_cast<const uint4*>(kg + (long long)kc * kD + sc * 8);
+        kbuf[i] = in ? kw : make_uint4(0, 0, 0, 0);
+        if (ROT_K) {
+          const float4* t = tab4 + ((a.k_pos0 + kc) * (kD / 2) + sc * 4) / 2;
+          tbuf[i][0] = t[0];
+          tbuf[i][1] = t[1];
+        }
       }
+    }
+    if (ROT_K && HALF) {
+      const int key = key0 + hr;
+      const bool in = key < a.Nk;
+      const int kc = in ? key : a.Nk - 1;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint4 kw = *reinterpret_cast<const uint4*>(kg + (long long)kc * kD + (hc + 8 * i) * 8);
+        kbuf[i] = in ? kw : make_uint4(0, 0, 0, 0);
+      }
+      const float4* t = tab4 + ((a.k_pos0 + kc) * (kD / 2) + hc * 8) / 2;   // pairs 8hc .. 8hc+7
+#pragma unroll
+      for (int q = 0; q < 4; ++q) tbuf[q >> 1][q & 1] = t[q];
     }
   };
   auto store_lds = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < kStageRows; ++i) {
       const int r = sr + (kThreads / 16) * i;
-      uint4 kw = kbuf[i];
-      if (ROT_K) kw = rotate_chunk(kw, tbuf[i][0], tbuf[i][1]);
-      *reinterpret_cast<uint4*>(&sm.k[buf][r * kKStr + sc * 8]) = kw;
+      if (!(ROT_K && HALF)) {
+        uint4 kw = kbuf[i];
+        if (ROT_K) kw = rotate_chunk(kw, tbuf[i][0], tbuf[i][1]);
+        *reinterpret_cast<uint4*>(&sm.k[buf][r * kKStr + sc * 8]) = kw;
+      }
       *reinterpret_cast<uint4*>(&sm.v[buf][r * kVStr + sc * 8]) = vbuf[i];
+    }
+    if (ROT_K && HALF) {
+      uint4 w1 = kbuf[0], w2 = kbuf[1];
+      const float4 tt[4] = {tbuf[0][0], tbuf[0][1], tbuf[1][0], tbuf[1][1]};
+      rotate_chunk_pair(w1, w2, tt);
+      *reinterpret_cast<uint4*>(&sm.k[buf][hr * kKStr + hc * 8]) = w1;
+      *reinterpret_cast<uint4*>(&sm.k[buf][hr * kKStr + (hc + 8) * 8]) = w2;
     }
   };
 
@@ -418,10 +485,15 @@ hipError_t launch_prefill_bf16_d128(const PrefillArgs& a, hipStream_t stream) {
   const int rows_per_wg = kBM * (kWaves / HPW);
   const int quads = G > 4 ? G / 4 : 1;
   const dim3 grid(a.Hkv * quads, (a.Nq + rows_per_wg - 1) / rows_per_wg, a.B), block(kThreads);
-  if (a.rope_flags & 2)
-    hipLaunchKernelGGL(prefill_bf16_kernel<true>, grid, block, 0, stream, a);
+  const bool rot_k = (a.rope_flags & 2) != 0, half = (a.rope_flags & 4) != 0;
+  if (rot_k && half)
+    hipLaunchKernelGGL((prefill_bf16_kernel<true, true>), grid, block, 0, stream, a);
+  else if (rot_k)
+    hipLaunchKernelGGL((prefill_bf16_kernel<true, false>), grid, block, 0, stream, a);
+  else if (half)
+    hipLaunchKernelGGL((prefill_bf16_kernel<false, true>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL(prefill_bf16_kernel<false>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_bf16_kernel<false, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

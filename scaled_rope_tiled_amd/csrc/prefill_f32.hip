@@ -46,13 +46,26 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillArgs a) {
   float o[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) { q[d] = row_ok ? qg[(long long)r * D + d] : 0.f; o[d] = 0.f; }
+  // pair i is (2i, 2i+1) (interleaved) or (i, i + D/2) (half-split)
+  const bool half_pairs = (a.rope_flags & 4) != 0;
+  // (two loops with compile-time indices keep q in registers)
   if ((a.rope_flags & 1) && row_ok) {
+    if (half_pairs) {
 #pragma unroll
-    for (int i = 0; i < D / 2; ++i) {
-      const float2 cs = tab[qpos * (D / 2) + i];
-      const float x0 = q[2 * i], x1 = q[2 * i + 1];
-      q[2 * i] = x0 * cs.x - x1 * cs.y;
-      q[2 * i + 1] = x0 * cs.y + x1 * cs.x;
+      for (int i = 0; i < D / 2; ++i) {
+        const float2 cs = tab[qpos * (D / 2) + i];
+        const float x0 = q[i], x1 = q[i + D / 2];
+        q[i] = x0 * cs.x - x1 * cs.y;
+        q[i + D / 2] = x0 * cs.y + x1 * cs.x;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < D / 2; ++i) {
+        const float2 cs = tab[qpos * (D / 2) + i];
+        const float x0 = q[2 * i], x1 = q[2 * i + 1];
+        q[2 * i] = x0 * cs.x - x1 * cs.y;
+        q[2 * i + 1] = x0 * cs.y + x1 * cs.x;
+      }
     }
   }
 #pragma unroll
@@ -72,18 +85,19 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillArgs a) {
     // stage 32 key rows (rotated) and value rows; lane handles pair columns
     for (int e = lane; e < kKeys * (D / 2); e += 64) {
       const int c = e / (D / 2), i = e % (D / 2);
+      const int i0 = half_pairs ? i : 2 * i, i1 = half_pairs ? i + D / 2 : 2 * i + 1;
       float k0 = 0.f, k1 = 0.f, v0 = 0.f, v1 = 0.f;
       if (c0 + c < a.Nk) {
-        const long long off = (long long)(c0 + c) * D + 2 * i;
-        k0 = kg[off]; k1 = kg[off + 1]; v0 = vg[off]; v1 = vg[off + 1];
+        const long long off = (long long)(c0 + c) * D;
+        k0 = kg[off + i0]; k1 = kg[off + i1]; v0 = vg[off + i0]; v1 = vg[off + i1];
         if (a.rope_flags & 2) {
           const float2 cs = tab[(a.k_pos0 + c0 + c) * (D / 2) + i];
           const float t0 = k0 * cs.x - k1 * cs.y, t1 = k0 * cs.y + k1 * cs.x;
           k0 = t0; k1 = t1;
         }
       }
-      ks[c][2 * i] = k0; ks[c][2 * i + 1] = k1;
-      vs[c][2 * i] = v0; vs[c][2 * i + 1] = v1;
+      ks[c][i0] = k0; ks[c][i1] = k1;
+      vs[c][i0] = v0; vs[c][i1] = v1;
     }
     __syncthreads();
     float s[kKeys];

@@ -7,7 +7,8 @@
 // §6.4 folds the YaRN temperature into the cached cos/sin).
 //
 // Rotation: interleaved pairs (x_{2i}, x_{2i+1}) turned counter-clockwise by
-// the table angle ("Long Context..." §2.2; "长上下文外推" §4.2).  HBM-bound:
+// the table angle ("Long Context..." §2.2; "长上下文外推" §4.2), or half-split
+// pairs (x_i, x_{i+D/2}) ("Long Context..." §2.4 code).  HBM-bound:
 // each thread moves 8 elements (one 16-byte bf16 vector or two fp32 vectors)
 // and reads the matching 4 table entries (32 bytes, L2-resident across heads).
 #include "srt_internal.h"
@@ -86,6 +87,64 @@ __global__ void __launch_bounds__(256) rope_apply_kernel(const void* __restrict_
   }
 }
 
+__device__ inline void load8(const void* base, long long idx8, bool bf16, float v[8]) {
+  if (bf16) {
+    const uint4 w = reinterpret_cast<const uint4*>(base)[idx8];
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[2 * i] = bf16_lo(ww[i]); v[2 * i + 1] = bf16_hi(ww[i]); }
+  } else {
+    const float4 a = reinterpret_cast<const float4*>(base)[2 * idx8];
+    const float4 b = reinterpret_cast<const float4*>(base)[2 * idx8 + 1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+__device__ inline void store8(void* base, long long idx8, bool bf16, const float o[8]) {
+  if (bf16) {
+    uint4 w;
+    w.x = pack_bf16x2(o[0], o[1]); w.y = pack_bf16x2(o[2], o[3]);
+    w.z = pack_bf16x2(o[4], o[5]); w.w = pack_bf16x2(o[6], o[7]);
+    reinterpret_cast<uint4*>(base)[idx8] = w;
+  } else {
+    reinterpret_cast<float4*>(base)[2 * idx8] = make_float4(o[0], o[1], o[2], o[3]);
+    reinterpret_cast<float4*>(base)[2 * idx8 + 1] = make_float4(o[4], o[5], o[6], o[7]);
+  }
+}
+
+// Half-split pairs ("Long Context..." §2.4 apply_rope): pair i is
+// (x_i, x_{i+D/2}).  One thread = 8 pairs = elements [8j, 8j+8) of the first
+// half and the same 8 of the second half.
+template <bool BF16>
+__global__ void __launch_bounds__(256) rope_apply_half_kernel(const void* __restrict__ x, void* y, long long groups,
+                                                              int N, int D, long long pos0,
+                                                              const float4* __restrict__ table) {
+  const int per_row = D / 16;
+  const long long total = groups * (long long)N * per_row;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (long long)gridDim.x * blockDim.x) {
+    const long long row = e / per_row;
+    const int j = (int)(e - row * per_row);
+    const long long p = pos0 + row % N;
+    const float4* trow = table + (p * (D / 2) + 8 * j) / 2;      // pairs 8j .. 8j+7
+    const long long i1 = row * (D / 8) + j, i2 = i1 + D / 16;     // 8-element chunks of the two halves
+    float a[8], b[8], o1[8], o2[8];
+    load8(x, i1, BF16, a);
+    load8(x, i2, BF16, b);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 t = trow[q];
+      // pairs 2q and 2q+1 of this thread: (cos, sin) = (t.x, t.y), (t.z, t.w)
+      o1[2 * q] = a[2 * q] * t.x - b[2 * q] * t.y;
+      o2[2 * q] = a[2 * q] * t.y + b[2 * q] * t.x;
+      o1[2 * q + 1] = a[2 * q + 1] * t.z - b[2 * q + 1] * t.w;
+      o2[2 * q + 1] = a[2 * q + 1] * t.w + b[2 * q + 1] * t.z;
+    }
+    store8(y, i1, BF16, o1);
+    store8(y, i2, BF16, o2);
+  }
+}
+
 inline unsigned grid_for(long long work, int block) {
   long long g = (work + block - 1) / block;
   const long long cap = 256LL * 64;   // enough waves in flight on 256 CUs; the loops stride beyond
@@ -102,10 +161,20 @@ hipError_t launch_rope_table(const Theta& th, int half, double mscale, long long
   return hipGetLastError();
 }
 
-hipError_t launch_rope_apply(const void* x, void* y, bool bf16, long long groups, int N, int D, long long pos0,
-                             const float* table, hipStream_t stream) {
-  const long long work = groups * (long long)N * (D / 8);
+hipError_t launch_rope_apply(const void* x, void* y, bool bf16, bool half_pairs, long long groups, int N, int D,
+                             long long pos0, const float* table, hipStream_t stream) {
   const float4* t = reinterpret_cast<const float4*>(table);
+  if (half_pairs) {
+    const long long work = groups * (long long)N * (D / 16);
+    if (bf16)
+      hipLaunchKernelGGL(rope_apply_half_kernel<true>, dim3(grid_for(work, 256)), dim3(256), 0, stream, x, y, groups,
+                         N, D, pos0, t);
+    else
+      hipLaunchKernelGGL(rope_apply_half_kernel<false>, dim3(grid_for(work, 256)), dim3(256), 0, stream, x, y,
+                         groups, N, D, pos0, t);
+    return hipGetLastError();
+  }
+  const long long work = groups * (long long)N * (D / 8);
   if (bf16)
     hipLaunchKernelGGL(rope_apply_kernel<true>, dim3(grid_for(work, 256)), dim3(256), 0, stream, x, y, groups, N,
                        D, pos0, t);

@@ -20,7 +20,7 @@ hipError_t launch_rope_table(const Theta& th, int half, double mscale, long long
                              hipStream_t stream);
 
 // rows = B*H rows-groups of N rows each; row r of a group sits at position pos0 + r.
-hipError_t launch_rope_apply(const void* x, void* y, bool bf16, long long groups, int N, int D,
+hipError_t launch_rope_apply(const void* x, void* y, bool bf16, bool half_pairs, long long groups, int N, int D,
                              long long pos0, const float* table, hipStream_t stream);
 
 // ---------------------------------------------------------------- prefill
@@ -35,7 +35,7 @@ struct PrefillArgs {
   long long q_pos0, k_pos0;
   int B, Hq, Hkv, Nq, Nk, D;
   int causal;
-  int rope_flags;       // bit0: rotate q, bit1: rotate k
+  int rope_flags;       // bit0: rotate q, bit1: rotate k, bit2: half-split pairs
   int out_bf16;         // 1: out is bf16, 0: fp32
   float sm_scale;
 };
@@ -70,6 +70,7 @@ struct DecodeArgs {
   void* out;              // [B][Hq][D] bf16
   float* lse;             // [B][Hq] or nullptr
   int B, Hq, Hkv, Nk, D, splits, split_len;
+  int half_pairs;         // q rotated with pairs (x_i, x_{i+D/2})
   float sm_scale;
 };
 

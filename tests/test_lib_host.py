@@ -15,10 +15,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 @pytest.fixture(scope="module")
 def srt():
-    from scaled_rope_tiled_amd import _lib
-    if not os.path.exists(_lib.LIB_PATH):
-        from scaled_rope_tiled_amd.build import build
-        build()
+    if not os.path.exists(os.environ.get("SRT_LIB", os.path.join(ROOT, "scaled_rope_tiled_amd", "libsrt.so"))):
+        import __graft_entry__
+        __graft_entry__.build()
     import scaled_rope_tiled_amd as m
     return m
 
@@ -110,20 +109,24 @@ def test_abi_rejects_before_launch(srt):
     st = lib.srt_attn_prefill(fake, fake, fake, 1, 1, 4, 2, 8, 8, 128, 1024, 1024, 0, 0, 1, 0.1,
                               fake, 4, 3, fake, 1, 1024, None, 0, None)
     assert st == 1 and b"outside table" in lib.srt_last_error()
-    st = lib.srt_rope_apply(fake, fake, 1, 1, 1, 8, 128, 5, fake, 10, None)
+    st = lib.srt_rope_apply(fake, fake, 1, 1, 1, 8, 128, 5, fake, 10, 0, None)
     assert st == 1 and b"outside table" in lib.srt_last_error()
-    st = lib.srt_rope_apply(fake, fake, 7, 1, 1, 8, 128, 0, fake, 10, None)
+    st = lib.srt_rope_apply(fake, fake, 7, 1, 1, 8, 128, 0, fake, 10, 0, None)
     assert st == 1
+    st = lib.srt_rope_apply(fake, fake, 1, 1, 1, 8, 128, 0, fake, 10, 2, None)
+    assert st == 1 and b"pairing" in lib.srt_last_error()
+    st = lib.srt_rope_apply(fake, fake, 1, 1, 1, 8, 40, 0, fake, 10, 1, None)
+    assert st in (1, 2)
     n = C.c_size_t()
     assert lib.srt_attn_decode_workspace_size(16, 32, 128, 64, C.byref(n)) == 0
     assert n.value == 16 * 32 * 64 * 129 * 4
-    st = lib.srt_attn_decode_splitk(fake, fake, fake, 1, 16, 32, 8, 1024, 128, None, 64, 0.1, None, 0,
+    st = lib.srt_attn_decode_splitk(fake, fake, fake, 1, 16, 32, 8, 1024, 128, None, 64, 0.1, None, 0, 0,
                                     fake, n.value - 1, fake, None, None)
     assert st == 4
-    st = lib.srt_attn_decode_splitk(fake, fake, fake, 1, 16, 24, 8, 1024, 128, None, 64, 0.1, None, 0,
+    st = lib.srt_attn_decode_splitk(fake, fake, fake, 1, 16, 24, 8, 1024, 128, None, 64, 0.1, None, 0, 0,
                                     fake, n.value, fake, None, None)
     assert st == 2
-    st = lib.srt_attn_decode_splitk(fake, fake, fake, 1, 16, 32, 8, 1024, 128, None, 0, 0.1, None, 0,
+    st = lib.srt_attn_decode_splitk(fake, fake, fake, 1, 16, 32, 8, 1024, 128, None, 0, 0.1, None, 0, 0,
                                     fake, n.value, fake, None, None)
     assert st == 1
     st = lib.srt_attn_merge_states(fake, fake, fake, fake, 0, 64, fake, 1, 128, None, 0, 1, 1, 1, 128, None)
@@ -133,3 +136,29 @@ def test_abi_rejects_before_launch(srt):
     th = (C.c_double * 4)(1.0, 0.1, 0.01, float("inf"))
     st = lib.srt_rope_cos_sin(th, 8, 1.0, 16, fake, None)
     assert st == 1 and b"finite" in lib.srt_last_error()
+
+
+@pytest.mark.parametrize("base,seq_len,L,D", [
+    (10000.0, 1000, 2048.0, 128),      # shorter than L: original frequencies
+    (10000.0, 2048, 2048.0, 128),      # exactly L
+    (10000.0, 32768, 2048.0, 128),     # s = 16
+    (500000.0, 12345, 4096.0, 64),     # non-integer s
+])
+def test_dynamic_ntk_matches_oracle(srt, base, seq_len, L, D):
+    th, s = srt.rope_inv_freq_dynamic_ntk(base, seq_len, L, D)
+    assert s == pytest.approx(orope.dynamic_ntk_scale(seq_len, L), rel=1e-15)
+    np.testing.assert_allclose(th, orope.inv_freq_dynamic_ntk(base, seq_len, L, D), rtol=1e-15, atol=0)
+
+
+def test_factors_match_oracle(srt):
+    lam = 1.0 + np.random.default_rng(3).random(64) * 15.0
+    np.testing.assert_allclose(srt.rope_inv_freq_factors(1e4, lam, 128), orope.inv_freq_factors(1e4, lam, 128),
+                               rtol=1e-15, atol=0)
+    from scaled_rope_tiled_amd._lib import SrtError
+    bad = lam.copy()
+    bad[5] = 0.0
+    with pytest.raises(SrtError):
+        srt.rope_inv_freq_factors(1e4, bad, 128)
+    bad[5] = float("nan")
+    with pytest.raises(SrtError):
+        srt.rope_inv_freq_factors(1e4, bad, 128)

@@ -192,3 +192,23 @@ def test_row_subset_matches_full():
     o2, l2 = A.attention(q, k, v, sm_scale=0.3, theta=th, rows=rows)
     np.testing.assert_allclose(o2, o[:, :, rows], atol=1e-14)
     np.testing.assert_allclose(l2, l[:, :, rows], atol=1e-14)
+
+
+def test_half_split_attention_is_interleaved_on_permuted_dims():
+    """"Long Context..." §2.4: the half-split rule is the interleaved one on permuted
+    dimensions, and q.k is invariant under one permutation of both q and k."""
+    B, Hq, Hkv, N, D = 1, 4, 2, 30, 16
+    q, k, v = _qkv(B, Hq, Hkv, N, N, D)
+    th, msc, _ = rope.inv_freq(rope.YARN, 1e4, 8.0, 64.0, 1.0, 32.0, D)
+    perm = np.empty(D, dtype=int)
+    perm[0::2] = np.arange(D // 2)
+    perm[1::2] = np.arange(D // 2) + D // 2
+    o1, l1 = A.attention(q, k, v, sm_scale=0.25, theta=th, mscale=msc, pairing="half")
+    o2, l2 = A.attention(q[..., perm], k[..., perm], v, sm_scale=0.25, theta=th, mscale=msc)
+    np.testing.assert_allclose(o1, o2, atol=1e-12)
+    np.testing.assert_allclose(l1, l2, atol=1e-12)
+    o3, _ = A.attention(q, k, v, sm_scale=0.25, theta=th, mscale=msc)
+    assert np.abs(o1 - o3).max() > 1e-3
+    kc = np.stack([rope.rotate_half(k[0], np.arange(N), th, msc)])
+    od, ld = A.decode(q[:, :, -1], kc, v, sm_scale=0.25, theta=th, mscale=msc, pairing="half")
+    np.testing.assert_allclose(od, o1[:, :, -1], atol=1e-12)

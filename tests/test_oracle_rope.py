@@ -284,3 +284,48 @@ def test_homework_angle():
     th = rope.base_inv_freq(4, 10000.0)
     assert 100 * th[0] == 100.0
     assert 0 * th[0] == 0.0
+
+
+# --------------------------------------------------------------------------- frequency-step variants
+
+def test_rotate_half_matches_complex_form_and_permutation():
+    """"Long Context..." §2.4: half-split pairs (x_i, x_{i+D/2}) are the interleaved rule on permuted dims."""
+    D = 16
+    th = rope.base_inv_freq(D, 10000.0)
+    x = RNG.standard_normal((9, D))
+    pos = np.array([0, 1, 2, 7, 100, 4095, 8191, 65536, 131071])
+    y = rope.rotate_half(x, pos, th, 1.3)
+    z = (x[:, :D // 2] + 1j * x[:, D // 2:]) * np.exp(1j * pos[:, None] * th[None, :]) * 1.3
+    np.testing.assert_allclose(y[:, :D // 2], z.real, atol=1e-12)
+    np.testing.assert_allclose(y[:, D // 2:], z.imag, atol=1e-12)
+    perm = np.empty(D, dtype=int)             # interleaved slot 2i <- half slot i, 2i+1 <- i + D/2
+    perm[0::2] = np.arange(D // 2)
+    perm[1::2] = np.arange(D // 2) + D // 2
+    np.testing.assert_allclose(rope.rotate(x[:, perm], pos, th, 1.3), y[:, perm], atol=1e-12)
+    # on random data the two pairings give different vectors: the table must match the pairing
+    assert np.abs(rope.rotate(x, pos, th) - rope.rotate_half(x, pos, th)).max() > 0.1
+
+
+def test_dynamic_ntk_follows_length():
+    """Short sequences keep the original base; at N = s L it is the NTK-aware base for s."""
+    D, b, L = 128, 10000.0, 8192.0
+    np.testing.assert_array_equal(rope.inv_freq_dynamic_ntk(b, 100, L, D), rope.base_inv_freq(D, b))
+    np.testing.assert_array_equal(rope.inv_freq_dynamic_ntk(b, L, L, D), rope.base_inv_freq(D, b))
+    th16, _, _ = rope.inv_freq(rope.NTK, b, 16.0, D=D)
+    np.testing.assert_allclose(rope.inv_freq_dynamic_ntk(b, 16 * L, L, D), th16, rtol=1e-14)
+    # the printed example of the NTK base for 8K -> 128K holds for the dynamic rule at N = 128K
+    b_eff = rope.inv_freq_dynamic_ntk(b, 131072, L, D)[1] ** (-D / 2)
+    assert 1.6e5 < b_eff < 1.8e5
+
+
+def test_factor_table_reduces_to_pi_ntk_none():
+    """theta / lambda: lambda = s gives PI, lambda_i = s^(2i/(D-2)) gives NTK-aware, lambda = 1 gives RoPE."""
+    D, b, s = 64, 10000.0, 8.0
+    d = np.arange(D // 2)
+    th_pi, _, _ = rope.inv_freq(rope.PI, b, s, D=D)
+    th_ntk, _, _ = rope.inv_freq(rope.NTK, b, s, D=D)
+    np.testing.assert_allclose(rope.inv_freq_factors(b, np.full(D // 2, s), D), th_pi, rtol=1e-15)
+    np.testing.assert_allclose(rope.inv_freq_factors(b, s ** (2.0 * d / (D - 2)), D), th_ntk, rtol=1e-13)
+    np.testing.assert_array_equal(rope.inv_freq_factors(b, np.ones(D // 2), D), rope.base_inv_freq(D, b))
+    with pytest.raises(ValueError):
+        rope.inv_freq_factors(b, np.zeros(D // 2), D)
