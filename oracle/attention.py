@@ -14,6 +14,10 @@ Conventions (readings of the pages where they are silent):
   * GQA: query head h reads kv head h // (Hq / Hkv);
   * causal mask on absolute positions: key at k_pos0 + c is visible to the
     query at q_pos0 + r iff k_pos0 + c <= q_pos0 + r;
+  * sliding window W (> 0) and S sink tokens on top of the causal mask
+    ("Long Context..." §10.1 sliding_window_mask: key j visible to query i iff
+    i - W < j <= i; §10.2 StreamingLLM: the first S tokens always stay), see
+    ``visible``; W = 0 means no window (full causal attention);
   * lse = M + ln(sum exp(s - M)) of the scaled scores (natural log); a row
     with no visible key has O = 0 and lse = -inf;
   * the temperature factor mscale multiplies both rotated q and rotated k
@@ -43,14 +47,52 @@ def _rotator(pairing: str):
     raise ValueError(f"unknown pairing {pairing}")
 
 
+def visible(qpos, kpos, *, causal: bool = True, window: int = 0, sink: int = 0) -> np.ndarray:
+    """Boolean mask [len(qpos), len(kpos)] on absolute positions.
+
+    Causal: kpos <= qpos.  Window W > 0 additionally keeps only kpos > qpos - W
+    (W keys including the query's own position, "Long Context..." §10.1),
+    except that positions kpos < S (the attention sinks of §10.2) stay visible.
+    A window needs the causal mask (the pages define it only there).
+    """
+    qpos = np.asarray(qpos, dtype=np.int64)[:, None]
+    kpos = np.asarray(kpos, dtype=np.int64)[None, :]
+    if window and not causal:
+        raise ValueError("a sliding window is defined on top of the causal mask")
+    m = np.ones((qpos.shape[0], kpos.shape[1]), dtype=bool)
+    if causal:
+        m &= kpos <= qpos
+    if window > 0:
+        m &= (kpos > qpos - window) | (kpos < sink)
+    return m
+
+
+def visible_pairs(N: int, window: int = 0, sink: int = 0) -> int:
+    """Number of visible (query, key) pairs of a causal N x N problem, one row at a time.
+
+    Row i sees min(i + 1, W) window keys plus the sinks that fell out of the
+    window, min(S, max(0, i - W + 1)); without a window, i + 1 keys.  This is
+    the work count behind "O(W N) instead of O(N^2)" ("Long Context..." §10.1).
+    """
+    total = 0
+    for i in range(N):
+        if window > 0:
+            total += min(i + 1, window) + min(sink, max(0, i - window + 1))
+        else:
+            total += i + 1
+    return total
+
+
 def attention(q, k, v, *, sm_scale: float, causal: bool = True, q_pos0: int = 0, k_pos0: int = 0,
-              theta=None, mscale: float = 1.0, rows=None, block: int = 256, pairing: str = "interleaved"):
+              theta=None, mscale: float = 1.0, rows=None, block: int = 256, pairing: str = "interleaved",
+              window: int = 0, sink: int = 0):
     """Softmax attention with RoPE applied to q and k.
 
     q: [B, Hq, Nq, D]; k, v: [B, Hkv, Nk, D].  theta=None means q and k are
     used as given (already rotated).  ``rows`` (optional int array) restricts
     the computation to those query rows.  ``pairing`` picks interleaved pairs
-    (default) or half-split pairs.  Returns (O [B, Hq, R, D], lse [B, Hq, R]).
+    (default) or half-split pairs.  ``window`` / ``sink``: see ``visible``.
+    Returns (O [B, Hq, R, D], lse [B, Hq, R]).
     """
     rot = _rotator(pairing)
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -74,8 +116,7 @@ def attention(q, k, v, *, sm_scale: float, causal: bool = True, q_pos0: int = 0,
                     qpos = q_pos0 + rr
                     qt = q[b, h, rr] if theta is None else rot(q[b, h, rr], qpos, theta, mscale)
                     s = sm_scale * (qt @ kt.T)                              # [r, Nk]
-                    if causal:
-                        s = np.where(kpos[None, :] <= qpos[:, None], s, -np.inf)
+                    s = np.where(visible(qpos, kpos, causal=causal, window=window, sink=sink), s, -np.inf)
                     M = s.max(axis=1)
                     ok = np.isfinite(M)
                     Ms = np.where(ok, M, 0.0)
@@ -89,7 +130,7 @@ def attention(q, k, v, *, sm_scale: float, causal: bool = True, q_pos0: int = 0,
 
 
 def brute_force(q, k, v, *, sm_scale: float, causal: bool = True, q_pos0: int = 0, k_pos0: int = 0,
-                theta=None, mscale: float = 1.0):
+                theta=None, mscale: float = 1.0, window: int = 0, sink: int = 0):
     """Tiny-input check: explicit D x D rotation matrices and the full score matrix.
 
     Rotates with ``rope.rotation_matrix`` (blkdiag form, "Long Context..."
@@ -103,10 +144,13 @@ def brute_force(q, k, v, *, sm_scale: float, causal: bool = True, q_pos0: int = 
     out = np.zeros((B, Hq, Nq, D))
     lse = np.zeros((B, Hq, Nq))
     mask = np.ones((Nq, Nk), dtype=bool)
-    if causal:
-        for r in range(Nq):
-            for c in range(Nk):
-                mask[r, c] = (k_pos0 + c) <= (q_pos0 + r)
+    for r in range(Nq):
+        for c in range(Nk):
+            i, j = q_pos0 + r, k_pos0 + c
+            ok = (j <= i) if causal else True
+            if window > 0:
+                ok = ok and (i - j < window or j < sink)
+            mask[r, c] = ok
     for b in range(B):
         for h in range(Hq):
             hk = h // g
@@ -159,13 +203,15 @@ def merge(o_a, lse_a, o_b, lse_b):
 
 
 def decode(q, k_cache_rotated, v_cache, *, sm_scale: float, seq_lens=None, theta=None, mscale: float = 1.0,
-           pairing: str = "interleaved"):
+           pairing: str = "interleaved", window: int = 0, sink: int = 0):
     """One new query per sequence against its cache (already rotated keys).
 
     q: [B, Hq, D] raw, rotated at position seq_len - 1 (the new token's own
     K/V is the last cache row, so every cached key is visible).  The decode
     step reads the whole cache ("Long Context..." §12.3; "长上下文推理" on
-    KV-cache reads).  Returns (O [B, Hq, D], lse [B, Hq]).
+    KV-cache reads).  With a window only the last W cached keys and the first
+    S (sinks) are visible, the query being at position seq_len - 1.
+    Returns (O [B, Hq, D], lse [B, Hq]).
     """
     q, kc, vc = _f64(q), _f64(k_cache_rotated), _f64(v_cache)
     B, Hq, D = q.shape
@@ -181,7 +227,7 @@ def decode(q, k_cache_rotated, v_cache, *, sm_scale: float, seq_lens=None, theta
         if theta is not None:
             qb = _rotator(pairing)(qb, np.array([n - 1]), theta, mscale)
         o, l = attention(qb[None], kc[b:b + 1, :, :n], vc[b:b + 1, :, :n], sm_scale=sm_scale,
-                         causal=False, theta=None)
+                         causal=True, q_pos0=n - 1, theta=None, window=window, sink=sink)
         out[b] = o[0, :, 0]
         lse[b] = l[0, :, 0]
     return out, lse

@@ -212,3 +212,95 @@ def test_half_split_attention_is_interleaved_on_permuted_dims():
     kc = np.stack([rope.rotate_half(k[0], np.arange(N), th, msc)])
     od, ld = A.decode(q[:, :, -1], kc, v, sm_scale=0.25, theta=th, mscale=msc, pairing="half")
     np.testing.assert_allclose(od, o1[:, :, -1], atol=1e-12)
+
+
+# --------------------------------------------------------------------------- sliding window and sinks
+
+def test_sliding_window_mask_matches_printed(golden):
+    """"Long Context..." §10.1: the printed L = 8, W = 4 mask, row by row."""
+    want = np.array([[c == "T" for c in row[1:]] for row in golden("sliding_window_mask_L8_W4.txt")])
+    got = A.visible(np.arange(8), np.arange(8), window=4)
+    np.testing.assert_array_equal(got, want)
+    # no window: the plain causal mask; a window as long as the sequence changes nothing
+    np.testing.assert_array_equal(A.visible(np.arange(8), np.arange(8)), np.tri(8, dtype=bool))
+    np.testing.assert_array_equal(A.visible(np.arange(8), np.arange(8), window=8), np.tri(8, dtype=bool))
+    with pytest.raises(ValueError):
+        A.visible(np.arange(8), np.arange(8), causal=False, window=4)
+
+
+def test_streaming_sinks_keep_first_s_and_last_w(golden):
+    """"Long Context..." §10.2: the last query sees the first S tokens and the last W: S + W keys."""
+    (_, S, W, n_keys), = [r for r in golden("sliding_window_work.txt") if r[0] == "streaming_cache"]
+    S, W, n_keys = int(S), int(W), int(n_keys)
+    N = 10000
+    row = A.visible([N - 1], np.arange(N), window=W, sink=S)[0]
+    assert row.sum() == n_keys == S + W
+    assert row[:S].all() and row[N - W:].all() and not row[S:N - W].any()
+    # rows still inside the first S + W positions see every earlier key
+    early = A.visible(np.arange(S + W), np.arange(S + W), window=W, sink=S)
+    assert early.sum(axis=1).tolist() == [min(i + 1, W) + min(S, max(0, i - W + 1)) for i in range(S + W)]
+
+
+def test_visible_pair_counts(golden):
+    """O(N W) work: the row-by-row count equals the mask's count on small cases and
+    reproduces the printed 16B -> 524M (97 % fewer) at N = 128K, W = 4096."""
+    for N, W, S in [(1, 0, 0), (50, 0, 0), (50, 7, 0), (50, 7, 4), (50, 60, 4), (33, 1, 3)]:
+        m = A.visible(np.arange(N), np.arange(N), window=W, sink=S)
+        assert A.visible_pairs(N, W, S) == int(m.sum())
+    rows = {r[0]: r for r in golden("sliding_window_work.txt")}
+    N, W = int(rows["window_dots"][1]), int(rows["window_dots"][2])
+    full, win = A.visible_pairs(N), A.visible_pairs(N, W)
+    assert abs(N * N - float(rows["full_dots"][3])) <= float(rows["full_dots"][4]) * float(rows["full_dots"][3])
+    assert abs(win - float(rows["window_dots"][3])) <= float(rows["window_dots"][4]) * float(rows["window_dots"][3])
+    assert win == N * W - W * (W - 1) // 2              # closed form of the ramp
+    assert full == N * (N + 1) // 2
+    pct = 100.0 * (1.0 - (N * W) / (N * N))
+    assert abs(pct - float(rows["reduction_pct"][3])) <= float(rows["reduction_pct"][4])
+
+
+@pytest.mark.parametrize("W,S", [(1, 0), (5, 0), (5, 3), (16, 4), (40, 2)])
+def test_window_attention_equals_brute_force(W, S):
+    B, Hq, Hkv, N, D = 1, 4, 2, 37, 8
+    q, k, v = _qkv(B, Hq, Hkv, N, N, D)
+    th, msc, _ = rope.inv_freq(rope.YARN, 1e4, 16.0, 64.0, 1.0, 32.0, D)
+    kw = dict(sm_scale=1 / math.sqrt(D), theta=th, mscale=msc, window=W, sink=S)
+    o1, l1 = A.attention(q, k, v, block=6, **kw)
+    o2, l2 = A.brute_force(q, k, v, **kw)
+    np.testing.assert_allclose(o1, o2, atol=1e-12)
+    np.testing.assert_allclose(l1, l2, atol=1e-12)
+    # offsets (one ring chunk): sinks are absolute positions, so a chunk past them has none
+    kw2 = dict(kw, q_pos0=30, k_pos0=0)
+    o3, l3 = A.attention(q[:, :, :7], k, v, **kw2)
+    o4, l4 = A.brute_force(q[:, :, :7], k, v, **kw2)
+    np.testing.assert_allclose(o3, o4, atol=1e-12)
+
+
+def test_window_special_cases():
+    """W = 1, no sink: each query sees only itself (O = v_i, lse = its own score);
+    W >= N: plain causal attention; window attention == full attention over the kept keys."""
+    B, H, N, D = 1, 2, 20, 8
+    q, k, v = _qkv(B, H, H, N, N, D)
+    o, l = A.attention(q, k, v, sm_scale=0.5, window=1)
+    np.testing.assert_allclose(o, v, atol=1e-14)
+    np.testing.assert_allclose(l, 0.5 * np.einsum("bhnd,bhnd->bhn", q, k), atol=1e-12)
+    o1, l1 = A.attention(q, k, v, sm_scale=0.5, window=N, sink=3)
+    o2, l2 = A.attention(q, k, v, sm_scale=0.5)
+    np.testing.assert_allclose(o1, o2, atol=1e-14)
+    W, S, i = 6, 2, 15
+    keep = sorted(set(range(S)) | set(range(i - W + 1, i + 1)))
+    o3, l3 = A.attention(q[:, :, i:i + 1], k[:, :, keep], v[:, :, keep], sm_scale=0.5, causal=False)
+    o4, l4 = A.attention(q, k, v, sm_scale=0.5, window=W, sink=S, rows=[i])
+    np.testing.assert_allclose(o4, o3, atol=1e-13)
+    np.testing.assert_allclose(l4, l3, atol=1e-13)
+
+
+def test_decode_window_equals_last_row():
+    B, Hq, Hkv, N, D = 2, 4, 2, 40, 16
+    q, k, v = _qkv(B, Hq, Hkv, N, N, D)
+    th, msc, _ = rope.inv_freq(rope.PI, 1e4, 16.0, D=D)
+    kc = np.stack([rope.rotate(k[b], np.arange(N), th, msc) for b in range(B)])
+    for W, S in [(8, 0), (8, 4), (100, 4)]:
+        full_o, full_l = A.attention(q, k, v, sm_scale=0.25, theta=th, mscale=msc, window=W, sink=S)
+        o, l = A.decode(q[:, :, -1], kc, v, sm_scale=0.25, theta=th, mscale=msc, window=W, sink=S)
+        np.testing.assert_allclose(o, full_o[:, :, -1], atol=1e-12)
+        np.testing.assert_allclose(l, full_l[:, :, -1], atol=1e-12)
