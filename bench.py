@@ -20,6 +20,8 @@ same line carries:
     algorithmic bytes / time against the 8 TB/s HBM peak;
   * ``ring``: the 128K NTK prefill as 8 K/V chunks of 16384 merged by
     log-sum-exp (one device's ring step), TFLOP/s;
+  * ``window``: the same prefill with a 4096-key sliding window and 4 sink
+    tokens (flops of the kept pairs only), and its time against full causal;
   * ``cpu_baseline``: the fp64 oracle on the host cores, on a bounded sample.
 
 FLOPs count only (query, key) pairs the causal mask keeps, 4*D per pair per
@@ -64,6 +66,13 @@ def causal_pairs(Nq: int, Nk: int, q_pos0: int = 0, k_pos0: int = 0) -> int:
 def prefill_flops(B, Hq, Nq, Nk, D, q_pos0=0, k_pos0=0, causal=True) -> float:
     pairs = causal_pairs(Nq, Nk, q_pos0, k_pos0) if causal else Nq * Nk
     return 4.0 * D * B * Hq * pairs
+
+
+def window_pairs(N: int, window: int, sink: int) -> int:
+    """(query, key) pairs a causal sliding window of W keys plus S sinks keeps."""
+    import numpy as np
+    i = np.arange(N, dtype=np.int64)
+    return int(np.sum(np.minimum(i + 1, window) + np.minimum(sink, np.maximum(0, i - window + 1))))
 
 
 def _sha(path: str) -> str:
@@ -160,6 +169,41 @@ def traffic_from_counters(flops_unit_note=None):
     fetch = c["fetch_kib_per_dispatch"] * 1024.0 * c["fetch_scale"]
     write = c["write_kib_per_dispatch"] * 1024.0 * c["write_scale"]
     return fetch + write, "rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated"
+
+
+# ----------------------------------------------------------------------------- sliding window
+
+def bench_window(srt, torch, w, window, sink, steps, warmup, full_kernel_ms):
+    """The prefill workload with a sliding window and sinks: O(N W) work."""
+    import synth
+    D = w.D
+    q = synth.randn((w.B, w.Hq, w.N, D), torch.bfloat16, w.seed, synth.Q_ID, "cuda")
+    k = synth.randn((w.B, w.Hkv, w.N, D), torch.bfloat16, w.seed, synth.K_ID, "cuda")
+    v = synth.randn((w.B, w.Hkv, w.N, D), torch.bfloat16, w.seed, synth.V_ID, "cuda")
+    rp = w.rope
+    th, ms, _ = srt.rope_inv_freq(rp.method, rp.base, rp.s, rp.L, rp.alpha, rp.beta, D)
+    table = srt.rope_cos_sin(th, D, ms, w.N, "cuda")
+    krot = srt.rope_apply(k, table)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device="cuda")
+    kt = Timer(torch)
+    fn = lambda: srt.attn_prefill(q, krot, v, table=table, rope_flags=srt.ROTATE_Q, out=out, lse=lse,
+                                  window=window, sink=sink)
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        kt.run(fn)
+    torch.cuda.synchronize()
+    kernel_ms = kt.mean_ms()
+    pairs = window_pairs(w.N, window, sink)
+    flops = 4.0 * D * w.B * w.Hq * pairs
+    tf = flops / (kernel_ms * 1e-3) / 1e12
+    return {"workload": f"{w.name} with window {window}, {sink} sinks", "unit": "TFLOP/s", "value": round(tf, 2),
+            "kernel_ms": round(kernel_ms, 4), "alg_flops_per_launch": flops,
+            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "work_vs_full_causal": round(pairs / causal_pairs(w.N, w.N), 4),
+            "time_vs_full_causal": round(kernel_ms / full_kernel_ms, 4)}
 
 
 # ----------------------------------------------------------------------------- decode
@@ -375,6 +419,8 @@ def main():
         line["decode"] = bench_decode(srt, torch, synth.WORKLOADS["c5"], max(5, args.steps), args.warmup)
         torch.cuda.empty_cache()
         line["ring"] = bench_ring(srt, torch, synth.WORKLOADS["c4"], max(2, args.steps // 5), 1)
+        torch.cuda.empty_cache()
+        line["window"] = bench_window(srt, torch, w, 4096, 4, args.steps, args.warmup, p["kernel_ms"])
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

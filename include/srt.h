@@ -171,6 +171,13 @@ int srt_rope_apply(const void* x, void* y, int dtype, int B, int H, int N, int D
  * tile with the online softmax (running max and sum, rescaled accumulator:
  * [BK] §8.3.4 (1)-(2)); tiles wholly above the causal diagonal are skipped.
  *
+ * Sliding window and sinks ([LC] §10.1-10.2): with window > 0 (causal only)
+ * a key at absolute position j stays visible to the query at position i only
+ * if i - j < window (the window counts the query's own position) or j < sink
+ * (the first `sink` positions of the sequence are attention sinks).  Tiles
+ * outside both are skipped, so the work is O(Nq * (window + sink)).
+ * window = 0 means no window (sink is then irrelevant); both must be >= 0.
+ *
  * q: [B][Hq][Nq][D] with head stride q_hstride; k, v: [B][Hkv][Nk][D] with head
  * stride kv_hstride; dtype for q, k, v.  out: [B][Hq][Nq][D] in out_dtype with
  * head stride o_hstride (SRT_F32 keeps a partial state exact for merging).
@@ -181,7 +188,7 @@ int srt_rope_apply(const void* x, void* y, int dtype, int B, int H, int N, int D
 int srt_attn_prefill(const void* q, const void* k, const void* v, int dtype,
                      int B, int Hq, int Hkv, int Nq, int Nk, int D,
                      long long q_hstride, long long kv_hstride,
-                     long long q_pos0, long long k_pos0, int causal, float sm_scale,
+                     long long q_pos0, long long k_pos0, int causal, int window, int sink, float sm_scale,
                      const float* table_dev, long long table_npos, int rope_flags,
                      void* out, int out_dtype, long long o_hstride,
                      float* lse, long long lse_hstride, void* stream);
@@ -217,7 +224,12 @@ int srt_attn_decode_workspace_size(int B, int Hq, int D, int num_splits, size_t*
  * seq_len_b - 1 with the table (skipped if table_dev is NULL), pairs chosen by
  * `pairing` (SRT_PAIRING_INTERLEAVED or SRT_PAIRING_HALF); the cache holds
  * keys already rotated at their positions (built with srt_rope_apply).  The
- * keys [0, seq_len_b) are cut into num_splits blocks of ceil(Nk/num_splits);
+ * visible keys are cut into num_splits blocks: all of [0, seq_len_b) without
+ * a window; with window > 0 only [max(0, seq_len_b - window), seq_len_b) plus
+ * the sinks [0, min(sink, seq_len_b)) ([LC] §10.1-10.2, same rule as
+ * srt_attn_prefill at query position seq_len_b - 1), so a windowed step reads
+ * O(window + sink) cache rows.  Blocks hold ceil(span/num_splits) keys, span =
+ * Nk without a window, min(Nk, window + sink) with one;
  * a first kernel computes each block's partial (O, lse) into the workspace,
  * a second merges the partials with the log-sum-exp rule ([BK] §8.3.6 query
  * phase: partial results combined by online softmax).
@@ -230,7 +242,7 @@ int srt_attn_decode_workspace_size(int B, int Hq, int D, int num_splits, size_t*
 int srt_attn_decode_splitk(const void* q, const void* k_cache, const void* v_cache, int dtype,
                            int B, int Hq, int Hkv, int Nk, int D, const int* seq_lens_dev,
                            int num_splits, float sm_scale, const float* table_dev, long long table_npos,
-                           int pairing, void* workspace, size_t workspace_bytes,
+                           int pairing, int window, int sink, void* workspace, size_t workspace_bytes,
                            void* out, float* lse, void* stream);
 
 #ifdef __cplusplus

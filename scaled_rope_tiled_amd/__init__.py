@@ -146,12 +146,14 @@ def rope_apply(x: torch.Tensor, table: torch.Tensor, pos0: int = 0, out: torch.T
 def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, sm_scale: float | None = None,
                  causal: bool = True, q_pos0: int = 0, k_pos0: int = 0, table: torch.Tensor | None = None,
                  rope_flags: int | None = None, out: torch.Tensor | None = None,
-                 out_dtype: torch.dtype | None = None, lse: torch.Tensor | bool = True):
+                 out_dtype: torch.dtype | None = None, lse: torch.Tensor | bool = True,
+                 window: int = 0, sink: int = 0):
     """Tiled causal attention with rotate-on-load RoPE.
 
     q [B, Hq, Nq, D], k/v [B, Hkv, Nk, D] (views sliced along N allowed).
     rope_flags defaults to ROTATE_Q|ROTATE_K when a table is given; add
-    PAIR_HALF for half-split pairs.
+    PAIR_HALF for half-split pairs.  window > 0 (causal only) keeps key j for
+    query i iff i - j < window or j < sink (absolute positions).
     Returns (out [B, Hq, Nq, D], lse [B, Hq, Nq] fp32 or None)."""
     B, Hq, Nq, D = q.shape
     _, Hkv, Nk, _ = k.shape
@@ -178,7 +180,7 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, sm_scale:
         rope_flags = (ROTATE_Q | ROTATE_K) if table is not None else 0
     sm = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
     _lib.check(lib().srt_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _dt(q), B, Hq, Hkv, Nq, Nk, D,
-                                      qs, ks, int(q_pos0), int(k_pos0), int(bool(causal)), sm,
+                                      qs, ks, int(q_pos0), int(k_pos0), int(bool(causal)), int(window), int(sink), sm,
                                       _ptr(table), 0 if table is None else table.shape[0], int(rope_flags),
                                       _ptr(out), _dt(out), os_, _ptr(lse), ls, _stream(q.device)),
                "attn_prefill")
@@ -217,7 +219,8 @@ def attn_decode_workspace_size(B: int, Hq: int, D: int, num_splits: int) -> int:
 
 def attn_decode_splitk(q, k_cache, v_cache, *, num_splits: int, sm_scale: float | None = None,
                        table: torch.Tensor | None = None, seq_lens: torch.Tensor | None = None,
-                       workspace: torch.Tensor | None = None, out=None, lse=True, pairing="interleaved"):
+                       workspace: torch.Tensor | None = None, out=None, lse=True, pairing="interleaved",
+                       window: int = 0, sink: int = 0):
     """Split-K decode.  q [B, Hq, D] raw (rotated at seq_len-1 when a table is given);
     k_cache/v_cache [B, Hkv, Nk, D] with rotated keys.  Returns (out [B, Hq, D], lse [B, Hq])."""
     B, Hq, D = q.shape
@@ -240,6 +243,7 @@ def attn_decode_splitk(q, k_cache, v_cache, *, num_splits: int, sm_scale: float 
     _lib.check(lib().srt_attn_decode_splitk(_ptr(q), _ptr(k_cache), _ptr(v_cache), _dt(q), B, Hq, Hkv, Nk, D,
                                             _ptr(seq_lens), int(num_splits), sm, _ptr(table),
                                             0 if table is None else table.shape[0], _pairing(pairing),
+                                            int(window), int(sink),
                                             _ptr(workspace),
                                             workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
                                             _stream(q.device)), "attn_decode_splitk")

@@ -29,7 +29,7 @@ SIGNATURES = {
                        c_void_p],
     "srt_attn_prefill": [c_void_p, c_void_p, c_void_p, c_int,
                          c_int, c_int, c_int, c_int, c_int, c_int,
-                         c_ll, c_ll, c_ll, c_ll, c_int, c_float,
+                         c_ll, c_ll, c_ll, c_ll, c_int, c_int, c_int, c_float,
                          c_void_p, c_ll, c_int,
                          c_void_p, c_int, c_ll, c_void_p, c_ll, c_void_p],
     "srt_attn_merge_states": [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_ll,
@@ -38,7 +38,7 @@ SIGNATURES = {
     "srt_attn_decode_workspace_size": [c_int, c_int, c_int, c_int, C.POINTER(c_size_t)],
     "srt_attn_decode_splitk": [c_void_p, c_void_p, c_void_p, c_int,
                                c_int, c_int, c_int, c_int, c_int, c_void_p,
-                               c_int, c_float, c_void_p, c_ll, c_int,
+                               c_int, c_float, c_void_p, c_ll, c_int, c_int, c_int,
                                c_void_p, c_size_t, c_void_p, c_void_p, c_void_p],
 }
 

@@ -3,6 +3,7 @@
 #include "../../include/srt.h"
 #include "srt_internal.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -165,7 +166,7 @@ int srt_rope_apply(const void* x, void* y, int dtype, int B, int H, int N, int D
 
 int srt_attn_prefill(const void* q, const void* k, const void* v, int dtype, int B, int Hq, int Hkv, int Nq,
                      int Nk, int D, long long q_hstride, long long kv_hstride, long long q_pos0,
-                     long long k_pos0, int causal, float sm_scale, const float* table_dev,
+                     long long k_pos0, int causal, int window, int sink, float sm_scale, const float* table_dev,
                      long long table_npos, int rope_flags, void* out, int out_dtype, long long o_hstride,
                      float* lse, long long lse_hstride, void* stream) {
   if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return fail(SRT_ERR_INVALID, "attn_prefill: bad dtype");
@@ -190,6 +191,8 @@ int srt_attn_prefill(const void* q, const void* k, const void* v, int dtype, int
     return fail(SRT_ERR_INVALID, "attn_prefill: k positions [%lld, %lld) outside table [0, %lld)", k_pos0,
                 k_pos0 + Nk, table_npos);
   if (!std::isfinite(sm_scale)) return fail(SRT_ERR_INVALID, "attn_prefill: sm_scale not finite");
+  if (window < 0 || sink < 0) return fail(SRT_ERR_INVALID, "attn_prefill: window and sink must be >= 0");
+  if (window > 0 && !causal) return fail(SRT_ERR_INVALID, "attn_prefill: a sliding window needs causal = 1");
   if (Nq > (1 << 30) || Nk > (1 << 30)) return fail(SRT_ERR_UNSUPPORTED, "attn_prefill: N above 2^30");
   srt::PrefillArgs a{};
   a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.table = table_dev;
@@ -197,6 +200,7 @@ int srt_attn_prefill(const void* q, const void* k, const void* v, int dtype, int
   a.q_pos0 = q_pos0; a.k_pos0 = k_pos0;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.D = D;
   a.causal = causal ? 1 : 0; a.rope_flags = rope_flags; a.out_bf16 = out_dtype == SRT_BF16;
+  a.window = window; a.sink = window > 0 ? sink : 0;
   a.sm_scale = sm_scale;
   if (dtype == SRT_BF16) {
     if (D != 128) return fail(SRT_ERR_UNSUPPORTED, "attn_prefill: bf16 kernel needs D = 128 (got %d)", D);
@@ -241,7 +245,8 @@ int srt_attn_decode_workspace_size(int B, int Hq, int D, int num_splits, size_t*
 
 int srt_attn_decode_splitk(const void* q, const void* k_cache, const void* v_cache, int dtype, int B, int Hq,
                            int Hkv, int Nk, int D, const int* seq_lens_dev, int num_splits, float sm_scale,
-                           const float* table_dev, long long table_npos, int pairing, void* workspace,
+                           const float* table_dev, long long table_npos, int pairing, int window, int sink,
+                           void* workspace,
                            size_t workspace_bytes, void* out, float* lse, void* stream) {
   if (!valid_dtype(dtype)) return fail(SRT_ERR_INVALID, "attn_decode_splitk: bad dtype");
   if (B < 0 || Hq < 1 || Hkv < 1 || Nk < 0) return fail(SRT_ERR_INVALID, "attn_decode_splitk: bad sizes");
@@ -256,6 +261,7 @@ int srt_attn_decode_splitk(const void* q, const void* k_cache, const void* v_cac
   if (table_dev && table_npos < Nk)
     return fail(SRT_ERR_INVALID, "attn_decode_splitk: table has %lld positions, query may sit at %d", table_npos, Nk - 1);
   if (!std::isfinite(sm_scale)) return fail(SRT_ERR_INVALID, "attn_decode_splitk: sm_scale not finite");
+  if (window < 0 || sink < 0) return fail(SRT_ERR_INVALID, "attn_decode_splitk: window and sink must be >= 0");
   if (dtype != SRT_BF16 || D != 128)
     return fail(SRT_ERR_UNSUPPORTED, "attn_decode_splitk: kernel needs bf16 and D = 128");
   {
@@ -277,7 +283,12 @@ int srt_attn_decode_splitk(const void* q, const void* k_cache, const void* v_cac
   a.ws_lse = (float*)((char*)workspace + (size_t)B * Hq * num_splits * D * sizeof(float));
   a.out = out; a.lse = lse;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nk = Nk; a.D = D; a.splits = num_splits;
-  a.split_len = Nk > 0 ? (Nk + num_splits - 1) / num_splits : 0;
+  a.window = window; a.sink = window > 0 ? sink : 0;
+  {
+    // keys a sequence can see: the whole cache, or its window plus the sinks
+    const long long span = window > 0 ? std::min<long long>(Nk, (long long)window + a.sink) : Nk;
+    a.split_len = (int)((span + num_splits - 1) / num_splits);
+  }
   a.sm_scale = sm_scale;
   return hip_status(srt::launch_decode(a, (hipStream_t)stream), "attn_decode_splitk launch");
 }

@@ -3,7 +3,8 @@
 //
 // Every decode step streams the whole K/V cache from HBM ("Long Context: RoPE
 // / YaRN / NTK / MLA" §12.3), so the kernel is bound by HBM bandwidth.  The
-// cache rows [0, seq_len) of a sequence are cut into `splits` blocks; one
+// cache rows [0, seq_len) of a sequence (with a sliding window, only the
+// window's rows and the sinks, §10.1-10.2) are cut into `splits` blocks; one
 // workgroup reads one block of one KV head exactly once (K and V in the same
 // pass) and serves all query heads of that GQA group from registers.  The
 // partial results (O_s, lse_s) are merged by a second, tiny kernel with the
@@ -57,8 +58,18 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
   const int rgroup = tid / kLanesPerRow;                 // 0..31
   int seq = a.seq_lens ? a.seq_lens[b] : a.Nk;
   seq = seq < 0 ? 0 : (seq > a.Nk ? a.Nk : seq);
+  // Visible keys, numbered u = 0 .. nvis-1: without a window the rows [0, seq);
+  // with one, the sinks [0, ns) that are not already in the window, then the
+  // window [wlo, seq).  Key u sits at cache row u (u < ns) or u + (wlo - ns).
+  int ns = 0, wshift = 0, nvis = seq;
+  if (a.window > 0) {
+    const int wlo = max(0, seq - a.window);
+    ns = min(a.sink, wlo);
+    wshift = wlo - ns;
+    nvis = ns + (seq - wlo);
+  }
   const int lo = split * a.split_len;
-  const int hi = min(seq, lo + a.split_len);
+  const int hi = min(nvis, lo + a.split_len);
   const int h0 = hk * G;
   float* ws_o = a.ws_o + (((long long)b * a.Hq + h0) * a.splits + split) * kD;
   float* ws_l = a.ws_lse + ((long long)b * a.Hq + h0) * a.splits + split;
@@ -137,7 +148,8 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     for (int u = 0; u < kUnroll; ++u) {
       const int row = r0 + u * kRowsPerIter + rgroup;
       valid[u] = row < hi;
-      const long long off = (long long)(valid[u] ? row : lo) * (kD / 8);
+      const int vrow = valid[u] ? row : lo;
+      const long long off = (long long)(vrow < ns ? vrow : vrow + wshift) * (kD / 8);
       kw[u][0] = kg[off + sub];
       kw[u][1] = kg[off + sub + 8];
       vw[u][0] = vg[off + sub];

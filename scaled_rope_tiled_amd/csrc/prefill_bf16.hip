@@ -16,9 +16,11 @@
 //     which the dispatcher spreads round-robin over the 8 XCDs, keep one head
 //     per XCD L2; the y index walks query tiles from the last (most keys under
 //     the causal mask) to the first, so the long tiles start first.
-//   * Key tiles wholly above the causal diagonal are never visited; only the
-//     32-key halves that cross the diagonal (or the ragged end of K) evaluate
-//     the mask, one integer compare per score.
+//   * Key tiles wholly above the causal diagonal, or wholly before the sliding
+//     window of the workgroup's rows (sinks aside: "Long Context..." §10.1-10.2),
+//     are never visited; only the 32-key halves that cross the diagonal, the
+//     window's edge or the ragged end of K evaluate the mask (integer
+//     compares per score).
 //
 // Matrix-core mapping (v_mfma_f32_32x32x16_bf16, wave64)
 //   S^T[keys][queries] = K[keys][d] Q^T[d][queries]: A = 32x16 block of K read
@@ -227,9 +229,27 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
     const long long lim = a.q_pos0 + wg_row_last - a.k_pos0 + 1;
     kend = (int)max(0LL, min((long long)a.Nk, lim));
   }
-  const int ntiles = (kend + kBN - 1) / kBN;
+  // Sliding window: keys before the window of the workgroup's first row are
+  // invisible to all its rows except the sinks (positions < sink).  Tiles run
+  // over [0, nsk) and then from the window's first tile; tile t of the walk is
+  // key tile t (t < nsk) or t + shift.  Each tile is visited once and the
+  // per-key mask is exact, so the two ranges may touch.
+  int nsk = 0, shift = 0, ntiles = (kend + kBN - 1) / kBN;
+  int csink = 0;                                  // keys c < csink are sinks
+  long long wave_lo_lim = -(1LL << 40);           // keys >= this are in every row's window
+  if (a.window > 0) {
+    const long long lo = a.q_pos0 + (long long)qt * (kBM * RB) - a.window + 1 - a.k_pos0;
+    csink = (int)min((long long)kend, max(0LL, (long long)a.sink - a.k_pos0));
+    nsk = (csink + kBN - 1) / kBN;
+    const int tstart = lo >= kend ? ntiles : max(nsk, (int)(max(0LL, lo) / kBN));
+    shift = tstart - nsk;
+    ntiles = nsk + max(0, ntiles - tstart);
+    wave_lo_lim = a.q_pos0 + wrow0 + (kBM - 1) - a.window + 1 - a.k_pos0;
+  }
+  auto tile_key0 = [&](int t) { return (t < nsk ? t : t + shift) * kBN; };
   // keys of a tile starting at key0 are all visible to every row of this wave iff
-  // key0 + kBN <= Nk and k_pos0 + key0 + kBN - 1 <= q_pos0 + wrow0
+  // key0 + kBN <= Nk and k_pos0 + key0 + kBN - 1 <= q_pos0 + wrow0 (and, with a
+  // window, the tile lies in every row's window or among the sinks)
   const long long wave_free_lim = a.causal ? (a.q_pos0 + wrow0 - a.k_pos0 + 1) : (long long)a.Nk;
 
   // ---- staging assignment: chunk sc (16 bytes = dims 8sc..8sc+7) of rows sr and sr + 32
@@ -304,13 +324,17 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   float m_run = -INFINITY;       // running max of this lane's query, in scaled log2 units
   float l_run = 0.f;             // this lane's partial sum (its 16 keys of every 32)
   const float cscale = a.sm_scale * kLog2e;
-  // Mask as one integer compare per score: key index c is visible to this
-  // lane's query iff c <= klim (causal: k_pos0 + c <= q_pos0 + wrow0 + l32; and c < Nk).
-  int klim;
+  // Mask as integer compares per score: key index c is visible to this lane's
+  // query iff c <= klim (causal: k_pos0 + c <= q_pos0 + wrow0 + l32; and
+  // c < Nk) and, with a window, c >= klo (inside the window) or c < csink.
+  int klim, klo;
   {
     long long lim = a.causal ? (a.q_pos0 + wrow0 + l32 - a.k_pos0) : (long long)a.Nk - 1;
     lim = lim < (long long)a.Nk - 1 ? lim : (long long)a.Nk - 1;
     klim = (int)(lim < -1 ? -1 : lim);
+    long long lo = a.window > 0 ? a.q_pos0 + wrow0 + l32 - a.window + 1 - a.k_pos0 : -(1LL << 30);
+    lo = lo < -(1LL << 30) ? -(1LL << 30) : lo;
+    klo = (int)(lo > (1LL << 30) ? (1LL << 30) : lo);
   }
   const int gj = lane & 15;
   const int gd = ((lane >> 4) & 1) * 16 + 4 * (gj & 3);    // d offset inside a 32-wide block
@@ -361,7 +385,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   // softmax, so with no branch in between the scheduler interleaves the wave's
   // MFMAs with its VALU softmax.  A rescale of O decided by the softmax of half
   // h is applied at the start of step h+1, after PV(h-1) and before PV(h).
-  auto step = [&](auto has_pv, int qbuf, auto qkb, int pbuf, auto pkb, int h, f32x16& s_in, f32x16& s_out,
+  auto step = [&](auto has_pv, int qbuf, auto qkb, int pbuf, auto pkb, int key0h, f32x16& s_in, f32x16& s_out,
                   const bf16x8 (&p_in)[2], bf16x8 (&p_out)[2]) {
     constexpr bool HAS_PV = decltype(has_pv)::value;
     if (HAS_PV && need_prev) {
@@ -370,11 +394,15 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
 #pragma unroll
         for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha_prev;
     }
-    const int key0h = h * 32;
-    if ((long long)key0h + 32 > wave_free_lim || key0h + 32 > a.Nk) {
-      const int rel = klim - (key0h + hl * 4);
+    if ((long long)key0h + 32 > wave_free_lim || key0h + 32 > a.Nk ||
+        ((long long)key0h < wave_lo_lim && key0h + 32 > csink)) {
+      const int base = key0h + hl * 4;
+      const int rel = klim - base, rlo = klo - base, rsk = csink - base;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) s_in[j] = ((j >> 2) * 8 + (j & 3)) <= rel ? s_in[j] : -INFINITY;
+      for (int j = 0; j < 16; ++j) {
+        const int cj = (j >> 2) * 8 + (j & 3);
+        s_in[j] = (cj <= rel && (cj >= rlo || cj < rsk)) ? s_in[j] : -INFINITY;
+      }
     }
 
     // matrix work of this step (the QK of the half after the last one reads a
@@ -416,7 +444,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   auto tile_io = [&](int next_buf, int t) {
     store_lds(next_buf);
     __syncthreads();
-    issue_loads((t + 2) * kBN);
+    issue_loads(tile_key0(t + 2));
   };
   using T = std::true_type;
   using F = std::false_type;
@@ -424,20 +452,22 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   using K1 = std::integral_constant<int, 1>;
 
   if (ntiles > 0) {
-    issue_loads(0);
+    issue_loads(tile_key0(0));
     store_lds(0);
     __syncthreads();
-    issue_loads(kBN);
+    issue_loads(tile_key0(1));
     qk(0, K0{}, s_a);
-    step(F{}, 0, K1{}, 0, K0{}, 0, s_a, s_b, p_b, p_a);
+    const int key00 = tile_key0(0);
+    step(F{}, 0, K1{}, 0, K0{}, key00, s_a, s_b, p_b, p_a);
     tile_io(1, 0);
-    step(T{}, 1, K0{}, 0, K0{}, 1, s_b, s_a, p_a, p_b);
+    step(T{}, 1, K0{}, 0, K0{}, key00 + 32, s_b, s_a, p_a, p_b);
     int cur = 1;                           // buffer of tile t = t % 3
     for (int t = 1; t < ntiles; ++t) {
       const int prev = cur == 0 ? 2 : cur - 1, next = cur == 2 ? 0 : cur + 1;
-      step(T{}, cur, K1{}, prev, K1{}, 2 * t, s_a, s_b, p_b, p_a);
+      const int key0 = tile_key0(t);
+      step(T{}, cur, K1{}, prev, K1{}, key0, s_a, s_b, p_b, p_a);
       tile_io(next, t);
-      step(T{}, next, K0{}, cur, K0{}, 2 * t + 1, s_b, s_a, p_a, p_b);
+      step(T{}, next, K0{}, cur, K0{}, key0 + 32, s_b, s_a, p_a, p_b);
       cur = next;
     }
     if (need_prev) {

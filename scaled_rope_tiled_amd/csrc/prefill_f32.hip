@@ -8,7 +8,8 @@
 // then applies the online softmax: new running max, rescale of the earlier
 // accumulator and sum, exponentials of this tile ("8.3 长上下文技术" §8.3.4
 // (1)-(2)); the N x N score matrix never exists.  Key tiles wholly above the
-// causal diagonal of the wave's rows are never visited.
+// causal diagonal of the wave's rows, or wholly before its sliding window
+// (sinks aside, "Long Context..." §10.1-10.2), are never visited.
 #include "srt_internal.h"
 
 namespace srt {
@@ -79,8 +80,24 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillArgs a) {
     kend = (int)max(0LL, min((long long)a.Nk, lim));
   }
 
+  // Sliding window: keys before (first query position - window + 1) are
+  // invisible to every row here except the sinks (positions < sink).  Tiles
+  // run over [0, sink tiles) and then [window start, kend); each tile is
+  // visited once and the per-key mask below is exact, so the two ranges may
+  // touch.
+  int nsk = 0, shift = 0, ntiles = (kend + kKeys - 1) / kKeys;
+  if (a.window > 0) {
+    const long long lo = a.q_pos0 + (long long)qtile * kRows - a.window + 1 - a.k_pos0;
+    const long long cs = min((long long)kend, max(0LL, (long long)a.sink - a.k_pos0));
+    nsk = (int)((cs + kKeys - 1) / kKeys);
+    const int tstart = lo >= kend ? ntiles : max(nsk, (int)(max(0LL, lo) / kKeys));
+    shift = tstart - nsk;
+    ntiles = nsk + max(0, ntiles - tstart);
+  }
+
   float m = -INFINITY, l = 0.f;
-  for (int c0 = 0; c0 < kend; c0 += kKeys) {
+  for (int ti = 0; ti < ntiles; ++ti) {
+    const int c0 = (ti < nsk ? ti : ti + shift) * kKeys;
     __syncthreads();
     // stage 32 key rows (rotated) and value rows; lane handles pair columns
     for (int e = lane; e < kKeys * (D / 2); e += 64) {
@@ -108,7 +125,8 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillArgs a) {
 #pragma unroll
       for (int d = 0; d < D; ++d) acc = fmaf(q[d], ks[c][d], acc);
       const long long kpos = a.k_pos0 + c0 + c;
-      const bool vis = (c0 + c < kend) && (!a.causal || kpos <= qpos);
+      const bool vis = (c0 + c < kend) && (!a.causal || kpos <= qpos) &&
+                       (a.window <= 0 || qpos - kpos < a.window || kpos < a.sink);
       s[c] = vis ? acc : -INFINITY;
       tmax = fmaxf(tmax, s[c]);
     }

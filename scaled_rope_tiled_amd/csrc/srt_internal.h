@@ -37,6 +37,8 @@ struct PrefillArgs {
   int causal;
   int rope_flags;       // bit0: rotate q, bit1: rotate k, bit2: half-split pairs
   int out_bf16;         // 1: out is bf16, 0: fp32
+  int window;           // > 0: key j visible to query i only if i - j < window or j < sink
+  int sink;             // first positions kept visible (used only with a window)
   float sm_scale;
 };
 
@@ -71,6 +73,7 @@ struct DecodeArgs {
   float* lse;             // [B][Hq] or nullptr
   int B, Hq, Hkv, Nk, D, splits, split_len;
   int half_pairs;         // q rotated with pairs (x_i, x_{i+D/2})
+  int window, sink;       // window > 0: keys [seq - window, seq) plus [0, sink) only
   float sm_scale;
 };
 

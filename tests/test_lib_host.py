@@ -94,21 +94,30 @@ def test_abi_rejects_before_launch(srt):
     """Argument errors return SRT_ERR_INVALID / UNSUPPORTED with no GPU call."""
     lib = srt.lib()
     fake = C.c_void_p(0x100000)      # never dereferenced: every call below fails validation first
-    st = lib.srt_attn_prefill(None, fake, fake, 1, 1, 4, 2, 8, 8, 128, 1024, 1024, 0, 0, 1, 0.1,
+    st = lib.srt_attn_prefill(None, fake, fake, 1, 1, 4, 2, 8, 8, 128, 1024, 1024, 0, 0, 1, 0, 0, 0.1,
                               None, 0, 0, fake, 1, 1024, None, 0, None)
     assert st == 1 and b"NULL" in lib.srt_last_error()
-    st = lib.srt_attn_prefill(fake, fake, fake, 1, 1, 4, 3, 8, 8, 128, 1024, 1024, 0, 0, 1, 0.1,
+    st = lib.srt_attn_prefill(fake, fake, fake, 1, 1, 4, 3, 8, 8, 128, 1024, 1024, 0, 0, 1, 0, 0, 0.1,
                               None, 0, 0, fake, 1, 1024, None, 0, None)
     assert st == 1 and b"multiple" in lib.srt_last_error()
-    st = lib.srt_attn_prefill(fake, fake, fake, 1, 1, 4, 2, 8, 8, 96, 768, 768, 0, 0, 1, 0.1,
+    st = lib.srt_attn_prefill(fake, fake, fake, 1, 1, 4, 2, 8, 8, 96, 768, 768, 0, 0, 1, 0, 0, 0.1,
                               None, 0, 0, fake, 1, 768, None, 0, None)
     assert st == 2
-    st = lib.srt_attn_prefill(fake, fake, fake, 1, 1, 4, 2, 8, 8, 128, 1024, 1024, 0, 0, 1, 0.1,
+    st = lib.srt_attn_prefill(fake, fake, fake, 1, 1, 4, 2, 8, 8, 128, 1024, 1024, 0, 0, 1, 0, 0, 0.1,
                               None, 0, 3, fake, 1, 1024, None, 0, None)
     assert st == 1 and b"table" in lib.srt_last_error()
-    st = lib.srt_attn_prefill(fake, fake, fake, 1, 1, 4, 2, 8, 8, 128, 1024, 1024, 0, 0, 1, 0.1,
+    st = lib.srt_attn_prefill(fake, fake, fake, 1, 1, 4, 2, 8, 8, 128, 1024, 1024, 0, 0, 1, 0, 0, 0.1,
                               fake, 4, 3, fake, 1, 1024, None, 0, None)
     assert st == 1 and b"outside table" in lib.srt_last_error()
+    st = lib.srt_attn_prefill(fake, fake, fake, 1, 1, 4, 2, 8, 8, 128, 1024, 1024, 0, 0, 0, 16, 0, 0.1,
+                              None, 0, 0, fake, 1, 1024, None, 0, None)
+    assert st == 1 and b"causal" in lib.srt_last_error()
+    st = lib.srt_attn_prefill(fake, fake, fake, 1, 1, 4, 2, 8, 8, 128, 1024, 1024, 0, 0, 1, -1, 0, 0.1,
+                              None, 0, 0, fake, 1, 1024, None, 0, None)
+    assert st == 1 and b"window" in lib.srt_last_error()
+    st = lib.srt_attn_prefill(fake, fake, fake, 1, 1, 4, 2, 8, 8, 128, 1024, 1024, 0, 0, 1, 16, -4, 0.1,
+                              None, 0, 0, fake, 1, 1024, None, 0, None)
+    assert st == 1 and b"sink" in lib.srt_last_error()
     st = lib.srt_rope_apply(fake, fake, 1, 1, 1, 8, 128, 5, fake, 10, 0, None)
     assert st == 1 and b"outside table" in lib.srt_last_error()
     st = lib.srt_rope_apply(fake, fake, 7, 1, 1, 8, 128, 0, fake, 10, 0, None)
@@ -120,15 +129,18 @@ def test_abi_rejects_before_launch(srt):
     n = C.c_size_t()
     assert lib.srt_attn_decode_workspace_size(16, 32, 128, 64, C.byref(n)) == 0
     assert n.value == 16 * 32 * 64 * 129 * 4
-    st = lib.srt_attn_decode_splitk(fake, fake, fake, 1, 16, 32, 8, 1024, 128, None, 64, 0.1, None, 0, 0,
+    st = lib.srt_attn_decode_splitk(fake, fake, fake, 1, 16, 32, 8, 1024, 128, None, 64, 0.1, None, 0, 0, 0, 0,
                                     fake, n.value - 1, fake, None, None)
     assert st == 4
-    st = lib.srt_attn_decode_splitk(fake, fake, fake, 1, 16, 24, 8, 1024, 128, None, 64, 0.1, None, 0, 0,
+    st = lib.srt_attn_decode_splitk(fake, fake, fake, 1, 16, 24, 8, 1024, 128, None, 64, 0.1, None, 0, 0, 0, 0,
                                     fake, n.value, fake, None, None)
     assert st == 2
-    st = lib.srt_attn_decode_splitk(fake, fake, fake, 1, 16, 32, 8, 1024, 128, None, 0, 0.1, None, 0, 0,
+    st = lib.srt_attn_decode_splitk(fake, fake, fake, 1, 16, 32, 8, 1024, 128, None, 0, 0.1, None, 0, 0, 0, 0,
                                     fake, n.value, fake, None, None)
     assert st == 1
+    st = lib.srt_attn_decode_splitk(fake, fake, fake, 1, 16, 32, 8, 1024, 128, None, 64, 0.1, None, 0, 0, -1, 0,
+                                    fake, n.value, fake, None, None)
+    assert st == 1 and b"window" in lib.srt_last_error()
     st = lib.srt_attn_merge_states(fake, fake, fake, fake, 0, 64, fake, 1, 128, None, 0, 1, 1, 1, 128, None)
     assert st == 1 and b"stride" in lib.srt_last_error()
     st = lib.srt_attn_merge_states(fake, fake, fake, fake, 0, 96, fake, 0, 96, None, 0, 1, 1, 1, 96, None)
