@@ -18,8 +18,9 @@ same line carries:
     on the current kernel source (else null);
   * ``decode``: 128K split-K decode (B=16, GQA 32/8, PI s=16, 64 splits):
     algorithmic bytes / time against the 8 TB/s HBM peak;
-  * ``ring``: the 128K NTK prefill as 8 K/V chunks of 16384 merged by
-    log-sum-exp (one device's ring step), TFLOP/s;
+  * ``ring``: the 128K NTK prefill as Ring Attention over 8 devices run on
+    this GPU (contiguous, zig-zag and striped shards): TFLOP/s of the whole
+    ring and each device's share timed alone;
   * ``window``: the same prefill with a 4096-key sliding window and 4 sink
     tokens (flops of the kept pairs only), and its time against full causal;
   * ``cpu_baseline``: the fp64 oracle on the host cores, on a bounded sample.
@@ -252,67 +253,73 @@ def bench_decode(srt, torch, w, steps, warmup):
 # ----------------------------------------------------------------------------- ring step on one GPU
 
 def bench_ring(srt, torch, w, steps, warmup):
+    """One device's ring step, for all P = w.chunks devices of a ring, run on
+    this GPU with srt_attn_ring_prefill (K rotated once into the workspace, q
+    on load); once per partition.  The whole ring gives the job's TFLOP/s;
+    each device's share, timed alone, gives the per-device balance (the step
+    time of a real P-GPU ring is its slowest device, transfers aside)."""
+    import numpy as np
     import synth
-    D, N, C = w.D, w.N, w.N // w.chunks
+    D, N, P = w.D, w.N, w.chunks
     q = synth.randn((w.B, w.Hq, N, D), torch.bfloat16, w.seed, synth.Q_ID, "cuda")
     k = synth.randn((w.B, w.Hkv, N, D), torch.bfloat16, w.seed, synth.K_ID, "cuda")
     v = synth.randn((w.B, w.Hkv, N, D), torch.bfloat16, w.seed, synth.V_ID, "cuda")
     rp = w.rope
     th, ms, _ = srt.rope_inv_freq(rp.method, rp.base, rp.s, rp.L, rp.alpha, rp.beta, D)
+    flops = prefill_flops(w.B, w.Hq, N, N, D)
     out = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, N), dtype=torch.float32, device="cuda")
-    acc = torch.empty((w.B, w.Hq, C, D), dtype=torch.float32, device="cuda")
-    acc_l = torch.empty((w.B, w.Hq, C), dtype=torch.float32, device="cuda")
-    tmp = torch.empty_like(acc)
-    tmp_l = torch.empty_like(acc_l)
-
-    krot = torch.empty_like(k)
-
-    def step():
-        table = srt.rope_cos_sin(th, D, ms, N, "cuda")
-        srt.rope_apply(k, table, out=krot)             # K rotated once at its absolute positions
-        ring_step(srt, q, krot, v, table, out, lse, acc, acc_l, tmp, tmp_l, w.chunks, srt.ROTATE_Q)
-
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / steps
-    flops = prefill_flops(w.B, w.Hq, N, N, D)
-    tf = flops / (ms_step * 1e-3) / 1e12
-    return {"workload": w.name, "unit": "TFLOP/s", "value": round(tf, 2), "ms_per_step": round(ms_step, 3),
-            "chunks": w.chunks, "launches": {"prefill": w.chunks * (w.chunks + 1) // 2,
-                                             "merge": w.chunks * (w.chunks - 1) // 2},
-            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
-
-
-def ring_step(srt, q, k, v, table, out, lse, acc, acc_l, tmp, tmp_l, chunks, rope_flags=None):
-    """Query chunk i attends K/V chunks 0..i at their absolute offsets; partial
-    states (fp32) are merged by log-sum-exp; the last merge writes bf16 output.
-    rope_flags=ROTATE_Q when k is already rotated; None rotates q and k on load."""
-    N = q.shape[2]
-    C = N // chunks
-    for i in range(chunks):
-        qi = q[:, :, i * C:(i + 1) * C]
-        oi, li = out[:, :, i * C:(i + 1) * C], lse[:, :, i * C:(i + 1) * C]
-        if i == 0:
-            srt.attn_prefill(qi, k[:, :, :C], v[:, :, :C], q_pos0=0, k_pos0=0, table=table, out=oi, lse=li,
-                             rope_flags=rope_flags)
-            continue
-        for j in range(i + 1):
-            kj, vj = k[:, :, j * C:(j + 1) * C], v[:, :, j * C:(j + 1) * C]
-            dst, dst_l = (acc, acc_l) if j == 0 else (tmp, tmp_l)
-            srt.attn_prefill(qi, kj, vj, q_pos0=i * C, k_pos0=j * C, table=table, out=dst, lse=dst_l,
-                             rope_flags=rope_flags)
-            if j == 0:
-                continue
-            if j < i:
-                srt.attn_merge_states(acc, acc_l, tmp, tmp_l, out=acc, lse_out=acc_l)
+    res = {}
+    for part in ("contiguous", "zigzag", "striped"):
+        if part == "contiguous":
+            qs, ks, vs = q, k, v
+        else:
+            C = N // P
+            if part == "striped":
+                pos = (np.arange(P)[:, None] + P * np.arange(C)[None, :]).reshape(-1)
             else:
-                srt.attn_merge_states(acc, acc_l, tmp, tmp_l, out=oi, lse_out=li)
+                h = C // 2
+                pos = np.concatenate([np.concatenate([r * h + np.arange(h), (2 * P - 1 - r) * h + np.arange(h)])
+                                      for r in range(P)])
+            ip = torch.from_numpy(pos).cuda()
+            qs, ks, vs = (t.index_select(2, ip).contiguous() for t in (q, k, v))
+        ws = torch.empty(srt.attn_ring_workspace_size(w.B, w.Hq, w.Hkv, N, D, torch.bfloat16, P, part),
+                         dtype=torch.uint8, device="cuda")
+
+        def ring(device=-1):
+            table = srt.rope_cos_sin(th, D, ms, N, "cuda")
+            srt.attn_ring_prefill(qs, ks, vs, num_devices=P, partition=part, device=device, table=table,
+                                  workspace=ws, out=out, lse=lse)
+
+        for _ in range(warmup):
+            ring()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            ring()
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t0) * 1e3 / steps
+        dev_ms = []
+        for r in range(P):
+            t = Timer(torch)
+            for _ in range(2):
+                t.run(lambda: ring(r))
+            torch.cuda.synchronize()
+            dev_ms.append(t.mean_ms())
+        tf = flops / (ms_step * 1e-3) / 1e12
+        res[part] = {"ms_per_step": round(ms_step, 3), "tflops": round(tf, 2),
+                     "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "device_ms": [round(x, 3) for x in dev_ms],
+                     "slowest_device_ms": round(max(dev_ms), 3),
+                     "slowest_over_mean": round(max(dev_ms) / (sum(dev_ms) / P), 3)}
+        if part != "contiguous":
+            del qs, ks, vs
+        del ws
+        torch.cuda.empty_cache()
+    c = res["contiguous"]
+    return {"workload": w.name, "unit": "TFLOP/s", "value": c["tflops"], "ms_per_step": c["ms_per_step"],
+            "devices": P, "frac_of_bf16_peak": c["frac_of_bf16_peak"], "partitions": res,
+            "note": "all devices' shares run on this GPU; device_ms times each share alone (compute only)"}
 
 
 # ----------------------------------------------------------------------------- CPU baseline (oracle)

@@ -245,6 +245,52 @@ int srt_attn_decode_splitk(const void* q, const void* k_cache, const void* v_cac
                            int pairing, int window, int sink, void* workspace, size_t workspace_bytes,
                            void* out, float* lse, void* stream);
 
+/* partition argument of srt_attn_ring_prefill ([BK] §8.3.5, causal load balance) */
+#define SRT_PART_CONTIGUOUS 0   /* shard r = positions [r C, (r+1) C), C = N / P              */
+#define SRT_PART_STRIPED 1      /* shard r = positions r, r + P, r + 2P, ...                  */
+#define SRT_PART_ZIGZAG 2       /* shard r = chunk r then chunk 2P-1-r of 2P chunks of N/(2P) */
+
+/*
+ * srt_attn_ring_workspace_size - bytes of workspace srt_attn_ring_prefill needs:
+ * two fp32 partial states of one query run ([B][Hq][R][D] + [B][Hq][R], R =
+ * N/P, or N/(2P) for zigzag) and, when rope_flags has SRT_ROTATE_K, a rotated
+ * copy of K ([B][Hkv][N][D] in dtype).
+ */
+int srt_attn_ring_workspace_size(int B, int Hq, int Hkv, int N, int D, int dtype, int num_devices, int partition,
+                                 int rope_flags, size_t* bytes_out_host);
+
+/*
+ * srt_attn_ring_prefill - causal Ring Attention over num_devices = P devices,
+ * every device's work run on this GPU ([BK] §8.3.5).
+ *
+ * Device r holds query shard r and K/V shard r.  It attends its own K/V shard,
+ * then at ring step s = 1 .. P-1 the shard of device (r - s) mod P, and folds
+ * each partial state into its running one with the log-sum-exp rule (the
+ * online-softmax rescaling; same rule as srt_attn_merge_states).  The result
+ * equals srt_attn_prefill over the whole sequence (causal, same window and
+ * sinks).  `partition` chooses the positions of a shard (SRT_PART_*: Striped
+ * and Zig-Zag balance the causal work across devices); tensors are stored
+ * shard-major: row r*(N/P) + t holds row t of shard r, at the position the
+ * partition gives it.  device = -1 runs every device; 0 <= device < P runs
+ * only that device's share (writes only its N/P rows of out and lse).
+ *
+ * q: [B][Hq][N][D], k, v: [B][Hkv][N][D], contiguous, dtype (BF16 with
+ * D = 128, or F32 with D in {64, 128}); out: [B][Hq][N][D] in dtype; lse:
+ * [B][Hq][N] fp32 or NULL.  rope_flags as srt_attn_prefill: with SRT_ROTATE_K
+ * the keys are rotated once into the workspace at their positions, and
+ * without it k must already be rotated.  N a multiple of P (of 2P for
+ * zigzag); window and sink as srt_attn_prefill (window with STRIPED is
+ * unsupported).  workspace: device, >= srt_attn_ring_workspace_size bytes,
+ * 256-byte aligned.  Launches run in order on `stream`.
+ */
+int srt_attn_ring_prefill(const void* q, const void* k, const void* v, int dtype,
+                          int B, int Hq, int Hkv, int N, int D,
+                          int num_devices, int partition, int device,
+                          int window, int sink, float sm_scale,
+                          const float* table_dev, long long table_npos, int rope_flags,
+                          void* workspace, size_t workspace_bytes,
+                          void* out, float* lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,6 +13,7 @@ HIP stream; every step of the computation runs in the library's kernels.
     attn_prefill(q, k, v, ...)                        -> (out, lse)
     attn_merge_states(o_a, lse_a, o_b, lse_b, ...)    -> (out, lse)
     attn_decode_splitk(q, k_cache, v_cache, ...)      -> (out, lse)
+    attn_ring_prefill(q, k, v, num_devices=, partition=, ...) -> (out, lse)
 """
 from __future__ import annotations
 
@@ -28,10 +29,11 @@ NONE, PI, NTK, YARN = 0, 1, 2, 3
 F32, BF16 = 0, 1
 ROTATE_Q, ROTATE_K, PAIR_HALF = 1, 2, 4
 PAIRING_INTERLEAVED, PAIRING_HALF = 0, 1
+PARTITIONS = {"contiguous": 0, "striped": 1, "zigzag": 2}
 BAND_LOW, BAND_MID, BAND_HIGH = 0, 1, 2
 
 __all__ = ["rope_inv_freq", "rope_inv_freq_dynamic_ntk", "rope_inv_freq_factors", "rope_cos_sin", "rope_apply", "attn_prefill", "attn_merge_states",
-           "attn_decode_splitk", "attn_decode_workspace_size", "NONE", "PI", "NTK", "YARN",
+           "attn_decode_splitk", "attn_decode_workspace_size", "attn_ring_prefill", "attn_ring_workspace_size", "NONE", "PI", "NTK", "YARN",
            "ROTATE_Q", "ROTATE_K", "PAIR_HALF", "PAIRING_INTERLEAVED", "PAIRING_HALF", "lib"]
 
 
@@ -247,4 +249,61 @@ def attn_decode_splitk(q, k_cache, v_cache, *, num_splits: int, sm_scale: float 
                                             _ptr(workspace),
                                             workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
                                             _stream(q.device)), "attn_decode_splitk")
+    return out, lse
+
+
+def _partition(p) -> int:
+    if isinstance(p, str):
+        if p not in PARTITIONS:
+            raise ValueError(f"unknown partition {p!r}")
+        return PARTITIONS[p]
+    return int(p)
+
+
+def attn_ring_workspace_size(B: int, Hq: int, Hkv: int, N: int, D: int, dtype: torch.dtype, num_devices: int,
+                             partition="contiguous", rope_flags: int = ROTATE_Q | ROTATE_K) -> int:
+    n = C.c_size_t()
+    _lib.check(lib().srt_attn_ring_workspace_size(B, Hq, Hkv, N, D, F32 if dtype == torch.float32 else BF16,
+                                                  int(num_devices), _partition(partition), int(rope_flags),
+                                                  C.byref(n)), "attn_ring_workspace_size")
+    return n.value
+
+
+def attn_ring_prefill(q, k, v, *, num_devices: int, partition="contiguous", device: int = -1,
+                      window: int = 0, sink: int = 0, sm_scale: float | None = None,
+                      table: torch.Tensor | None = None, rope_flags: int | None = None,
+                      workspace: torch.Tensor | None = None, out=None, lse=True):
+    """Causal Ring Attention over num_devices devices run on this GPU.
+
+    q [B, Hq, N, D], k/v [B, Hkv, N, D] contiguous, rows shard-major for the
+    partition ("contiguous", "striped", "zigzag"); device=-1 runs all devices.
+    rope_flags defaults to ROTATE_Q|ROTATE_K with a table (K rotated once into
+    the workspace).  Returns (out [B, Hq, N, D] shard-major, lse [B, Hq, N])."""
+    B, Hq, N, D = q.shape
+    _, Hkv, _, _ = k.shape
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("ring tensors must be contiguous")
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != D:
+        raise ValueError("k and v must be [B, Hkv, N, D] matching q")
+    if rope_flags is None:
+        rope_flags = (ROTATE_Q | ROTATE_K) if table is not None else 0
+    need = attn_ring_workspace_size(B, Hq, Hkv, N, D, q.dtype, num_devices, partition, rope_flags)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is True:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    elif lse is False:
+        lse = None
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must match q")
+    sm = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
+    _lib.check(lib().srt_attn_ring_prefill(_ptr(q), _ptr(k), _ptr(v), _dt(q), B, Hq, Hkv, N, D,
+                                           int(num_devices), _partition(partition), int(device), int(window),
+                                           int(sink), sm, _ptr(table), 0 if table is None else table.shape[0],
+                                           int(rope_flags), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
+                                           _stream(q.device)), "attn_ring_prefill")
     return out, lse

@@ -159,8 +159,9 @@ int srt_rope_apply(const void* x, void* y, int dtype, int B, int H, int N, int D
                 pos0 + N, table_npos);
   if (misaligned16(x) || misaligned16(y) || misaligned16(table_dev))
     return fail(SRT_ERR_INVALID, "rope_apply: pointers must be 16-byte aligned");
+  const srt::PosMap map{pos0, srt::kContiguous, 1, N};
   return hip_status(srt::launch_rope_apply(x, y, dtype == SRT_BF16, pairing == SRT_PAIRING_HALF, (long long)B * H,
-                                           N, D, pos0, table_dev, (hipStream_t)stream),
+                                           N, D, map, table_dev, (hipStream_t)stream),
                     "rope_apply launch");
 }
 
@@ -198,12 +199,16 @@ int srt_attn_prefill(const void* q, const void* k, const void* v, int dtype, int
   a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.table = table_dev;
   a.q_hstride = q_hstride; a.kv_hstride = kv_hstride; a.o_hstride = o_hstride; a.lse_hstride = lse_hstride;
   a.q_pos0 = q_pos0; a.k_pos0 = k_pos0;
+  a.q_rope0 = q_pos0; a.k_rope0 = k_pos0; a.rope_step = 1;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.D = D;
   a.causal = causal ? 1 : 0; a.rope_flags = rope_flags; a.out_bf16 = out_dtype == SRT_BF16;
   a.window = window; a.sink = window > 0 ? sink : 0;
   a.sm_scale = sm_scale;
   if (dtype == SRT_BF16) {
     if (D != 128) return fail(SRT_ERR_UNSUPPORTED, "attn_prefill: bf16 kernel needs D = 128 (got %d)", D);
+    const int g = Hq / Hkv;
+    if (!(g == 1 || g == 2 || g % 4 == 0))
+      return fail(SRT_ERR_UNSUPPORTED, "attn_prefill: bf16 kernel needs Hq/Hkv in {1, 2} or a multiple of 4");
     return hip_status(srt::launch_prefill_bf16_d128(a, (hipStream_t)stream), "attn_prefill bf16 launch");
   }
   if (D != 64 && D != 128) return fail(SRT_ERR_UNSUPPORTED, "attn_prefill: fp32 kernel needs D in {64,128}");
@@ -291,6 +296,75 @@ int srt_attn_decode_splitk(const void* q, const void* k_cache, const void* v_cac
   }
   a.sm_scale = sm_scale;
   return hip_status(srt::launch_decode(a, (hipStream_t)stream), "attn_decode_splitk launch");
+}
+
+namespace {
+
+// Shared checks of the ring entry points; fills `a` on success.
+int ring_args(int dtype, int B, int Hq, int Hkv, int N, int D, int P, int partition, int rope_flags,
+              srt::RingArgs& a) {
+  if (!valid_dtype(dtype)) return fail(SRT_ERR_INVALID, "attn_ring: bad dtype");
+  if (B < 0 || Hq < 1 || Hkv < 1 || N < 0) return fail(SRT_ERR_INVALID, "attn_ring: bad sizes");
+  if (Hq % Hkv) return fail(SRT_ERR_INVALID, "attn_ring: Hq=%d not a multiple of Hkv=%d", Hq, Hkv);
+  if (P < 1 || P > 4096) return fail(SRT_ERR_INVALID, "attn_ring: num_devices=%d out of [1, 4096]", P);
+  if (partition != SRT_PART_CONTIGUOUS && partition != SRT_PART_STRIPED && partition != SRT_PART_ZIGZAG)
+    return fail(SRT_ERR_INVALID, "attn_ring: bad partition %d", partition);
+  const int parts = partition == SRT_PART_ZIGZAG ? 2 * P : P;
+  if (N % parts) return fail(SRT_ERR_INVALID, "attn_ring: N=%d must be a multiple of %d", N, parts);
+  if (rope_flags & ~(SRT_ROTATE_Q | SRT_ROTATE_K | SRT_PAIR_HALF))
+    return fail(SRT_ERR_INVALID, "attn_ring: bad rope_flags");
+  if (dtype == SRT_BF16) {
+    if (D != 128) return fail(SRT_ERR_UNSUPPORTED, "attn_ring: bf16 kernel needs D = 128 (got %d)", D);
+    const int g = Hq / Hkv;
+    if (!(g == 1 || g == 2 || g % 4 == 0))
+      return fail(SRT_ERR_UNSUPPORTED, "attn_ring: bf16 kernel needs Hq/Hkv in {1, 2} or a multiple of 4");
+  } else if (D != 64 && D != 128) {
+    return fail(SRT_ERR_UNSUPPORTED, "attn_ring: fp32 kernel needs D in {64, 128}");
+  }
+  a = srt::RingArgs{};
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N = N; a.D = D; a.P = P;
+  a.mode = partition == SRT_PART_STRIPED ? srt::kStriped : (partition == SRT_PART_ZIGZAG ? srt::kZigzag : srt::kContiguous);
+  a.rope_flags = rope_flags; a.bf16 = dtype == SRT_BF16;
+  return SRT_OK;
+}
+
+}  // namespace
+
+int srt_attn_ring_workspace_size(int B, int Hq, int Hkv, int N, int D, int dtype, int num_devices, int partition,
+                                 int rope_flags, size_t* bytes_out) {
+  if (!bytes_out) return fail(SRT_ERR_INVALID, "attn_ring_workspace_size: NULL output");
+  srt::RingArgs a;
+  const int st = ring_args(dtype, B, Hq, Hkv, N, D, num_devices, partition, rope_flags, a);
+  if (st != SRT_OK) return st;
+  *bytes_out = srt::ring_workspace_bytes(a);
+  return ok();
+}
+
+int srt_attn_ring_prefill(const void* q, const void* k, const void* v, int dtype, int B, int Hq, int Hkv, int N,
+                          int D, int num_devices, int partition, int device, int window, int sink, float sm_scale,
+                          const float* table_dev, long long table_npos, int rope_flags, void* workspace,
+                          size_t workspace_bytes, void* out, float* lse, void* stream) {
+  srt::RingArgs a;
+  const int st = ring_args(dtype, B, Hq, Hkv, N, D, num_devices, partition, rope_flags, a);
+  if (st != SRT_OK) return st;
+  if (device < -1 || device >= num_devices) return fail(SRT_ERR_INVALID, "attn_ring: device=%d out of range", device);
+  if (window < 0 || sink < 0) return fail(SRT_ERR_INVALID, "attn_ring: window and sink must be >= 0");
+  if (window > 0 && partition == SRT_PART_STRIPED)
+    return fail(SRT_ERR_UNSUPPORTED, "attn_ring: a sliding window with the striped partition is not supported");
+  if (!std::isfinite(sm_scale)) return fail(SRT_ERR_INVALID, "attn_ring: sm_scale not finite");
+  if ((long long)B * N == 0) return ok();      // nothing to compute: pointers may be NULL
+  if (!q || !k || !v || !out) return fail(SRT_ERR_INVALID, "attn_ring: NULL q, k, v or out");
+  if ((rope_flags & (SRT_ROTATE_Q | SRT_ROTATE_K)) && (!table_dev || table_npos < N))
+    return fail(SRT_ERR_INVALID, "attn_ring: rotation needs a table covering positions [0, %d)", N);
+  if (misaligned16(q) || misaligned16(k) || misaligned16(v) || misaligned16(out) || misaligned16(table_dev))
+    return fail(SRT_ERR_INVALID, "attn_ring: tensors must be 16-byte aligned");
+  const size_t need = srt::ring_workspace_bytes(a);
+  if (!workspace || workspace_bytes < need)
+    return fail(SRT_ERR_WORKSPACE, "attn_ring: workspace %zu bytes, need %zu", workspace_bytes, need);
+  if (((uintptr_t)workspace) & 255) return fail(SRT_ERR_INVALID, "attn_ring: workspace not 256-byte aligned");
+  a.q = q; a.k = k; a.v = v; a.table = table_dev; a.workspace = workspace; a.out = out; a.lse = lse;
+  a.device = device; a.window = window; a.sink = window > 0 ? sink : 0; a.sm_scale = sm_scale;
+  return hip_status(srt::ring_prefill(a, (hipStream_t)stream), "attn_ring_prefill launch");
 }
 
 }  // extern "C"

@@ -188,7 +188,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   {
     const int row = wrow0 + l32;
     const bool ok = row < a.Nq;
-    const long long qpos = a.q_pos0 + row;
+    const long long qpos = a.q_rope0 + (long long)row * a.rope_step;   // RoPE position
     if constexpr (HALF) {
       uint4 w[8];
 #pragma unroll
@@ -276,7 +276,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
         const uint4 kw = *reinterpret_cast<const uint4*>(kg + (long long)kc * kD + sc * 8);
         kbuf[i] = in ? kw : make_uint4(0, 0, 0, 0);
         if (ROT_K) {
-          const float4* t = tab4 + ((a.k_pos0 + kc) * (kD / 2) + sc * 4) / 2;
+          const float4* t = tab4 + ((a.k_rope0 + kc * a.rope_step) * (kD / 2) + sc * 4) / 2;
           tbuf[i][0] = t[0];
           tbuf[i][1] = t[1];
         }
@@ -291,7 +291,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
         const uint4 kw = *reinterpret_cast<const uint4*>(kg + (long long)kc * kD + (hc + 8 * i) * 8);
         kbuf[i] = in ? kw : make_uint4(0, 0, 0, 0);
       }
-      const float4* t = tab4 + ((a.k_pos0 + kc) * (kD / 2) + hc * 8) / 2;   // pairs 8hc .. 8hc+7
+      const float4* t = tab4 + ((a.k_rope0 + kc * a.rope_step) * (kD / 2) + hc * 8) / 2;   // pairs 8hc .. 8hc+7
 #pragma unroll
       for (int q = 0; q < 4; ++q) tbuf[q >> 1][q & 1] = t[q];
     }

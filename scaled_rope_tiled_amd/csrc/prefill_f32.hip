@@ -33,7 +33,8 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillArgs a) {
   const int hk = h / group;
   const int r = qtile * kRows + lane;
   const bool row_ok = r < a.Nq;
-  const long long qpos = a.q_pos0 + r;
+  const long long qpos = a.q_pos0 + r;                          // mask position
+  const long long qrope = a.q_rope0 + (long long)r * a.rope_step;  // RoPE position
 
   const float* qg = reinterpret_cast<const float*>(a.q) + ((long long)b * a.Hq + h) * a.q_hstride;
   const float* kg = reinterpret_cast<const float*>(a.k) + ((long long)b * a.Hkv + hk) * a.kv_hstride;
@@ -54,7 +55,7 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillArgs a) {
     if (half_pairs) {
 #pragma unroll
       for (int i = 0; i < D / 2; ++i) {
-        const float2 cs = tab[qpos * (D / 2) + i];
+        const float2 cs = tab[qrope * (D / 2) + i];
         const float x0 = q[i], x1 = q[i + D / 2];
         q[i] = x0 * cs.x - x1 * cs.y;
         q[i + D / 2] = x0 * cs.y + x1 * cs.x;
@@ -62,7 +63,7 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillArgs a) {
     } else {
 #pragma unroll
       for (int i = 0; i < D / 2; ++i) {
-        const float2 cs = tab[qpos * (D / 2) + i];
+        const float2 cs = tab[qrope * (D / 2) + i];
         const float x0 = q[2 * i], x1 = q[2 * i + 1];
         q[2 * i] = x0 * cs.x - x1 * cs.y;
         q[2 * i + 1] = x0 * cs.y + x1 * cs.x;
@@ -108,7 +109,7 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillArgs a) {
         const long long off = (long long)(c0 + c) * D;
         k0 = kg[off + i0]; k1 = kg[off + i1]; v0 = vg[off + i0]; v1 = vg[off + i1];
         if (a.rope_flags & 2) {
-          const float2 cs = tab[(a.k_pos0 + c0 + c) * (D / 2) + i];
+          const float2 cs = tab[(a.k_rope0 + (long long)(c0 + c) * a.rope_step) * (D / 2) + i];
           const float t0 = k0 * cs.x - k1 * cs.y, t1 = k0 * cs.y + k1 * cs.x;
           k0 = t0; k1 = t1;
         }

@@ -29,6 +29,15 @@ __global__ void __launch_bounds__(256) rope_table_kernel(Theta th, int half, dou
   }
 }
 
+// Position of row n of a group (see PosMap).
+__device__ inline long long row_pos(const PosMap& m, long long n) {
+  if (m.mode == kContiguous) return m.pos0 + n;
+  const long long j = n / m.C, t = n - j * m.C;
+  if (m.mode == kStriped) return m.pos0 + j + (long long)m.P * t;
+  const long long h = m.C / 2;
+  return m.pos0 + (t < h ? j * h + t : (2LL * m.P - 1 - j) * h + (t - h));
+}
+
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -43,7 +52,7 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
 // One thread = 8 consecutive elements of one row = 4 pairs.
 template <bool BF16>
 __global__ void __launch_bounds__(256) rope_apply_kernel(const void* __restrict__ x, void* y, long long groups,
-                                                         int N, int D, long long pos0,
+                                                         int N, int D, PosMap map,
                                                          const float4* __restrict__ table) {
   const int vec_per_row = D / 8;
   const long long total = groups * (long long)N * vec_per_row;
@@ -51,8 +60,7 @@ __global__ void __launch_bounds__(256) rope_apply_kernel(const void* __restrict_
        e += (long long)gridDim.x * blockDim.x) {
     const long long row = e / vec_per_row;
     const int j = (int)(e - row * vec_per_row);        // which 8-element chunk of the row
-    const long long n = row % N;
-    const long long p = pos0 + n;
+    const long long p = row_pos(map, row % N);
     // table row p, pairs 4j .. 4j+3 = two float4 of (cos, sin, cos, sin)
     const float4* trow = table + (p * (D / 2) + 4 * j) / 2;
     const float4 t0 = trow[0], t1 = trow[1];
@@ -117,7 +125,7 @@ __device__ inline void store8(void* base, long long idx8, bool bf16, const float
 // half and the same 8 of the second half.
 template <bool BF16>
 __global__ void __launch_bounds__(256) rope_apply_half_kernel(const void* __restrict__ x, void* y, long long groups,
-                                                              int N, int D, long long pos0,
+                                                              int N, int D, PosMap map,
                                                               const float4* __restrict__ table) {
   const int per_row = D / 16;
   const long long total = groups * (long long)N * per_row;
@@ -125,7 +133,7 @@ __global__ void __launch_bounds__(256) rope_apply_half_kernel(const void* __rest
        e += (long long)gridDim.x * blockDim.x) {
     const long long row = e / per_row;
     const int j = (int)(e - row * per_row);
-    const long long p = pos0 + row % N;
+    const long long p = row_pos(map, row % N);
     const float4* trow = table + (p * (D / 2) + 8 * j) / 2;      // pairs 8j .. 8j+7
     const long long i1 = row * (D / 8) + j, i2 = i1 + D / 16;     // 8-element chunks of the two halves
     float a[8], b[8], o1[8], o2[8];
@@ -162,25 +170,25 @@ hipError_t launch_rope_table(const Theta& th, int half, double mscale, long long
 }
 
 hipError_t launch_rope_apply(const void* x, void* y, bool bf16, bool half_pairs, long long groups, int N, int D,
-                             long long pos0, const float* table, hipStream_t stream) {
+                             const PosMap& map, const float* table, hipStream_t stream) {
   const float4* t = reinterpret_cast<const float4*>(table);
   if (half_pairs) {
     const long long work = groups * (long long)N * (D / 16);
     if (bf16)
       hipLaunchKernelGGL(rope_apply_half_kernel<true>, dim3(grid_for(work, 256)), dim3(256), 0, stream, x, y, groups,
-                         N, D, pos0, t);
+                         N, D, map, t);
     else
       hipLaunchKernelGGL(rope_apply_half_kernel<false>, dim3(grid_for(work, 256)), dim3(256), 0, stream, x, y,
-                         groups, N, D, pos0, t);
+                         groups, N, D, map, t);
     return hipGetLastError();
   }
   const long long work = groups * (long long)N * (D / 8);
   if (bf16)
     hipLaunchKernelGGL(rope_apply_kernel<true>, dim3(grid_for(work, 256)), dim3(256), 0, stream, x, y, groups, N,
-                       D, pos0, t);
+                       D, map, t);
   else
     hipLaunchKernelGGL(rope_apply_kernel<false>, dim3(grid_for(work, 256)), dim3(256), 0, stream, x, y, groups,
-                       N, D, pos0, t);
+                       N, D, map, t);
   return hipGetLastError();
 }
 

@@ -19,9 +19,19 @@ struct Theta {
 hipError_t launch_rope_table(const Theta& th, int half, double mscale, long long npos, float* table,
                              hipStream_t stream);
 
-// rows = B*H rows-groups of N rows each; row r of a group sits at position pos0 + r.
+// Position of row n (0 <= n < N) of a group: pos0 + n (kContiguous), or the
+// shard-major layouts of a ring over P devices with C = N / P rows per shard:
+// striped (shard n / C, row t = n % C sits at n / C + P t) and zigzag (rows
+// t < C/2 of shard j at j C/2 + t, the rest at (2P - 1 - j) C/2 + t - C/2).
+enum PosMode { kContiguous = 0, kStriped = 1, kZigzag = 2 };
+struct PosMap {
+  long long pos0;
+  int mode, P, C;
+};
+
+// rows = B*H rows-groups of N rows each; row n of a group sits at position map(n).
 hipError_t launch_rope_apply(const void* x, void* y, bool bf16, bool half_pairs, long long groups, int N, int D,
-                             long long pos0, const float* table, hipStream_t stream);
+                             const PosMap& map, const float* table, hipStream_t stream);
 
 // ---------------------------------------------------------------- prefill
 struct PrefillArgs {
@@ -32,7 +42,11 @@ struct PrefillArgs {
   float* lse;
   const float* table;   // [npos][D/2] float2 or nullptr
   long long q_hstride, kv_hstride, o_hstride, lse_hstride;  // elements
-  long long q_pos0, k_pos0;
+  long long q_pos0, k_pos0;   // mask positions of row 0 of q and of k
+  // RoPE positions: q row r turns by the table row q_rope0 + r * rope_step, k
+  // row c by k_rope0 + c * rope_step (equal to the mask positions with step 1
+  // except for strided ring shards, whose mask is stated in index space)
+  long long q_rope0, k_rope0, rope_step;
   int B, Hq, Hkv, Nq, Nk, D;
   int causal;
   int rope_flags;       // bit0: rotate q, bit1: rotate k, bit2: half-split pairs
@@ -79,5 +93,26 @@ struct DecodeArgs {
 
 size_t decode_workspace_bytes(int B, int Hq, int D, int splits);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- ring
+struct RingArgs {
+  const void* q;          // [B][Hq][N][D], shard-major rows
+  const void* k;          // [B][Hkv][N][D], shard-major rows
+  const void* v;
+  const float* table;     // or nullptr
+  void* workspace;        // ring_workspace_bytes(*this) bytes, 256-byte aligned
+  void* out;              // [B][Hq][N][D] in the input dtype, shard-major
+  float* lse;             // [B][Hq][N] or nullptr
+  int B, Hq, Hkv, N, D;
+  int P, mode;            // devices, PosMode of the shards
+  int device;             // -1: every device, else that device's share only
+  int window, sink;
+  int rope_flags;         // as PrefillArgs; K is rotated once into the workspace
+  bool bf16;
+  float sm_scale;
+};
+
+size_t ring_workspace_bytes(const RingArgs& a);
+hipError_t ring_prefill(const RingArgs& a, hipStream_t stream);
 
 }  // namespace srt

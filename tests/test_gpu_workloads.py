@@ -6,7 +6,6 @@ kernel tile edge near the sample points, both sides of every ring chunk edge,
 and seeded random rows.  Bar: max-abs <= 1e-4 (fp32) / 2e-2 (bf16) on O and lse."""
 import math
 import os
-import sys
 
 import numpy as np
 import pytest
@@ -78,25 +77,30 @@ def test_prefill_full_size(name):
     assert max_abs(f64(o2[:, :, -64:]), f64(o[:, :, -64:])) <= 1e-2
 
 
-def test_ring_128k_full_size():
-    """NTK 128K as 8 K/V chunks of 16384 merged by log-sum-exp (the benchmark's ring leg)."""
+@pytest.mark.parametrize("partition", ["contiguous", "zigzag"])
+def test_ring_128k_full_size(partition):
+    """NTK 128K as a ring of 8 devices (the benchmark's ring leg): contiguous
+    shards of 16384, and zig-zag shards (chunks r and 15 - r of 8192)."""
     srt = need_gpu()
-    sys.path.insert(0, ROOT)
-    from bench import ring_step
+    from oracle import ring as R
     w = synth.WORKLOADS["c4"]
     q, k, v = _inputs(w)
     table, _ = device_table(srt, w.rope, w.D, w.N)
-    C = w.N // w.chunks
-    out = torch.empty_like(q)
-    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device="cuda")
-    acc = torch.empty((w.B, w.Hq, C, w.D), dtype=torch.float32, device="cuda")
-    accl = torch.empty((w.B, w.Hq, C), dtype=torch.float32, device="cuda")
-    tmp, tmpl = torch.empty_like(acc), torch.empty_like(accl)
-    ring_step(srt, q, k, v, table, out, lse, acc, accl, tmp, tmpl, w.chunks)
+    pos = torch.from_numpy(R.partition_positions(w.N, w.chunks, partition)).cuda()
+    if partition == "contiguous":
+        o, l = srt.attn_ring_prefill(q, k, v, num_devices=w.chunks, partition=partition, table=table)
+    else:
+        qs, ks, vs = (t.index_select(2, pos).contiguous() for t in (q, k, v))
+        os_, ls_ = srt.attn_ring_prefill(qs, ks, vs, num_devices=w.chunks, partition=partition, table=table)
+        del qs, ks, vs
+        o, l = torch.empty_like(os_), torch.empty_like(ls_)
+        o.index_copy_(2, pos, os_)                 # back to natural order
+        l.index_copy_(2, pos, ls_)
     torch.cuda.synchronize()
-    ranges = _row_ranges(w.N, w.seed, chunk=C, n_random=8)
-    wo, wl = _check_rows(w, q, k, v, out, lse, ranges)
-    print(f"c4 ring: max|dO|={wo:.3g} max|dlse|={wl:.3g}", flush=True)
+    C = w.N // w.chunks
+    ranges = _row_ranges(w.N, w.seed, chunk=C // 2 if partition == "zigzag" else C, n_random=8)
+    wo, wl = _check_rows(w, q, k, v, o, l, ranges)
+    print(f"c4 ring {partition}: max|dO|={wo:.3g} max|dlse|={wl:.3g}", flush=True)
     assert wo <= TOL and wl <= TOL
 
 
