@@ -14,7 +14,7 @@ Sources (cited by title and section):
   * "8.3 长上下文技术" (LLM full-stack book, paper.xwysyy.cn): RoPE recap
     (§8.3.1), PI / NTK-aware and the over-extrapolated range (§8.3.2), the
     piecewise gamma(d) of NTK-by-parts and YaRN (§8.3.3), FlashAttention's
-    exactness (§8.3.4), Ring Attention and its Striped / Zig-Zag partitions
+    exactness and backward recomputation (§8.3.4), Ring Attention and its Striped / Zig-Zag partitions
     (§8.3.5).
   * "长上下文外推" notebook (doc.minddiy.top): worked 2-D rotation (§4.2),
     printed frequency table (§5.2), printed angles (§6.3), NTK table (§15.1).
@@ -28,9 +28,11 @@ Modules:
                          single-query decode.
   * ``oracle.ring``      Ring Attention over P simulated devices with
                          contiguous, Striped and Zig-Zag partitions.
+  * ``oracle.backward``  gradients dq, dk, dv (chain rule, rotated back by
+                         the opposite angle).
 
 Every function here is pinned by a ``-m "not gpu"`` test against values the
 pages print, closed forms, invariants or library routines (see
 ``tests/test_oracle_*.py``).  None is "parity unpinned".
 """
-from . import rope, attention, ring  # noqa: F401
+from . import rope, attention, ring, backward  # noqa: F401
