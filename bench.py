@@ -23,6 +23,8 @@ same line carries:
     ring and each device's share timed alone;
   * ``window``: the same prefill with a 4096-key sliding window and 4 sink
     tokens (flops of the kept pairs only), and its time against full causal;
+  * ``backward``: dq, dk, dv of the same prefill, TFLOP/s of the five
+    backward products;
   * ``cpu_baseline``: the fp64 oracle on the host cores, on a bounded sample.
 
 FLOPs count only (query, key) pairs the causal mask keeps, 4*D per pair per
@@ -205,6 +207,44 @@ def bench_window(srt, torch, w, window, sink, steps, warmup, full_kernel_ms):
             "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
             "work_vs_full_causal": round(pairs / causal_pairs(w.N, w.N), 4),
             "time_vs_full_causal": round(kernel_ms / full_kernel_ms, 4)}
+
+
+# ----------------------------------------------------------------------------- backward
+
+def bench_backward(srt, torch, w, steps, warmup):
+    """Gradients of the prefill workload (dq, dk, dv from out, lse and dO):
+    delta, dk/dv and dq launches.  Algorithmic flops: the five products of
+    the backward pass (S, dP, dV, dK, dQ), 10 D per kept pair per query head;
+    the kernels recompute S and dP in both the dk/dv and the dq kernel (14 D)."""
+    import synth
+    D = w.D
+    q = synth.randn((w.B, w.Hq, w.N, D), torch.bfloat16, w.seed, synth.Q_ID, "cuda")
+    k = synth.randn((w.B, w.Hkv, w.N, D), torch.bfloat16, w.seed, synth.K_ID, "cuda")
+    v = synth.randn((w.B, w.Hkv, w.N, D), torch.bfloat16, w.seed, synth.V_ID, "cuda")
+    do = synth.randn((w.B, w.Hq, w.N, D), torch.bfloat16, w.seed, synth.DO_ID, "cuda")
+    rp = w.rope
+    th, ms, _ = srt.rope_inv_freq(rp.method, rp.base, rp.s, rp.L, rp.alpha, rp.beta, D)
+    table = srt.rope_cos_sin(th, D, ms, w.N, "cuda")
+    out, lse = srt.attn_prefill(q, k, v, table=table)
+    dq = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    dk = torch.empty(k.shape, dtype=torch.float32, device="cuda")
+    dv = torch.empty(v.shape, dtype=torch.float32, device="cuda")
+    ws = torch.empty(w.B * w.Hq * w.N * 4, dtype=torch.uint8, device="cuda")
+    fn = lambda: srt.attn_backward(q, k, v, out, do, lse, table=table, workspace=ws, dq=dq, dk=dk, dv=dv)
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    kt = Timer(torch)
+    for _ in range(steps):
+        kt.run(fn)
+    torch.cuda.synchronize()
+    ms_ = kt.mean_ms()
+    flops = 2.5 * prefill_flops(w.B, w.Hq, w.N, w.N, D)
+    tf = flops / (ms_ * 1e-3) / 1e12
+    return {"workload": f"{w.name} backward (dq, dk, dv)", "unit": "TFLOP/s", "value": round(tf, 2),
+            "ms_per_step": round(ms_, 4), "alg_flops_per_step": flops,
+            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "note": "three launches (delta, dk/dv, dq) timed together with HIP events; 10 D flops per kept pair"}
 
 
 # ----------------------------------------------------------------------------- decode
@@ -428,6 +468,8 @@ def main():
         line["ring"] = bench_ring(srt, torch, synth.WORKLOADS["c4"], max(2, args.steps // 5), 1)
         torch.cuda.empty_cache()
         line["window"] = bench_window(srt, torch, w, 4096, 4, args.steps, args.warmup, p["kernel_ms"])
+        torch.cuda.empty_cache()
+        line["backward"] = bench_backward(srt, torch, w, max(3, args.steps // 4), 1)
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

@@ -245,6 +245,41 @@ int srt_attn_decode_splitk(const void* q, const void* k_cache, const void* v_cac
                            int pairing, int window, int sink, void* workspace, size_t workspace_bytes,
                            void* out, float* lse, void* stream);
 
+/*
+ * srt_attn_backward_workspace_size - bytes of workspace srt_attn_backward
+ * needs: delta = rowsum(dO * O), fp32 [B][Hq][Nq].
+ */
+int srt_attn_backward_workspace_size(int B, int Hq, int Nq, size_t* bytes_out_host);
+
+/*
+ * srt_attn_backward - gradients of srt_attn_prefill with respect to q, k, v.
+ *
+ * For upstream dO and the forward's out and lse, with P = exp(S - lse) the
+ * recomputed attention matrix ([BK] §8.3.4 (3): recompute from Q, K, V and
+ * the saved softmax statistics instead of storing P):
+ *   dv = P^T dO;  dS = P * (dO V^T - delta), delta = rowsum(dO * out);
+ *   dq~ = sm_scale dS k~;  dk~ = sm_scale dS^T q~;
+ * and, for inputs rotated on load (SRT_ROTATE_Q / SRT_ROTATE_K), the gradient
+ * turned back by the transposed rotation, the rotation by the opposite angle
+ * with the same table ([NB] §4: R^T = R(-a)), so dq, dk are gradients with
+ * respect to the raw q, k.  Without the flag the input is taken as given and
+ * so is its gradient.  GQA: dk, dv sum over the query heads of a group.
+ * The arguments mean what they mean for srt_attn_prefill (same mask: causal,
+ * window, sink; same table and flags); lse must be the forward's lse of
+ * exactly these inputs.
+ *
+ * q, out, dout: [B][Hq][Nq][D]; k, v: [B][Hkv][Nk][D]; all contiguous, dtype
+ * (BF16 with D = 128 on the matrix cores, F32 with D = 64).  lse: [B][Hq][Nq]
+ * fp32.  dq: [B][Hq][Nq][D], dk, dv: [B][Hkv][Nk][D], fp32 device buffers,
+ * overwritten.  workspace: >= srt_attn_backward_workspace_size bytes.
+ */
+int srt_attn_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                      const float* lse, int dtype, int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                      long long q_pos0, long long k_pos0, int causal, int window, int sink, float sm_scale,
+                      const float* table_dev, long long table_npos, int rope_flags,
+                      void* workspace, size_t workspace_bytes,
+                      float* dq, float* dk, float* dv, void* stream);
+
 /* partition argument of srt_attn_ring_prefill ([BK] §8.3.5, causal load balance) */
 #define SRT_PART_CONTIGUOUS 0   /* shard r = positions [r C, (r+1) C), C = N / P              */
 #define SRT_PART_STRIPED 1      /* shard r = positions r, r + P, r + 2P, ...                  */

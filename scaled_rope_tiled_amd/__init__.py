@@ -14,6 +14,7 @@ HIP stream; every step of the computation runs in the library's kernels.
     attn_merge_states(o_a, lse_a, o_b, lse_b, ...)    -> (out, lse)
     attn_decode_splitk(q, k_cache, v_cache, ...)      -> (out, lse)
     attn_ring_prefill(q, k, v, num_devices=, partition=, ...) -> (out, lse)
+    attn_backward(q, k, v, out, dout, lse, ...)      -> (dq, dk, dv) fp32
 """
 from __future__ import annotations
 
@@ -33,7 +34,8 @@ PARTITIONS = {"contiguous": 0, "striped": 1, "zigzag": 2}
 BAND_LOW, BAND_MID, BAND_HIGH = 0, 1, 2
 
 __all__ = ["rope_inv_freq", "rope_inv_freq_dynamic_ntk", "rope_inv_freq_factors", "rope_cos_sin", "rope_apply", "attn_prefill", "attn_merge_states",
-           "attn_decode_splitk", "attn_decode_workspace_size", "attn_ring_prefill", "attn_ring_workspace_size", "NONE", "PI", "NTK", "YARN",
+           "attn_decode_splitk", "attn_decode_workspace_size", "attn_ring_prefill", "attn_ring_workspace_size",
+           "attn_backward", "NONE", "PI", "NTK", "YARN",
            "ROTATE_Q", "ROTATE_K", "PAIR_HALF", "PAIRING_INTERLEAVED", "PAIRING_HALF", "lib"]
 
 
@@ -307,3 +309,43 @@ def attn_ring_prefill(q, k, v, *, num_devices: int, partition="contiguous", devi
                                            workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
                                            _stream(q.device)), "attn_ring_prefill")
     return out, lse
+
+
+def attn_backward(q, k, v, out, dout, lse, *, sm_scale: float | None = None, causal: bool = True,
+                  q_pos0: int = 0, k_pos0: int = 0, table: torch.Tensor | None = None,
+                  rope_flags: int | None = None, window: int = 0, sink: int = 0,
+                  workspace: torch.Tensor | None = None, dq=None, dk=None, dv=None):
+    """Gradients of attn_prefill for upstream dout, given its out and lse.
+
+    Same arguments as attn_prefill (rope_flags defaults to ROTATE_Q|ROTATE_K with
+    a table; dq, dk are then gradients with respect to the raw q, k).  All
+    tensors contiguous.  Returns (dq, dk, dv) in fp32."""
+    B, Hq, Nq, D = q.shape
+    _, Hkv, Nk, _ = k.shape
+    for t in (q, k, v, out, dout, lse):
+        if not t.is_contiguous():
+            raise ValueError("backward tensors must be contiguous")
+    if out.shape != q.shape or dout.shape != q.shape or tuple(lse.shape) != (B, Hq, Nq):
+        raise ValueError("out, dout must be [B, Hq, Nq, D] and lse [B, Hq, Nq]")
+    if lse.dtype != torch.float32:
+        raise ValueError("lse must be fp32")
+    if rope_flags is None:
+        rope_flags = (ROTATE_Q | ROTATE_K) if table is not None else 0
+    n = C.c_size_t()
+    _lib.check(lib().srt_attn_backward_workspace_size(B, Hq, Nq, C.byref(n)), "attn_backward_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=q.device)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device) if dv is None else dv
+    for t, ref in ((dq, q), (dk, k), (dv, v)):
+        if t.shape != ref.shape or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("gradient buffers must be contiguous fp32 of the input's shape")
+    sm = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
+    _lib.check(lib().srt_attn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _dt(q),
+                                       B, Hq, Hkv, Nq, Nk, D, int(q_pos0), int(k_pos0), int(bool(causal)),
+                                       int(window), int(sink), sm, _ptr(table),
+                                       0 if table is None else table.shape[0], int(rope_flags), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _ptr(dq), _ptr(dk), _ptr(dv),
+                                       _stream(q.device)), "attn_backward")
+    return dq, dk, dv

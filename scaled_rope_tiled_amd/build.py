@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libsrt.so")
 
-SOURCES = ["abi.cpp", "ring.cpp", "rope.hip", "merge.hip", "prefill_f32.hip", "prefill_bf16.hip", "decode.hip"]
+SOURCES = ["abi.cpp", "ring.cpp", "rope.hip", "merge.hip", "prefill_f32.hip", "prefill_bf16.hip", "decode.hip", "backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

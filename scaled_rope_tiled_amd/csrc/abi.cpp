@@ -298,6 +298,61 @@ int srt_attn_decode_splitk(const void* q, const void* k_cache, const void* v_cac
   return hip_status(srt::launch_decode(a, (hipStream_t)stream), "attn_decode_splitk launch");
 }
 
+int srt_attn_backward_workspace_size(int B, int Hq, int Nq, size_t* bytes_out) {
+  if (!bytes_out) return fail(SRT_ERR_INVALID, "attn_backward_workspace_size: NULL output");
+  if (B < 0 || Hq < 1 || Nq < 0) return fail(SRT_ERR_INVALID, "attn_backward_workspace_size: bad sizes");
+  *bytes_out = (size_t)B * Hq * Nq * sizeof(float);
+  return ok();
+}
+
+int srt_attn_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                      const float* lse, int dtype, int B, int Hq, int Hkv, int Nq, int Nk, int D, long long q_pos0,
+                      long long k_pos0, int causal, int window, int sink, float sm_scale, const float* table_dev,
+                      long long table_npos, int rope_flags, void* workspace, size_t workspace_bytes, float* dq,
+                      float* dk, float* dv, void* stream) {
+  if (!valid_dtype(dtype)) return fail(SRT_ERR_INVALID, "attn_backward: bad dtype");
+  if (B < 0 || Hq < 1 || Hkv < 1 || Nq < 0 || Nk < 0) return fail(SRT_ERR_INVALID, "attn_backward: bad sizes");
+  if (Hq % Hkv) return fail(SRT_ERR_INVALID, "attn_backward: Hq=%d not a multiple of Hkv=%d", Hq, Hkv);
+  if (rope_flags & ~(SRT_ROTATE_Q | SRT_ROTATE_K | SRT_PAIR_HALF))
+    return fail(SRT_ERR_INVALID, "attn_backward: bad rope_flags");
+  if (window < 0 || sink < 0) return fail(SRT_ERR_INVALID, "attn_backward: window and sink must be >= 0");
+  if (window > 0 && !causal) return fail(SRT_ERR_INVALID, "attn_backward: a sliding window needs causal = 1");
+  if (q_pos0 < 0 || k_pos0 < 0) return fail(SRT_ERR_INVALID, "attn_backward: negative position offset");
+  if (!std::isfinite(sm_scale)) return fail(SRT_ERR_INVALID, "attn_backward: sm_scale not finite");
+  if (dtype == SRT_BF16) {
+    if (D != 128) return fail(SRT_ERR_UNSUPPORTED, "attn_backward: bf16 kernels need D = 128 (got %d)", D);
+    const int g = Hq / Hkv;
+    if (!(g == 1 || g == 2 || g % 4 == 0))
+      return fail(SRT_ERR_UNSUPPORTED, "attn_backward: bf16 kernels need Hq/Hkv in {1, 2} or a multiple of 4");
+  } else if (D != 64) {
+    return fail(SRT_ERR_UNSUPPORTED, "attn_backward: fp32 kernels need D = 64 (got %d)", D);
+  }
+  if ((long long)B * (Nq + (long long)Nk) == 0) return ok();   // nothing to compute: pointers may be NULL
+  if (Nq > (1 << 30) || Nk > (1 << 30)) return fail(SRT_ERR_UNSUPPORTED, "attn_backward: N above 2^30");
+  if ((rope_flags & SRT_ROTATE_Q) && (!table_dev || q_pos0 + Nq > table_npos))
+    return fail(SRT_ERR_INVALID, "attn_backward: q positions [%lld, %lld) outside table [0, %lld)", q_pos0,
+                q_pos0 + Nq, table_npos);
+  if ((rope_flags & SRT_ROTATE_K) && (!table_dev || k_pos0 + Nk > table_npos))
+    return fail(SRT_ERR_INVALID, "attn_backward: k positions [%lld, %lld) outside table [0, %lld)", k_pos0,
+                k_pos0 + Nk, table_npos);
+  if ((Nq > 0 && (!q || !out || !dout || !lse || !dq)) || (Nk > 0 && (!k || !v || !dk || !dv)))
+    return fail(SRT_ERR_INVALID, "attn_backward: NULL pointer");
+  if (misaligned16(q) || misaligned16(k) || misaligned16(v) || misaligned16(out) || misaligned16(dout) ||
+      misaligned16(dq) || misaligned16(dk) || misaligned16(dv) || misaligned16(lse) || misaligned16(table_dev))
+    return fail(SRT_ERR_INVALID, "attn_backward: tensors must be 16-byte aligned");
+  const size_t need = (size_t)B * Hq * Nq * sizeof(float);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(SRT_ERR_WORKSPACE, "attn_backward: workspace %zu bytes, need %zu", workspace_bytes, need);
+  srt::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse; a.delta = (float*)workspace;
+  a.table = table_dev; a.dq = dq; a.dk = dk; a.dv = dv;
+  a.q_pos0 = q_pos0; a.k_pos0 = k_pos0;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.D = D;
+  a.causal = causal ? 1 : 0; a.window = window; a.sink = window > 0 ? sink : 0;
+  a.rope_flags = rope_flags; a.bf16 = dtype == SRT_BF16; a.sm_scale = sm_scale;
+  return hip_status(srt::launch_backward(a, (hipStream_t)stream), "attn_backward launch");
+}
+
 namespace {
 
 // Shared checks of the ring entry points; fills `a` on success.

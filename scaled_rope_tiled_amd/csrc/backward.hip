@@ -1,0 +1,784 @@
+// Backward pass of RoPE-scaled softmax attention (dq, dk, dv).
+//
+// The attention matrix is recomputed tile by tile from q, k, v and the lse the
+// forward pass saved, never stored ("8.3 长上下文技术" §8.3.4 (3)).  With
+// P = exp(S - lse), S = sm_scale q~ k~^T (q~, k~ rotated, mscale in the table):
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - delta),  delta = rowsum(dO * O),
+//   dq~ = sm_scale dS k~,  dk~ = sm_scale dS^T q~,
+// and the gradient of a rotated input is turned back by the transposed
+// rotation (the rotation by the opposite angle): dq = R^T dq~ with the same
+// (mscale cos, mscale sin) table entries.
+//
+// Three launches: delta (HBM-bound), dk/dv (a workgroup owns a block of keys
+// of one KV head and walks the query tiles of every query head of its GQA
+// group that can see them) and dq (a workgroup owns query rows, like the
+// forward kernel, and walks the visible key tiles).  bf16 kernels (D = 128)
+// use v_mfma_f32_32x32x16_bf16 for all five products; fp32 kernels (D = 64)
+// keep every product in fp32 on the vector ALUs.  Gradients are written in
+// fp32.
+#include "mfma_common.h"
+
+namespace srt {
+namespace {
+
+using namespace mc;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ inline void load8f(const void* base, long long idx8, bool bf16, float v[8]) {
+  if (bf16) {
+    const uint4 w = reinterpret_cast<const uint4*>(base)[idx8];
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[2 * i] = bf_lo(ww[i]); v[2 * i + 1] = bf_hi(ww[i]); }
+  } else {
+    const float4 x = reinterpret_cast<const float4*>(base)[2 * idx8];
+    const float4 y = reinterpret_cast<const float4*>(base)[2 * idx8 + 1];
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w; v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+  }
+}
+
+// ------------------------------------------------------------------ delta
+// delta[row] = sum_d dO[row][d] O[row][d] in fp32; D/8 lanes per row.
+template <bool BF16>
+__global__ void __launch_bounds__(256) bwd_delta_kernel(const void* __restrict__ o, const void* __restrict__ dout,
+                                                        float* __restrict__ delta, long long rows, int D) {
+  const int per_row = D / 8;                    // 8 or 16: divides the wave
+  const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long row = e / per_row;
+  float acc = 0.f;
+  if (row < rows) {
+    float x[8], y[8];
+    load8f(o, e, BF16, x);
+    load8f(dout, e, BF16, y);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = fmaf(x[i], y[i], acc);
+  }
+  for (int m = per_row / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, per_row);
+  if (row < rows && (e % per_row) == 0) delta[row] = acc;
+}
+
+// Visibility of key position kp to query position qp (causal, window, sinks).
+__device__ inline bool visible(const BwdArgs& a, long long qp, long long kp) {
+  if (!a.causal) return true;
+  if (kp > qp) return false;
+  return a.window <= 0 || qp - kp < a.window || kp < a.sink;
+}
+
+// Turn a gradient pair back: (g0, g1) -> R^T (g0, g1) with (c, s) = mscale (cos, sin).
+__device__ inline void rotate_back(float& g0, float& g1, float2 cs) {
+  const float y0 = cs.x * g0 + cs.y * g1, y1 = -cs.y * g0 + cs.x * g1;
+  g0 = y0;
+  g1 = y1;
+}
+
+// ------------------------------------------------------------------ fp32 (D = 64)
+template <int D>
+__global__ void __launch_bounds__(64) bwd_dq_f32_kernel(BwdArgs a) {
+  __shared__ float ks[32][D + 1];
+  __shared__ float vs[32][D + 1];
+  const int lane = threadIdx.x, qtile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int hk = h / (a.Hq / a.Hkv);
+  const int r = qtile * 64 + lane;
+  const bool row_ok = r < a.Nq;
+  const long long qpos = a.q_pos0 + r;
+  const bool half = (a.rope_flags & 4) != 0;
+  const long long qrow = ((long long)b * a.Hq + h) * a.Nq + r;
+  const float* qg = reinterpret_cast<const float*>(a.q);
+  const float* dog = reinterpret_cast<const float*>(a.dout);
+  const float* kg = reinterpret_cast<const float*>(a.k) + ((long long)b * a.Hkv + hk) * a.Nk * D;
+  const float* vg = reinterpret_cast<const float*>(a.v) + ((long long)b * a.Hkv + hk) * a.Nk * D;
+  const float2* tab = reinterpret_cast<const float2*>(a.table);
+
+  float q[D], dov[D], dq[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    q[d] = row_ok ? qg[qrow * D + d] : 0.f;
+    dov[d] = row_ok ? dog[qrow * D + d] : 0.f;
+    dq[d] = 0.f;
+  }
+  if ((a.rope_flags & 1) && row_ok) {
+#pragma unroll
+    for (int i = 0; i < D / 2; ++i) {
+      const int i0 = half ? i : 2 * i, i1 = half ? i + D / 2 : 2 * i + 1;
+      const float2 cs = tab[qpos * (D / 2) + i];
+      const float x0 = q[i0], x1 = q[i1];
+      q[i0] = x0 * cs.x - x1 * cs.y;
+      q[i1] = x0 * cs.y + x1 * cs.x;
+    }
+  }
+  const float c2 = a.sm_scale * kLog2e;
+  const float lse2 = row_ok ? a.lse[qrow] * kLog2e : 0.f;
+  const float dl = row_ok ? a.delta[qrow] : 0.f;
+
+  int kend = a.Nk;
+  if (a.causal) {
+    const long long last_q = a.q_pos0 + min(a.Nq, (qtile + 1) * 64) - 1;
+    kend = (int)max(0LL, min((long long)a.Nk, last_q - a.k_pos0 + 1));
+  }
+  int kbeg = 0;
+  if (a.causal && a.window > 0 && a.sink <= a.k_pos0) {   // no sink in this K: skip keys before every window
+    const long long lo = a.q_pos0 + (long long)qtile * 64 - a.window + 1 - a.k_pos0;
+    kbeg = (int)max(0LL, min((long long)kend, lo)) / 32 * 32;
+  }
+  for (int c0 = kbeg; c0 < kend; c0 += 32) {
+    __syncthreads();
+    for (int e = lane; e < 32 * (D / 2); e += 64) {
+      const int c = e / (D / 2), i = e % (D / 2);
+      const int i0 = half ? i : 2 * i, i1 = half ? i + D / 2 : 2 * i + 1;
+      float k0 = 0.f, k1 = 0.f, v0 = 0.f, v1 = 0.f;
+      if (c0 + c < a.Nk) {
+        const long long off = (long long)(c0 + c) * D;
+        k0 = kg[off + i0]; k1 = kg[off + i1]; v0 = vg[off + i0]; v1 = vg[off + i1];
+        if (a.rope_flags & 2) {
+          const float2 cs = tab[(a.k_pos0 + c0 + c) * (D / 2) + i];
+          const float t0 = k0 * cs.x - k1 * cs.y, t1 = k0 * cs.y + k1 * cs.x;
+          k0 = t0; k1 = t1;
+        }
+      }
+      ks[c][i0] = k0; ks[c][i1] = k1;
+      vs[c][i0] = v0; vs[c][i1] = v1;
+    }
+    __syncthreads();
+    for (int c = 0; c < 32; ++c) {
+      const bool vis = row_ok && c0 + c < kend && visible(a, qpos, a.k_pos0 + c0 + c);
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) { s = fmaf(q[d], ks[c][d], s); dp = fmaf(dov[d], vs[c][d], dp); }
+      const float p = vis ? exp2f(s * c2 - lse2) : 0.f;
+      const float ds = p * (dp - dl);
+#pragma unroll
+      for (int d = 0; d < D; ++d) dq[d] = fmaf(ds, ks[c][d], dq[d]);
+    }
+  }
+  if (!row_ok) return;
+#pragma unroll
+  for (int d = 0; d < D; ++d) dq[d] *= a.sm_scale;
+  if (a.rope_flags & 1) {
+#pragma unroll
+    for (int i = 0; i < D / 2; ++i) {
+      const int i0 = half ? i : 2 * i, i1 = half ? i + D / 2 : 2 * i + 1;
+      rotate_back(dq[i0], dq[i1], tab[qpos * (D / 2) + i]);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < D; ++d) a.dq[qrow * D + d] = dq[d];
+}
+
+template <int D>
+__global__ void __launch_bounds__(64) bwd_dkdv_f32_kernel(BwdArgs a) {
+  __shared__ float qs[32][D + 1];
+  __shared__ float dos[32][D + 1];
+  __shared__ float l2s[32], dls[32];
+  const int lane = threadIdx.x, ktile = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  const int G = a.Hq / a.Hkv;
+  const int c = ktile * 64 + lane;
+  const bool key_ok = c < a.Nk;
+  const long long kpos = a.k_pos0 + c;
+  const bool half = (a.rope_flags & 4) != 0;
+  const long long krow = ((long long)b * a.Hkv + hk) * a.Nk + c;
+  const float2* tab = reinterpret_cast<const float2*>(a.table);
+
+  float kk[D], vv[D], dk[D], dv[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    kk[d] = key_ok ? reinterpret_cast<const float*>(a.k)[krow * D + d] : 0.f;
+    vv[d] = key_ok ? reinterpret_cast<const float*>(a.v)[krow * D + d] : 0.f;
+    dk[d] = 0.f;
+    dv[d] = 0.f;
+  }
+  if ((a.rope_flags & 2) && key_ok) {
+#pragma unroll
+    for (int i = 0; i < D / 2; ++i) {
+      const int i0 = half ? i : 2 * i, i1 = half ? i + D / 2 : 2 * i + 1;
+      const float2 cs = tab[kpos * (D / 2) + i];
+      const float x0 = kk[i0], x1 = kk[i1];
+      kk[i0] = x0 * cs.x - x1 * cs.y;
+      kk[i1] = x0 * cs.y + x1 * cs.x;
+    }
+  }
+  const float c2 = a.sm_scale * kLog2e;
+  // query rows that can see some key of this block
+  const long long kp_first = a.k_pos0 + (long long)ktile * 64;
+  const long long kp_last = a.k_pos0 + min(a.Nk, (ktile + 1) * 64) - 1;
+  long long r_lo = 0, r_hi = a.Nq;
+  if (a.causal) r_lo = max(0LL, min((long long)a.Nq, kp_first - a.q_pos0));
+  if (a.causal && a.window > 0 && kp_first >= a.sink) r_hi = max(0LL, min((long long)a.Nq, kp_last + a.window - a.q_pos0));
+  for (int g = 0; g < G; ++g) {
+    const int h = hk * G + g;
+    const long long hbase = ((long long)b * a.Hq + h) * a.Nq;
+    for (long long rt = r_lo / 32 * 32; rt < r_hi; rt += 32) {
+      __syncthreads();
+      for (int e = lane; e < 32 * (D / 2); e += 64) {
+        const int rr = e / (D / 2), i = e % (D / 2);
+        const int i0 = half ? i : 2 * i, i1 = half ? i + D / 2 : 2 * i + 1;
+        const long long r = rt + rr;
+        float q0 = 0.f, q1 = 0.f, o0 = 0.f, o1 = 0.f;
+        if (r < a.Nq) {
+          const long long off = (hbase + r) * D;
+          q0 = reinterpret_cast<const float*>(a.q)[off + i0];
+          q1 = reinterpret_cast<const float*>(a.q)[off + i1];
+          o0 = reinterpret_cast<const float*>(a.dout)[off + i0];
+          o1 = reinterpret_cast<const float*>(a.dout)[off + i1];
+          if (a.rope_flags & 1) {
+            const float2 cs = tab[(a.q_pos0 + r) * (D / 2) + i];
+            const float t0 = q0 * cs.x - q1 * cs.y, t1 = q0 * cs.y + q1 * cs.x;
+            q0 = t0; q1 = t1;
+          }
+        }
+        qs[rr][i0] = q0; qs[rr][i1] = q1;
+        dos[rr][i0] = o0; dos[rr][i1] = o1;
+      }
+      if (lane < 32) {
+        const long long r = rt + lane;
+        l2s[lane] = r < a.Nq ? a.lse[hbase + r] * kLog2e : 0.f;
+        dls[lane] = r < a.Nq ? a.delta[hbase + r] : 0.f;
+      }
+      __syncthreads();
+      for (int rr = 0; rr < 32; ++rr) {
+        const long long r = rt + rr;
+        const bool vis = key_ok && r < a.Nq && visible(a, a.q_pos0 + r, kpos);
+        float s = 0.f, dp = 0.f;
+#pragma unroll
+        for (int d = 0; d < D; ++d) { s = fmaf(kk[d], qs[rr][d], s); dp = fmaf(vv[d], dos[rr][d], dp); }
+        const float p = vis ? exp2f(s * c2 - l2s[rr]) : 0.f;
+        const float ds = p * (dp - dls[rr]);
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+          dv[d] = fmaf(p, dos[rr][d], dv[d]);
+          dk[d] = fmaf(ds, qs[rr][d], dk[d]);
+        }
+      }
+    }
+  }
+  if (!key_ok) return;
+#pragma unroll
+  for (int d = 0; d < D; ++d) dk[d] *= a.sm_scale;
+  if (a.rope_flags & 2) {
+#pragma unroll
+    for (int i = 0; i < D / 2; ++i) {
+      const int i0 = half ? i : 2 * i, i1 = half ? i + D / 2 : 2 * i + 1;
+      rotate_back(dk[i0], dk[i1], tab[kpos * (D / 2) + i]);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    a.dk[krow * D + d] = dk[d];
+    a.dv[krow * D + d] = dv[d];
+  }
+}
+
+// ------------------------------------------------------------------ bf16 (D = 128), matrix cores
+//
+// Tile layouts follow v_mfma_f32_32x32x16_bf16 (wave64): A operand lane l =
+// row l % 32, k = (l / 32) * 8 + 0..7; B operand lane l = column l % 32, same
+// k; accumulator lane l = column l % 32, rows (j / 4) * 8 + (l / 32) * 4 + j % 4.
+// A product whose B operand comes straight from an accumulator (P, dS) takes
+// its k elements in the accumulator's row order; the A operand is then read
+// with the transposing LDS read in that same order, as the forward kernel does
+// for O^T = V^T P^T.
+
+constexpr int kD = 128;
+constexpr int kTStr = kD + 24;    // 304 B: conflict-free 16-byte row reads and transposing reads
+constexpr int kRStr = kD + 8;     // 272 B: rows read only as 16-byte row chunks
+
+// Load 8 d-chunks of one row (d = ks * 16 + hl * 8 + 0..7) and rotate them
+// (interleaved pairs in-chunk; half-split pairs chunk ks with ks + 4).
+template <bool HALF>
+__device__ inline void load_row_rotated(const __hip_bfloat16* row, bool ok, bool rotate, const float4* tab4,
+                                        long long pos, int hl, bf16x8 (&out)[8]) {
+  uint4 w[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+    w[ks] = ok ? *reinterpret_cast<const uint4*>(row + ks * 16 + hl * 8) : make_uint4(0, 0, 0, 0);
+  if (ok && rotate) {
+    if (HALF) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int d0 = ks * 16 + hl * 8;
+        const float4* t = tab4 + (pos * (kD / 2) + d0) / 2;
+        const float4 tt[4] = {t[0], t[1], t[2], t[3]};
+        rotate_chunk_pair(w[ks], w[ks + 4], tt);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const float4* t = tab4 + (pos * (kD / 2) + (ks * 16 + hl * 8) / 2) / 2;
+        w[ks] = rotate_chunk(w[ks], t[0], t[1]);
+      }
+    }
+  }
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) out[ks] = as_bf16x8(w[ks]);
+}
+
+// Staging of one 32-row tile: thread t moves chunks (t & 7) and (t & 7) + 8
+// of row t >> 3 of two tensors, the first rotated when asked.
+struct Stage {
+  uint4 x[2], y[2];
+  float4 t[4];
+};
+
+template <bool HALF>
+__device__ inline void stage_load(Stage& st, const __hip_bfloat16* xg, const __hip_bfloat16* yg, long long row,
+                                  bool ok, bool rotate, const float4* tab4, long long pos, int sc) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    st.x[i] = ok ? *reinterpret_cast<const uint4*>(xg + row * kD + (sc + 8 * i) * 8) : make_uint4(0, 0, 0, 0);
+    st.y[i] = ok ? *reinterpret_cast<const uint4*>(yg + row * kD + (sc + 8 * i) * 8) : make_uint4(0, 0, 0, 0);
+  }
+  if (ok && rotate) {
+    if (HALF) {
+      const float4* t = tab4 + (pos * (kD / 2) + sc * 8) / 2;     // pairs 8 sc .. 8 sc + 7
+#pragma unroll
+      for (int q = 0; q < 4; ++q) st.t[q] = t[q];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float4* t = tab4 + (pos * (kD / 2) + (sc + 8 * i) * 4) / 2;   // pairs 4 chunk .. 4 chunk + 3
+        st.t[2 * i] = t[0];
+        st.t[2 * i + 1] = t[1];
+      }
+    }
+  }
+}
+
+template <bool HALF>
+__device__ inline void stage_store(Stage& st, __hip_bfloat16* xs, int xstr, __hip_bfloat16* ys, int ystr, int sr,
+                                   int sc, bool rotate) {
+  uint4 x0 = st.x[0], x1 = st.x[1];
+  if (rotate) {
+    if (HALF) {
+      rotate_chunk_pair(x0, x1, st.t);
+    } else {
+      x0 = rotate_chunk(x0, st.t[0], st.t[1]);
+      x1 = rotate_chunk(x1, st.t[2], st.t[3]);
+    }
+  }
+  *reinterpret_cast<uint4*>(xs + sr * xstr + sc * 8) = x0;
+  *reinterpret_cast<uint4*>(xs + sr * xstr + (sc + 8) * 8) = x1;
+  *reinterpret_cast<uint4*>(ys + sr * ystr + sc * 8) = st.y[0];
+  *reinterpret_cast<uint4*>(ys + sr * ystr + (sc + 8) * 8) = st.y[1];
+}
+
+// acc[db] += X^T[d][rows] B[rows][cols] over a 32-row tile X held row-major in
+// LDS (stride kTStr), B given as two 16-row k-steps in accumulator row order.
+__device__ inline void mma_tr(f32x16 (&acc)[4], uint32_t x_lane, const bf16x8 (&bk)[2]) {
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const i16x4 lo = lds_read_tr(x_lane + ((half * 16) * kTStr + db * 32) * 2);
+      const i16x4 hi = lds_read_tr(x_lane + ((half * 16 + 8) * kTStr + db * 32) * 2);
+      const bf16x8 xa = __builtin_bit_cast(
+          bf16x8, (__attribute__((__vector_size__(8 * sizeof(short)))) short){lo[0], lo[1], lo[2], lo[3], hi[0],
+                                                                             hi[1], hi[2], hi[3]});
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, bk[half], acc[db], 0, 0, 0);
+    }
+  }
+}
+
+// acc = X[rows][d] R[d][cols] with X a 32-row tile in LDS (16-byte row reads) and R in registers.
+__device__ inline f32x16 mma_rows(uint32_t x_lane, const bf16x8 (&r)[8]) {
+  f32x16 acc;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read16(x_lane + ks * 32), r[ks], acc, 0, 0, 0);
+  return acc;
+}
+
+__device__ inline void pack16(const float (&x)[16], bf16x8 (&out)[2]) {
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = pack2(x[half * 8 + 2 * i], x[half * 8 + 2 * i + 1]);
+    out[half] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+  }
+}
+
+// Write a transposed accumulator (lane = one row of the result, d across
+// (j / 4) * 8 + hl * 4 + j % 4 of each 32-wide d block) as fp32, scaled and,
+// when asked, rotated back at position pos.
+template <bool HALF>
+__device__ inline void store_grad(float* dst, f32x16 (&acc)[4], float scale, bool rotate, const float2* tab,
+                                  long long pos, int hl) {
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[db][j] *= scale;
+  if (rotate) {
+    if (HALF) {
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int d = db * 32 + (j >> 2) * 8 + hl * 4 + (j & 3);      // pairs (d, d + 64)
+          float g0 = acc[db][j], g1 = acc[db + 2][j];
+          rotate_back(g0, g1, tab[pos * (kD / 2) + d]);
+          acc[db][j] = g0;
+          acc[db + 2][j] = g1;
+        }
+    } else {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) {
+          const int d = db * 32 + (j >> 2) * 8 + hl * 4 + (j & 3);      // pairs (d, d + 1), d even
+          float g0 = acc[db][j], g1 = acc[db][j + 1];
+          rotate_back(g0, g1, tab[pos * (kD / 2) + d / 2]);
+          acc[db][j] = g0;
+          acc[db][j + 1] = g1;
+        }
+    }
+  }
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4)
+      *reinterpret_cast<float4*>(dst + db * 32 + g4 * 8 + hl * 4) =
+          make_float4(acc[db][g4 * 4], acc[db][g4 * 4 + 1], acc[db][g4 * 4 + 2], acc[db][g4 * 4 + 3]);
+}
+
+// ---- dk / dv: a workgroup of 4 waves owns 128 keys of one KV head; wave w
+// its 32 keys (rotated k~ and v in registers, the B operands of S = q~ k~^T and
+// dP = dO V^T).  Query tiles of 32 rows (q~ rotated on load, dO, lse, delta)
+// are staged in LDS, double-buffered, for every query head of the group.
+constexpr int kKVWaves = 4;
+constexpr int kKVThreads = 64 * kKVWaves;
+constexpr int kKVKeys = 32 * kKVWaves;
+
+struct DkdvSmem {
+  __hip_bfloat16 q[2][32 * kTStr];
+  __hip_bfloat16 o[2][32 * kTStr];
+  float l2[2][32];
+  float dl[2][32];
+};
+
+template <bool HALF>
+__global__ void __launch_bounds__(kKVThreads) bwd_dkdv_bf16_kernel(BwdArgs a) {
+  __shared__ DkdvSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int hk = blockIdx.x, kblk = blockIdx.y, b = blockIdx.z;
+  const int G = a.Hq / a.Hkv;
+  const int wk0 = kblk * kKVKeys + wave * 32;
+  const int key = wk0 + l32;
+  const bool key_ok = key < a.Nk;
+  const long long kpos = a.k_pos0 + key;
+  const float4* tab4 = reinterpret_cast<const float4*>(a.table);
+  const float2* tab2 = reinterpret_cast<const float2*>(a.table);
+  const __hip_bfloat16* kg = reinterpret_cast<const __hip_bfloat16*>(a.k) + ((long long)b * a.Hkv + hk) * a.Nk * kD;
+  const __hip_bfloat16* vg = reinterpret_cast<const __hip_bfloat16*>(a.v) + ((long long)b * a.Hkv + hk) * a.Nk * kD;
+
+  bf16x8 kreg[8], vreg[8];
+  load_row_rotated<HALF>(kg + (long long)key * kD, key_ok, (a.rope_flags & 2) != 0, tab4, kpos, hl, kreg);
+  load_row_rotated<HALF>(vg + (long long)key * kD, key_ok, false, tab4, 0, hl, vreg);
+
+  f32x16 dvacc[4], dkacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) { dvacc[db][j] = 0.f; dkacc[db][j] = 0.f; }
+  const float c2 = a.sm_scale * kLog2e;
+
+  // query rows [r_lo, r_hi) that can see some key of this workgroup
+  const int wg_k0 = kblk * kKVKeys;
+  const long long kp_first = a.k_pos0 + wg_k0;
+  const long long kp_last = a.k_pos0 + min(a.Nk, wg_k0 + kKVKeys) - 1;
+  long long r_lo = 0, r_hi = a.Nq;
+  if (a.causal) r_lo = max(0LL, min((long long)a.Nq, kp_first - a.q_pos0));
+  if (a.causal && a.window > 0 && kp_first >= a.sink)
+    r_hi = max(0LL, min((long long)a.Nq, kp_last + a.window - a.q_pos0));
+  const int t0 = (int)(r_lo / 32);
+  const int ntq = r_hi > r_lo ? (int)((r_hi + 31) / 32) - t0 : 0;
+  const int nit = G * ntq;
+
+  // the wave's keys: all visible to a tile's rows iff the tile lies inside the
+  // causal triangle, inside every window (or the keys are all sinks) and in Nq
+  const long long kw_first = a.k_pos0 + wk0, kw_last = kw_first + 31;
+  const bool is_sink = kpos < a.sink;
+
+  const int sr = tid >> 3, sc = tid & 7;
+  Stage st;
+  float l2v = 0.f, dlv = 0.f;
+  auto issue = [&](int it) {
+    const int g = it / ntq, t = t0 + it % ntq;
+    const int h = hk * G + g;
+    const long long hrow = ((long long)b * a.Hq + h) * a.Nq;
+    const long long r = (long long)t * 32 + sr;
+    const bool ok = r < a.Nq;
+    stage_load<HALF>(st, reinterpret_cast<const __hip_bfloat16*>(a.q) + hrow * kD,
+                     reinterpret_cast<const __hip_bfloat16*>(a.dout) + hrow * kD, r, ok, (a.rope_flags & 1) != 0,
+                     tab4, a.q_pos0 + r, sc);
+    if (tid < 32) {
+      const long long rr = (long long)t * 32 + tid;
+      l2v = rr < a.Nq ? a.lse[hrow + rr] * kLog2e : 0.f;
+      dlv = rr < a.Nq ? a.delta[hrow + rr] : 0.f;
+    }
+  };
+  auto store = [&](int buf) {
+    stage_store<HALF>(st, sm.q[buf], kTStr, sm.o[buf], kTStr, sr, sc, (a.rope_flags & 1) != 0);
+    if (tid < 32) {
+      sm.l2[buf][tid] = l2v;
+      sm.dl[buf][tid] = dlv;
+    }
+  };
+
+  const int gj = lane & 15;
+  const int gd = ((lane >> 4) & 1) * 16 + 4 * (gj & 3);
+  if (nit > 0) {
+    issue(0);
+    store(0);
+    __syncthreads();
+  }
+  for (int it = 0; it < nit; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < nit) issue(it + 1);
+    const int t = t0 + it % ntq;
+    const int qt0 = t * 32;
+    // S = q~ k~^T and dP = dO V^T: lane = key, rows = 16 of the tile's queries
+    const f32x16 s = mma_rows(lds_off(&sm.q[buf][l32 * kTStr + hl * 8]), kreg);
+    const f32x16 dp = mma_rows(lds_off(&sm.o[buf][l32 * kTStr + hl * 8]), vreg);
+    float p[16], ds[16];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const float4 L = *reinterpret_cast<const float4*>(&sm.l2[buf][g4 * 8 + hl * 4]);
+      const float4 Dl = *reinterpret_cast<const float4*>(&sm.dl[buf][g4 * 8 + hl * 4]);
+      const float Lj[4] = {L.x, L.y, L.z, L.w}, Dj[4] = {Dl.x, Dl.y, Dl.z, Dl.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = g4 * 4 + e;
+        p[j] = __builtin_amdgcn_exp2f(fmaf(s[j], c2, -Lj[e]));
+        ds[j] = dp[j] - Dj[e];
+      }
+    }
+    const long long qp0 = a.q_pos0 + qt0;
+    const bool masked = (qt0 + 32 > a.Nq) || (a.causal && kw_last > qp0) ||
+                        (a.causal && a.window > 0 && kw_last >= a.sink && qp0 + 31 - kw_first >= a.window);
+    if (masked) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int row = (j >> 2) * 8 + hl * 4 + (j & 3);
+        const long long rel = qp0 + row - kpos;
+        const bool vis = (qt0 + row < a.Nq) &&
+                         (!a.causal || (rel >= 0 && (a.window <= 0 || rel < a.window || is_sink)));
+        p[j] = vis ? p[j] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) ds[j] *= p[j];
+    bf16x8 pb[2], dsb[2];
+    pack16(p, pb);
+    pack16(ds, dsb);
+    // dV^T += dO^T P and dK~^T += q~^T dS (transposing reads of the row-major tiles)
+    mma_tr(dvacc, lds_off(&sm.o[buf][(hl * 4 + (gj >> 2)) * kTStr + gd]), pb);
+    mma_tr(dkacc, lds_off(&sm.q[buf][(hl * 4 + (gj >> 2)) * kTStr + gd]), dsb);
+    if (it + 1 < nit) store(buf ^ 1);
+    __syncthreads();
+  }
+  if (!key_ok) return;
+  const long long krow = ((long long)b * a.Hkv + hk) * a.Nk + key;
+  store_grad<HALF>(a.dv + krow * kD, dvacc, 1.f, false, tab2, kpos, hl);
+  store_grad<HALF>(a.dk + krow * kD, dkacc, a.sm_scale, (a.rope_flags & 2) != 0, tab2, kpos, hl);
+}
+
+// ---- dq: a workgroup of 4 waves owns one KV head and 32 * (4 / HPW) query
+// rows of HPW = min(G, 4) query heads (as the forward kernel); wave w holds
+// rotated q and dO of its 32 rows in registers and walks 32-key tiles of
+// rotated k and v staged in LDS.
+constexpr int kQWaves = 4;
+constexpr int kQThreads = 64 * kQWaves;
+
+struct DqSmem {
+  __hip_bfloat16 k[2][32 * kTStr];
+  __hip_bfloat16 v[2][32 * kRStr];
+};
+
+template <bool HALF>
+__global__ void __launch_bounds__(kQThreads) bwd_dq_bf16_kernel(BwdArgs a) {
+  __shared__ DqSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int G = a.Hq / a.Hkv;
+  const int HPW = G < 4 ? G : 4;
+  const int RB = kQWaves / HPW;
+  const int quads = G > 4 ? G / 4 : 1;
+  const int hk = blockIdx.x / quads, quad = blockIdx.x - hk * quads;
+  const int b = blockIdx.z;
+  const int qt = a.causal ? ((int)gridDim.y - 1 - (int)blockIdx.y) : (int)blockIdx.y;
+  const int hq = hk * G + quad * 4 + (wave % HPW);
+  const int wrow0 = qt * (32 * RB) + (wave / HPW) * 32;
+  const int wg_row_last = min(a.Nq, (qt + 1) * 32 * RB) - 1;
+  const int row = wrow0 + l32;
+  const bool row_ok = row < a.Nq;
+  const long long qpos = a.q_pos0 + row;
+  const float4* tab4 = reinterpret_cast<const float4*>(a.table);
+  const float2* tab2 = reinterpret_cast<const float2*>(a.table);
+  const long long qrow = ((long long)b * a.Hq + hq) * a.Nq + row;
+  const __hip_bfloat16* kg = reinterpret_cast<const __hip_bfloat16*>(a.k) + ((long long)b * a.Hkv + hk) * a.Nk * kD;
+  const __hip_bfloat16* vg = reinterpret_cast<const __hip_bfloat16*>(a.v) + ((long long)b * a.Hkv + hk) * a.Nk * kD;
+
+  bf16x8 qreg[8], doreg[8];
+  load_row_rotated<HALF>(reinterpret_cast<const __hip_bfloat16*>(a.q) + qrow * kD, row_ok, (a.rope_flags & 1) != 0,
+                         tab4, qpos, hl, qreg);
+  load_row_rotated<HALF>(reinterpret_cast<const __hip_bfloat16*>(a.dout) + qrow * kD, row_ok, false, tab4, 0, hl,
+                         doreg);
+  const float c2 = a.sm_scale * kLog2e;
+  const float lse2 = row_ok ? a.lse[qrow] * kLog2e : 0.f;
+  const float dl = row_ok ? a.delta[qrow] : 0.f;
+  f32x16 dqacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) dqacc[db][j] = 0.f;
+
+  // key tiles of 32: [0, sink tiles) then from the first row's window start to the causal end
+  int kend = a.Nk;
+  if (a.causal) kend = (int)max(0LL, min((long long)a.Nk, a.q_pos0 + wg_row_last - a.k_pos0 + 1));
+  int nsk = 0, shift = 0, ntiles = (kend + 31) / 32, csink = 0;
+  long long wave_lo_lim = -(1LL << 40);
+  if (a.causal && a.window > 0) {
+    const long long lo = a.q_pos0 + (long long)qt * (32 * RB) - a.window + 1 - a.k_pos0;
+    csink = (int)min((long long)kend, max(0LL, (long long)a.sink - a.k_pos0));
+    nsk = (csink + 31) / 32;
+    const int tstart = lo >= kend ? ntiles : max(nsk, (int)(max(0LL, lo) / 32));
+    shift = tstart - nsk;
+    ntiles = nsk + max(0, ntiles - tstart);
+    wave_lo_lim = a.q_pos0 + wrow0 + 31 - a.window + 1 - a.k_pos0;
+  }
+  auto tile_key0 = [&](int t) { return (t < nsk ? t : t + shift) * 32; };
+  const long long wave_free_lim = a.causal ? (a.q_pos0 + wrow0 - a.k_pos0 + 1) : (long long)a.Nk;
+  int klim, klo;
+  {
+    long long lim = a.causal ? (qpos - a.k_pos0) : (long long)a.Nk - 1;
+    lim = lim < (long long)a.Nk - 1 ? lim : (long long)a.Nk - 1;
+    klim = (int)(lim < -1 ? -1 : lim);
+    long long lo = (a.causal && a.window > 0) ? qpos - a.window + 1 - a.k_pos0 : -(1LL << 30);
+    lo = lo < -(1LL << 30) ? -(1LL << 30) : lo;
+    klo = (int)(lo > (1LL << 30) ? (1LL << 30) : lo);
+  }
+
+  const int sr = tid >> 3, sc = tid & 7;
+  Stage st;
+  auto issue = [&](int t) {
+    const int key0 = tile_key0(t);
+    const long long r = key0 + sr;
+    stage_load<HALF>(st, kg, vg, r, r < a.Nk, (a.rope_flags & 2) != 0, tab4, a.k_pos0 + r, sc);
+  };
+  auto store = [&](int buf) {
+    stage_store<HALF>(st, sm.k[buf], kTStr, sm.v[buf], kRStr, sr, sc, (a.rope_flags & 2) != 0);
+  };
+  const int gj = lane & 15;
+  const int gd = ((lane >> 4) & 1) * 16 + 4 * (gj & 3);
+  if (ntiles > 0) {
+    issue(0);
+    store(0);
+    __syncthreads();
+  }
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) issue(t + 1);
+    const int key0 = tile_key0(t);
+    // S^T = k~ q~^T and dP^T = V dO^T: lane = query, rows = 16 of the tile's keys
+    const f32x16 s = mma_rows(lds_off(&sm.k[buf][l32 * kTStr + hl * 8]), qreg);
+    const f32x16 dp = mma_rows(lds_off(&sm.v[buf][l32 * kRStr + hl * 8]), doreg);
+    float p[16], ds[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(s[j], c2, -lse2));
+    if ((long long)key0 + 32 > wave_free_lim || key0 + 32 > a.Nk ||
+        ((long long)key0 < wave_lo_lim && key0 + 32 > csink)) {
+      const int base = key0 + hl * 4;
+      const int rel = klim - base, rlo = klo - base, rsk = csink - base;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int cj = (j >> 2) * 8 + (j & 3);
+        p[j] = (cj <= rel && (cj >= rlo || cj < rsk)) ? p[j] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) ds[j] = p[j] * (dp[j] - dl);
+    bf16x8 dsb[2];
+    pack16(ds, dsb);
+    // dq~^T += k~^T dS^T (transposing reads of the row-major k~ tile)
+    mma_tr(dqacc, lds_off(&sm.k[buf][(hl * 4 + (gj >> 2)) * kTStr + gd]), dsb);
+    if (t + 1 < ntiles) store(buf ^ 1);
+    __syncthreads();
+  }
+  if (!row_ok) return;
+  store_grad<HALF>(a.dq + qrow * kD, dqacc, a.sm_scale, (a.rope_flags & 1) != 0, tab2, qpos, hl);
+}
+
+__global__ void __launch_bounds__(256) fill_zero_kernel(float* p, long long n) {
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x)
+    p[i] = 0.f;
+}
+
+// grid of a grid-stride loop: enough waves to fill the chip, capped
+inline unsigned grid_for(long long work, int block) {
+  long long g = (work + block - 1) / block;
+  const long long cap = 256LL * 64;
+  return (unsigned)(g < 1 ? 1 : (g > cap ? cap : g));
+}
+
+// grid with one thread per work item (no stride loop)
+inline unsigned grid_exact(long long work, int block) {
+  long long g = (work + block - 1) / block;
+  return (unsigned)(g < 1 ? 1 : g);
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
+  const long long rows = (long long)a.B * a.Hq * a.Nq;
+  const long long work = rows * (a.D / 8);
+  if (rows == 0) {                     // no query: dk = dv = 0 (a fill kernel, safe under graph capture)
+    const long long n = (long long)a.B * a.Hkv * a.Nk * a.D;
+    if (n > 0) {
+      hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(n, 256)), dim3(256), 0, stream, a.dk, n);
+      hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(n, 256)), dim3(256), 0, stream, a.dv, n);
+    }
+    return hipGetLastError();
+  }
+  if (a.bf16)
+    hipLaunchKernelGGL(bwd_delta_kernel<true>, dim3(grid_exact(work, 256)), dim3(256), 0, stream, a.out, a.dout,
+                       a.delta, rows, a.D);
+  else
+    hipLaunchKernelGGL(bwd_delta_kernel<false>, dim3(grid_exact(work, 256)), dim3(256), 0, stream, a.out, a.dout,
+                       a.delta, rows, a.D);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const bool half = (a.rope_flags & 4) != 0;
+  if (a.bf16) {
+    if (a.D != kD) return hipErrorInvalidValue;
+    const int G = a.Hq / a.Hkv;
+    if (!(G == 1 || G == 2 || G % 4 == 0)) return hipErrorInvalidValue;
+    const dim3 gkv(a.Hkv, (a.Nk + kKVKeys - 1) / kKVKeys, a.B);
+    if (a.Nk > 0) {
+      if (half) hipLaunchKernelGGL(bwd_dkdv_bf16_kernel<true>, gkv, dim3(kKVThreads), 0, stream, a);
+      else hipLaunchKernelGGL(bwd_dkdv_bf16_kernel<false>, gkv, dim3(kKVThreads), 0, stream, a);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    const int HPW = G < 4 ? G : 4;
+    const int rows_per_wg = 32 * (kQWaves / HPW);
+    const int quads = G > 4 ? G / 4 : 1;
+    const dim3 gq(a.Hkv * quads, (a.Nq + rows_per_wg - 1) / rows_per_wg, a.B);
+    if (half) hipLaunchKernelGGL(bwd_dq_bf16_kernel<true>, gq, dim3(kQThreads), 0, stream, a);
+    else hipLaunchKernelGGL(bwd_dq_bf16_kernel<false>, gq, dim3(kQThreads), 0, stream, a);
+    return hipGetLastError();
+  }
+  if (a.D != 64) return hipErrorInvalidValue;
+  if (a.Nk > 0) {
+    hipLaunchKernelGGL(bwd_dkdv_f32_kernel<64>, dim3((a.Nk + 63) / 64, a.Hkv, a.B), dim3(64), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(bwd_dq_f32_kernel<64>, dim3((a.Nq + 63) / 64, a.Hq, a.B), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace srt

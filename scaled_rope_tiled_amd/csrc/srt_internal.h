@@ -94,6 +94,29 @@ struct DecodeArgs {
 size_t decode_workspace_bytes(int B, int Hq, int D, int splits);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
+// ---------------------------------------------------------------- backward
+struct BwdArgs {
+  const void* q;          // [B][Hq][Nq][D] dtype, raw (rotated on load with ROTATE_Q)
+  const void* k;          // [B][Hkv][Nk][D]
+  const void* v;
+  const void* out;        // forward output [B][Hq][Nq][D] dtype
+  const void* dout;       // upstream gradient [B][Hq][Nq][D] dtype
+  const float* lse;       // forward lse [B][Hq][Nq]
+  float* delta;           // workspace [B][Hq][Nq]: sum_d dO * O
+  const float* table;
+  float* dq;              // [B][Hq][Nq][D] fp32
+  float* dk;              // [B][Hkv][Nk][D] fp32
+  float* dv;              // [B][Hkv][Nk][D] fp32
+  long long q_pos0, k_pos0;
+  int B, Hq, Hkv, Nq, Nk, D;
+  int causal, window, sink;
+  int rope_flags;         // bit0: q rotated on load, bit1: k, bit2: half-split pairs
+  int bf16;
+  float sm_scale;
+};
+
+hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
+
 // ---------------------------------------------------------------- ring
 struct RingArgs {
   const void* q;          // [B][Hq][N][D], shard-major rows

@@ -18,7 +18,7 @@ from dataclasses import dataclass, field
 
 import torch
 
-Q_ID, K_ID, V_ID = 0, 1, 2
+Q_ID, K_ID, V_ID, DO_ID = 0, 1, 2, 3   # dO: upstream gradient of the backward tests
 
 # rope method codes, same numbering as the C header
 NONE, PI, NTK, YARN = 0, 1, 2, 3

@@ -1,0 +1,113 @@
+"""GPU parity of srt_attn_backward (dq, dk, dv) vs the fp64 oracle.
+
+The forward pass (srt_attn_prefill) supplies out and lse; the oracle
+recomputes everything in fp64 from the same inputs.  Bars: fp32 kernels
+1e-4 max-abs; bf16 kernels 2e-2 max-abs after each gradient is scaled to its
+largest entry (max|err| <= 2e-2 max(1, max|ref|)).  The gradients reach ~10
+here (dv of an early key sums P dO over every later query), and the bf16
+kernels round rotated q~, k~ (so S moves by ~2^-8 |S| and P with it), P and
+dS: errors are a fixed fraction of the gradient's scale, not of 1.
+Cases span several tiles, a ragged tail, GQA 1/2/4/8, both pairings, windows
+and sinks, offsets with fully masked rows, non-causal, inputs used as given."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_helpers import device_table, f64, max_abs, need_gpu, oracle_freq, qkv
+from oracle import backward as BW
+from oracle import rope as orope
+
+pytestmark = pytest.mark.gpu
+
+YARN_SMALL = synth.Rope(synth.YARN, 10000.0, 16.0, 64.0, 1.0, 32.0)
+
+
+def _run(srt, *, dtype, D, B=1, Hq=4, Hkv=2, Nq=150, Nk=150, q_pos0=0, k_pos0=0, causal=True, window=0, sink=0,
+         half=False, rotate=True, seed=51):
+    q, k, v = qkv(B, Hq, Hkv, Nq, Nk, D, dtype, seed)
+    do = synth.randn((B, Hq, Nq, D), dtype, seed, synth.DO_ID, "cuda")
+    table, _ = device_table(srt, YARN_SMALL, D, max(q_pos0 + Nq, k_pos0 + Nk, 1))
+    th, ms, _ = oracle_freq(YARN_SMALL, D)
+    pairing = "half" if half else "interleaved"
+    if rotate:
+        flags = srt.ROTATE_Q | srt.ROTATE_K | (srt.PAIR_HALF if half else 0)
+    else:                                   # inputs already rotated, used as given
+        q = srt.rope_apply(q, table, pos0=q_pos0, pairing=pairing)
+        k = srt.rope_apply(k, table, pos0=k_pos0, pairing=pairing)
+        flags = 0
+    kw = dict(causal=causal, q_pos0=q_pos0, k_pos0=k_pos0, window=window, sink=sink)
+    o, l = srt.attn_prefill(q, k, v, table=table, rope_flags=flags, **kw)
+    dq, dk, dv = srt.attn_backward(q, k, v, o, do, l, table=table, rope_flags=flags, **kw)
+    rq, rk, rv, _ = BW.attention_backward(f64(q), f64(k), f64(v), f64(do), sm_scale=1 / math.sqrt(D),
+                                          theta=th if rotate else None, mscale=ms, pairing=pairing, **kw)
+    return (f64(dq), f64(dk), f64(dv)), (rq, rk, rv)
+
+
+def _err(got, ref):
+    return max(max_abs(g, r) for g, r in zip(got, ref))
+
+
+def _rel_err(got, ref):
+    """max|err| of each gradient over max(1, its largest reference entry)."""
+    return max(max_abs(g, r) / max(1.0, float(np.abs(r).max())) for g, r in zip(got, ref))
+
+
+def _report(tag, got, ref):
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        e = max_abs(g, r)
+        print(f"{tag} {name}: max|err| {e:.3g}  max|ref| {np.abs(r).max():.3g}  rms err {np.sqrt(np.mean((g - r) ** 2)):.3g}",
+              flush=True)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(half=True), dict(window=40, sink=4), dict(q_pos0=300, k_pos0=340),
+                                dict(causal=False), dict(rotate=False)],
+                         ids=["plain", "half", "window", "offsets", "noncausal", "given"])
+def test_backward_fp32(kw):
+    srt = need_gpu()
+    got, ref = _run(srt, dtype=torch.float32, D=64, **kw)
+    assert _err(got, ref) <= 1e-4
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(half=True), dict(window=100, sink=4), dict(window=70, sink=90),
+                                dict(q_pos0=300, k_pos0=340, Nq=130, Nk=257), dict(causal=False),
+                                dict(rotate=False), dict(B=2, Nq=64, Nk=64)],
+                         ids=["plain", "half", "window", "wide_sink", "offsets", "noncausal", "given", "batch"])
+def test_backward_bf16(kw):
+    srt = need_gpu()
+    base = dict(Nq=300, Nk=300)
+    base.update(kw)
+    got, ref = _run(srt, dtype=torch.bfloat16, D=128, Hq=8, Hkv=2, **base)
+    _report(f"bf16 {kw}", got, ref)
+    assert _rel_err(got, ref) <= 2e-2
+
+
+@pytest.mark.parametrize("G", [1, 2, 8])
+def test_backward_bf16_group_sizes(G):
+    srt = need_gpu()
+    got, ref = _run(srt, dtype=torch.bfloat16, D=128, Hq=G * (2 if G < 8 else 1), Hkv=2 if G < 8 else 1, Nq=200,
+                    Nk=200, seed=52)
+    _report(f"bf16 G={G}", got, ref)
+    assert _rel_err(got, ref) <= 2e-2
+
+
+def test_backward_bf16_2k():
+    """2048 tokens, GQA 8/2: many tiles in both kernels."""
+    srt = need_gpu()
+    got, ref = _run(srt, dtype=torch.bfloat16, D=128, Hq=8, Hkv=2, Nq=2048, Nk=2048, seed=53)
+    _report("bf16 2K", got, ref)
+    assert _rel_err(got, ref) <= 2e-2
+
+
+def test_backward_empty():
+    srt = need_gpu()
+    D = 128
+    q, k, v = qkv(1, 4, 1, 0, 64, D, torch.bfloat16, 54)
+    o = torch.empty_like(q)
+    l = torch.empty((1, 4, 0), device="cuda")
+    dk = torch.full(k.shape, float("nan"), device="cuda")
+    dv = torch.full(v.shape, float("nan"), device="cuda")
+    _, dk, dv = srt.attn_backward(q, k, v, o, o, l, dk=dk, dv=dv)
+    assert (dk == 0).all() and (dv == 0).all()

@@ -145,6 +145,15 @@ def test_abi_rejects_before_launch(srt):
     assert st == 1 and b"stride" in lib.srt_last_error()
     st = lib.srt_attn_merge_states(fake, fake, fake, fake, 0, 96, fake, 0, 96, None, 0, 1, 1, 1, 96, None)
     assert st == 2
+    # backward: workspace size, bad D, window without causal, missing workspace
+    assert lib.srt_attn_backward_workspace_size(2, 8, 100, C.byref(n)) == 0 and n.value == 2 * 8 * 100 * 4
+    bw = lambda dt, D, causal, window, ws, wsb: lib.srt_attn_backward(
+        fake, fake, fake, fake, fake, fake, dt, 1, 8, 2, 64, 64, D, 0, 0, causal, window, 0, 0.1, None, 0, 0,
+        ws, wsb, fake, fake, fake, None)
+    assert bw(1, 64, 1, 0, fake, 1 << 20) == 2
+    assert bw(0, 128, 1, 0, fake, 1 << 20) == 2
+    assert bw(1, 128, 0, 16, fake, 1 << 20) == 1 and b"causal" in lib.srt_last_error()
+    assert bw(1, 128, 1, 0, None, 0) == 4
     th = (C.c_double * 4)(1.0, 0.1, 0.01, float("inf"))
     st = lib.srt_rope_cos_sin(th, 8, 1.0, 16, fake, None)
     assert st == 1 and b"finite" in lib.srt_last_error()
