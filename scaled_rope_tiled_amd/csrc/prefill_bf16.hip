@@ -33,9 +33,13 @@
 //   from the row-major V tile with the gfx950 transposing LDS read
 //   ds_read_b64_tr_b16, four consecutive keys of one d column per read.
 //   The O^T accumulator again holds one query per lane, so the online-softmax
-//   rescale is a per-lane multiply.  The rescale runs only when a row maximum
-//   grows by more than 2^8 (exact for any reference maximum; the bound keeps
-//   e^(s - m) <= 2^8 so bf16/fp32 stay far from overflow).
+//   rescale is a per-lane multiply.  The reference m of the exponentials is
+//   folded into the QK product: q~ is stored pre-scaled by sm_scale log2(e)
+//   and the accumulator starts at -m, so the scores arrive as
+//   s sm_scale log2(e) - m and each probability is one exp2.  m is set to the
+//   first visible half's maximum and then moves only when a half's maximum
+//   exceeds it by more than 2^8 (exact for any reference; the bound keeps
+//   2^(s - m) <= 2^8 so bf16/fp32 stay far from overflow).
 //
 // Pipeline: the key range is walked in 32-key halves.  Step h issues PV of
 // half h-1 and QK of half h+1 (matrix work) next to the softmax of half h
@@ -105,6 +109,17 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   // ---- Q^T operand: query wrow0 + l32, d = ks*16 + hl*8 + 0..7, rotated on load
   // With half-split pairs, dims d and d + 64 pair up; chunks ks and ks + 4
   // of the same lane hold exactly those, so the rotation stays in-lane.
+  // q~ is stored pre-multiplied by cscale = sm_scale * log2(e) (one rounding),
+  // so S^T comes out in log2 units and the softmax needs no multiply.
+  const float cscale = a.sm_scale * kLog2e;
+  auto scale4 = [&](float4 t) { return make_float4(t.x * cscale, t.y * cscale, t.z * cscale, t.w * cscale); };
+  auto scale_chunk = [&](uint4 w) {
+    const uint32_t in[4] = {w.x, w.y, w.z, w.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack2(bf_lo(in[i]) * cscale, bf_hi(in[i]) * cscale);
+    return make_uint4(o[0], o[1], o[2], o[3]);
+  };
   bf16x8 qreg[8];
   {
     const int row = wrow0 + l32;
@@ -121,9 +136,12 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
         for (int ks = 0; ks < 4; ++ks) {
           const int d0 = ks * 16 + hl * 8;                  // first-half dims d0..d0+7 = pairs d0..d0+7
           const float4* t = tab4 + (qpos * (kD / 2) + d0) / 2;
-          const float4 tt[4] = {t[0], t[1], t[2], t[3]};
+          const float4 tt[4] = {scale4(t[0]), scale4(t[1]), scale4(t[2]), scale4(t[3])};
           rotate_chunk_pair(w[ks], w[ks + 4], tt);
         }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) w[ks] = scale_chunk(w[ks]);
       }
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) qreg[ks] = as_bf16x8(w[ks]);
@@ -136,7 +154,9 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
           w = *reinterpret_cast<const uint4*>(qg + (long long)row * kD + d0);
           if (a.rope_flags & 1) {
             const float4* t = tab4 + (qpos * (kD / 2) + d0 / 2) / 2;
-            w = rotate_chunk(w, t[0], t[1]);
+            w = rotate_chunk(w, scale4(t[0]), scale4(t[1]));
+          } else {
+            w = scale_chunk(w);
           }
         }
         qreg[ks] = as_bf16x8(w);
@@ -242,9 +262,18 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int j = 0; j < 16; ++j) oacc[db][j] = 0.f;
-  float m_run = -INFINITY;       // running max of this lane's query, in scaled log2 units
+  // Reference point of this lane's exponentials, in log2 units: scores enter
+  // the softmax as s * cscale - m_run because the QK accumulator starts at
+  // negm = -m_run.  It starts at 0, is set to the maximum of the first half
+  // holding a visible key, and afterwards moves only up, when a half's maximum
+  // exceeds it by more than 2^8.  All of it is per query: the two lanes of a
+  // query see the same pair-maximum and take the same decisions.
+  float m_run = 0.f;
+  bool seen = false;             // a visible key has been met
   float l_run = 0.f;             // this lane's partial sum (its 16 keys of every 32)
-  const float cscale = a.sm_scale * kLog2e;
+  f32x16 negm;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) negm[j] = 0.f;
   // Mask as integer compares per score: key index c is visible to this lane's
   // query iff c <= klim (causal: k_pos0 + c <= q_pos0 + wrow0 + l32; and
   // c < Nk) and, with a window, c >= klo (inside the window) or c < csink.
@@ -269,10 +298,9 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   auto qk = [&](int buf, auto kb, f32x16& acc) {
     constexpr int KB = decltype(kb)::value;
     const uint32_t kl = opaque(k_lane + buf * (kBN * kKStr * 2)) + KB * 32 * kKStr * 2;
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read16(kl), qreg[0], negm, 0, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc[j] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 1; ks < 8; ++ks) {
       const bf16x8 ka = lds_read16(kl + ks * 32);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], acc, 0, 0, 0);
     }
@@ -326,37 +354,53 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
       }
     }
 
+    // online softmax of half h: its scores arrive as s * cscale - m_run.  The
+    // reference moves (rarely, in a wave-uniform branch) before this step's
+    // QK is issued, so the next half's scores already use the new reference.
+    float mx = fmaxf(fmaxf(s_in[0], s_in[1]), s_in[2]);
+#pragma unroll
+    for (int j = 3; j < 15; j += 2) mx = fmaxf(fmaxf(mx, s_in[j]), s_in[j + 1]);
+    mx = pair_max(fmaxf(mx, s_in[15]));
+    const bool first = !seen && mx > -INFINITY;
+    seen = seen || first;
+    const bool need = __any(mx > kLazy || first);
+    float alpha = 1.f;
+    if (need) {
+      const float d = (mx > kLazy || first) ? mx : 0.f;
+      m_run += d;
+      alpha = __builtin_amdgcn_exp2f(-d);
+      l_run *= alpha;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        s_in[j] -= d;
+        negm[j] = -m_run;
+      }
+    }
+
     // matrix work of this step (the QK of the half after the last one reads a
     // buffer holding stale data; its result is never used)
     qk(qbuf, qkb, s_out);
     if (HAS_PV) pv(p_in, pbuf, pkb);
 
-    // online softmax of half h (branch-free)
-    float mx = fmaxf(fmaxf(s_in[0], s_in[1]), s_in[2]);
-#pragma unroll
-    for (int j = 3; j < 15; j += 2) mx = fmaxf(fmaxf(mx, s_in[j]), s_in[j + 1]);
-    mx = pair_max(fmaxf(mx, s_in[15])) * cscale;
-    const bool need = __any(mx > m_run + kLazy);
-    const float mnew = need ? fmaxf(m_run, mx) : m_run;
-    const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - mnew);
-    m_run = mnew;
-    const float mref = m_run == -INFINITY ? 0.f : m_run;
     float lsum = 0.f;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       uint32_t w[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s_in[half * 8 + 2 * i], cscale, -mref));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s_in[half * 8 + 2 * i + 1], cscale, -mref));
+        const float p0 = __builtin_amdgcn_exp2f(s_in[half * 8 + 2 * i]);
+        const float p1 = __builtin_amdgcn_exp2f(s_in[half * 8 + 2 * i + 1]);
         lsum += p0 + p1;
         w[i] = pack2(p0, p1);
       }
       p_out[half] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
     }
-    l_run = fmaf(l_run, alpha, lsum);
+    l_run += lsum;
     alpha_prev = alpha;
     need_prev = need;
+    // keep this half's exponentials in this step's block, next to its MFMAs
+    // (otherwise they sink past the tile barrier into the next step)
+    asm volatile("" : : "v"(p_out[0]), "v"(p_out[1]), "v"(l_run));
   };
   // Tile t+1 goes into LDS buffer (t+1) % 3 at the end of step 2t; that buffer
   // last served tile t-2, whose last reader (PV of step 2t-2) every wave has
