@@ -161,17 +161,18 @@ def bench_prefill(srt, torch, w, steps, warmup, prerotate_k=False):
             "tflops_step": flops / (ms_step * 1e-3) / 1e12, "tflops_kernel": flops / (kernel_ms * 1e-3) / 1e12}
 
 
-def traffic_from_counters(flops_unit_note=None):
-    """HBM bytes per launch from committed rocprofv3 counters, if taken on this kernel source."""
+def traffic_from_counters():
+    """HBM bytes per launch and MFMA busy fraction of the prefill kernel from
+    committed rocprofv3 counters, if they were taken on this kernel source."""
     if not os.path.exists(COUNTERS_FILE):
-        return None, "no counter file"
+        return None, None, "no counter file"
     with open(COUNTERS_FILE) as f:
         c = json.load(f)
     if c.get("source_sha256") != _sha(PREFILL_SRC):
-        return None, "kernel changed since the counters were taken"
+        return None, None, "kernel changed since the counters were taken"
     fetch = c["fetch_kib_per_dispatch"] * 1024.0 * c["fetch_scale"]
     write = c["write_kib_per_dispatch"] * 1024.0 * c["write_scale"]
-    return fetch + write, "rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated"
+    return fetch + write, c.get("mfma_util"), "rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated"
 
 
 # ----------------------------------------------------------------------------- sliding window
@@ -429,11 +430,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--only", choices=["decode", "ring", "window", "backward"], default=None,
+                    help="run one extra leg alone and print its JSON (for profiling that leg's kernels)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (multi-GPU sharding is "
-                                   "described in DESIGN.md, not built)"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1 (the multi-GPU ring is "
+                                   "not built: its per-device share is the ring leg's device_ms)"}))
         sys.exit(2)
 
     import torch
@@ -445,11 +448,23 @@ def main():
     import synth
 
     w = synth.WORKLOADS[args.workload]
+    if args.only:
+        if args.only == "decode":
+            r = bench_decode(srt, torch, synth.WORKLOADS["c5"], args.steps, args.warmup)
+        elif args.only == "ring":
+            r = bench_ring(srt, torch, synth.WORKLOADS["c4"], args.steps, args.warmup)
+        elif args.only == "window":
+            r = bench_window(srt, torch, w, 4096, 4, args.steps, args.warmup, float("nan"))
+        else:
+            r = bench_backward(srt, torch, w, args.steps, args.warmup)
+        print(json.dumps({args.only: r}), flush=True)
+        return
     p = bench_prefill(srt, torch, w, args.steps, args.warmup, not args.rotate_k_on_load)
-    traffic, traffic_note = traffic_from_counters()
+    traffic, mfma_util, traffic_note = traffic_from_counters()
     roof = {"bound": "mfma", "achieved": round(p["tflops_kernel"], 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(p["tflops_kernel"] / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic, "traffic_note": traffic_note,
+            "mfma_busy_from_counters": None if mfma_util is None else round(mfma_util, 4),
             "kernel": "prefill_bf16_kernel", "kernel_ms": round(p["kernel_ms"], 4),
             "alg_flops_per_launch": p["flops"]}
     line = {"metric": METRIC, "value": round(p["tflops_step"], 2), "unit": "TFLOP/s", "n_gpus": 1,
