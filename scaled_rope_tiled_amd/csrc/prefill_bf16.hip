@@ -36,10 +36,12 @@
 //   rescale is a per-lane multiply.  The reference m of the exponentials is
 //   folded into the QK product: q~ is stored pre-scaled by sm_scale log2(e)
 //   and the accumulator starts at -m, so the scores arrive as
-//   s sm_scale log2(e) - m and each probability is one exp2.  m is set to the
-//   first visible half's maximum and then moves only when a half's maximum
-//   exceeds it by more than 2^8 (exact for any reference; the bound keeps
-//   2^(s - m) <= 2^8 so bf16/fp32 stay far from overflow).
+//   s sm_scale log2(e) - m and each probability is one exp2.  A half's
+//   exponentials are taken against the current m at once (no row maximum on
+//   the common path); m moves, in a rare branch, to the half's maximum only
+//   when a lane's sum over the half exceeds a bound or the lane has no
+//   reference yet.  The result is exact for any reference; the bound keeps
+//   every term below it, far from bf16/fp32 overflow.
 //
 // Pipeline: the key range is walked in 32-key halves.  Step h issues PV of
 // half h-1 and QK of half h+1 (matrix work) next to the softmax of half h
@@ -70,7 +72,7 @@ constexpr int kKStr = kD + 8;     // K tile row stride (bf16 elements) = 272 B
 constexpr int kVStr = kD + 32;    // V tile row stride (bf16 elements) = 320 B
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLazy = 8.0f;     // rescale threshold (log2 units)
+constexpr float kSumBound = 4096.0f;   // a lane's exponential sum over a half that moves the reference
 constexpr int kStageRows = kBN * 16 / kThreads;   // 16-byte chunks per thread per tile and tensor
 
 struct Smem {
@@ -262,18 +264,6 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int j = 0; j < 16; ++j) oacc[db][j] = 0.f;
-  // Reference point of this lane's exponentials, in log2 units: scores enter
-  // the softmax as s * cscale - m_run because the QK accumulator starts at
-  // negm = -m_run.  It starts at 0, is set to the maximum of the first half
-  // holding a visible key, and afterwards moves only up, when a half's maximum
-  // exceeds it by more than 2^8.  All of it is per query: the two lanes of a
-  // query see the same pair-maximum and take the same decisions.
-  float m_run = 0.f;
-  bool seen = false;             // a visible key has been met
-  float l_run = 0.f;             // this lane's partial sum (its 16 keys of every 32)
-  f32x16 negm;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) negm[j] = 0.f;
   // Mask as integer compares per score: key index c is visible to this lane's
   // query iff c <= klim (causal: k_pos0 + c <= q_pos0 + wrow0 + l32; and
   // c < Nk) and, with a window, c >= klo (inside the window) or c < csink.
@@ -286,6 +276,22 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
     lo = lo < -(1LL << 30) ? -(1LL << 30) : lo;
     klo = (int)(lo > (1LL << 30) ? (1LL << 30) : lo);
   }
+  // Reference point of this lane's exponentials, in log2 units: scores enter
+  // the softmax as s * cscale - m_run because the QK accumulator starts at
+  // negm = -m_run.  It starts at 0.  After a half's exponentials are taken,
+  // a lane whose sum over the half exceeds kSumBound (some term may be large)
+  // or that has no reference yet sends the wave into a rare branch that sets
+  // m_run to the half's maximum (when above it, or for the first visible half)
+  // and takes the half's exponentials again.  The reference is then the value
+  // of a visible score, so the row's sum stays >= 1; every term stays <=
+  // kSumBound.  The two lanes of a query see the same pair maximum and take
+  // the same decisions.  Rows that see no key at all need no reference.
+  float m_run = 0.f;
+  bool mset = !(klim >= 0 && (klim >= klo || csink > 0));
+  float l_run = 0.f;             // this lane's partial sum (its 16 keys of every 32)
+  f32x16 negm;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) negm[j] = 0.f;
   const int gj = lane & 15;
   const int gd = ((lane >> 4) & 1) * 16 + 4 * (gj & 3);    // d offset inside a 32-wide block
 
@@ -325,23 +331,46 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
 
   f32x16 s_a, s_b;
   bf16x8 p_a[2], p_b[2];
-  float alpha_prev = 1.f;
+  float alpha_prev = 1.f, d_prev = 0.f;
   bool need_prev = false;
+
+  // exponentials of one half into packed bf16 P^T; returns this lane's sum
+  auto exps = [&](const f32x16& sv, bf16x8 (&pout)[2]) {
+    float lsum = 0.f;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = __builtin_amdgcn_exp2f(sv[half * 8 + 2 * i]);
+        const float p1 = __builtin_amdgcn_exp2f(sv[half * 8 + 2 * i + 1]);
+        lsum += p0 + p1;
+        w[i] = pack2(p0, p1);
+      }
+      pout[half] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+    }
+    return lsum;
+  };
 
   // One pipeline step on half h = 2t + kb: scores of half h arrive in s_in,
   // the step computes QK(h+1) into s_out and PV(h-1) from p_in while the
   // softmax of half h writes p_out.  The matrix work does not depend on the
   // softmax, so with no branch in between the scheduler interleaves the wave's
-  // MFMAs with its VALU softmax.  A rescale of O decided by the softmax of half
-  // h is applied at the start of step h+1, after PV(h-1) and before PV(h).
+  // MFMAs with its VALU softmax.  A reference moved at the end of step h-1
+  // is applied at the start of step h: to O (after PV(h-2), before PV(h-1))
+  // and to the scores of half h, whose QK was issued before the move.
   auto step = [&](auto has_pv, int qbuf, auto qkb, int pbuf, auto pkb, int key0h, f32x16& s_in, f32x16& s_out,
                   const bf16x8 (&p_in)[2], bf16x8 (&p_out)[2]) {
     constexpr bool HAS_PV = decltype(has_pv)::value;
-    if (HAS_PV && need_prev) {
+    if (need_prev) {
+      if (HAS_PV) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha_prev;
+          for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha_prev;
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s_in[j] -= d_prev;
     }
     if ((long long)key0h + 32 > wave_free_lim || key0h + 32 > a.Nk ||
         ((long long)key0h < wave_lo_lim && key0h + 32 > csink)) {
@@ -354,53 +383,36 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
       }
     }
 
-    // online softmax of half h: its scores arrive as s * cscale - m_run.  The
-    // reference moves (rarely, in a wave-uniform branch) before this step's
-    // QK is issued, so the next half's scores already use the new reference.
-    float mx = fmaxf(fmaxf(s_in[0], s_in[1]), s_in[2]);
-#pragma unroll
-    for (int j = 3; j < 15; j += 2) mx = fmaxf(fmaxf(mx, s_in[j]), s_in[j + 1]);
-    mx = pair_max(fmaxf(mx, s_in[15]));
-    const bool first = !seen && mx > -INFINITY;
-    seen = seen || first;
-    const bool need = __any(mx > kLazy || first);
-    float alpha = 1.f;
-    if (need) {
-      const float d = (mx > kLazy || first) ? mx : 0.f;
-      m_run += d;
-      alpha = __builtin_amdgcn_exp2f(-d);
-      l_run *= alpha;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        s_in[j] -= d;
-        negm[j] = -m_run;
-      }
-    }
-
     // matrix work of this step (the QK of the half after the last one reads a
     // buffer holding stale data; its result is never used)
     qk(qbuf, qkb, s_out);
     if (HAS_PV) pv(p_in, pbuf, pkb);
 
-    float lsum = 0.f;
+    // online softmax of half h against the current reference
+    float lsum = exps(s_in, p_out);
+    need_prev = __any(lsum > kSumBound || !mset);
+    if (need_prev) {
+      float mx = fmaxf(fmaxf(s_in[0], s_in[1]), s_in[2]);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      uint32_t w[4];
+      for (int j = 3; j < 15; j += 2) mx = fmaxf(fmaxf(mx, s_in[j]), s_in[j + 1]);
+      mx = pair_max(fmaxf(mx, s_in[15]));
+      const bool first = !mset && mx > -INFINITY;
+      mset = mset || first;
+      const float d = (first || mx > 0.f) ? mx : 0.f;
+      m_run += d;
+      d_prev = d;
+      // before its first visible key a row has l = 0 and O = 0; a first
+      // reference far below 0 would overflow exp2(-d), so that move scales by 1
+      alpha_prev = first ? 1.f : __builtin_amdgcn_exp2f(-d);
+      l_run *= alpha_prev;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p0 = __builtin_amdgcn_exp2f(s_in[half * 8 + 2 * i]);
-        const float p1 = __builtin_amdgcn_exp2f(s_in[half * 8 + 2 * i + 1]);
-        lsum += p0 + p1;
-        w[i] = pack2(p0, p1);
+      for (int j = 0; j < 16; ++j) {
+        s_in[j] -= d;
+        negm[j] = -m_run;
       }
-      p_out[half] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+      lsum = exps(s_in, p_out);
     }
     l_run += lsum;
-    alpha_prev = alpha;
-    need_prev = need;
-    // keep this half's exponentials in this step's block, next to its MFMAs
-    // (otherwise they sink past the tile barrier into the next step)
-    asm volatile("" : : "v"(p_out[0]), "v"(p_out[1]), "v"(l_run));
   };
   // Tile t+1 goes into LDS buffer (t+1) % 3 at the end of step 2t; that buffer
   // last served tile t-2, whose last reader (PV of step 2t-2) every wave has

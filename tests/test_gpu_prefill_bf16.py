@@ -90,3 +90,47 @@ def test_repeat_is_bitwise_deterministic():
     o2, l2 = srt.attn_prefill(q, k, v, table=table)
     assert not torch.isnan(o1).any()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# sm_scale * log2(e) = 1/8 exactly: the kernel's scaling of q is then a power
+# of two (no rounding), so large scores stay comparable at the bf16 bar.
+SM_POW2 = 0.125 * math.log(2.0)
+
+
+def _plain(srt, q, k, v, causal):
+    """q, k taken as already rotated (no table) against the oracle with no rotation."""
+    o, l = srt.attn_prefill(q, k, v, causal=causal, sm_scale=SM_POW2)
+    ro, rl = A.attention(f64(q), f64(k), f64(v), sm_scale=SM_POW2, causal=causal)
+    return f64(o), f64(l), ro, rl
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_reference_moves_as_scores_grow(causal):
+    """Key c is scaled by 1 + 5c/N, so the row maxima keep rising along the key
+    walk (from ~7 to ~40 in log2 units) and the exponentials' reference must
+    move several times; each move rescales O and the partial sums."""
+    srt = need_gpu()
+    N, D = 640, 128
+    g = torch.Generator().manual_seed(11)
+    q = (2.0 * torch.randn(1, 4, N, D, generator=g)).to(torch.bfloat16).cuda()
+    ramp = 1.0 + 5.0 * torch.arange(N, dtype=torch.float32) / N
+    k = (torch.randn(1, 1, N, D, generator=g) * ramp[None, None, :, None]).to(torch.bfloat16).cuda()
+    v = torch.randn(1, 1, N, D, generator=g).to(torch.bfloat16).cuda()
+    o, l, ro, rl = _plain(srt, q, k, v, causal)
+    assert max_abs(o, ro) <= TOL and max_abs(l, rl) <= TOL
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_reference_far_below_zero(causal):
+    """Every score is near -256 in log2 units: taken against the starting
+    reference 0 the exponentials underflow to 0, so the first visible half of
+    each row must set the reference from its maximum."""
+    srt = need_gpu()
+    N, D = 300, 128
+    g = torch.Generator().manual_seed(12)
+    q = (-4.0 * (1.0 + 0.1 * torch.randn(1, 4, N, D, generator=g))).to(torch.bfloat16).cuda()
+    k = (4.0 * (1.0 + 0.1 * torch.randn(1, 2, N, D, generator=g))).to(torch.bfloat16).cuda()
+    v = torch.randn(1, 2, N, D, generator=g).to(torch.bfloat16).cuda()
+    o, l, ro, rl = _plain(srt, q, k, v, causal)
+    assert np.all(rl < -150)
+    assert max_abs(o, ro) <= TOL and max_abs(l, rl) <= TOL
