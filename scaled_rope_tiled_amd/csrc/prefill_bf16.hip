@@ -49,9 +49,9 @@
 // exponentials overlap its own MFMAs as well as the other wave's on the SIMD.
 //
 // Staging: each thread moves two 16-byte chunks of K and of V per 64-key tile
-// (16 threads per 256-byte row: fully coalesced), rotating K in fp32 on the
-// way when asked.  Tiles rotate through three LDS buffers with one barrier per
-// tile; the next tile's global loads are in flight during two steps.  Row
+// (16 threads per 256-byte row: fully coalesced) with buffer loads whose
+// descriptor range ends at Nk, rotating K in fp32 on the way when asked.
+// Tiles rotate through three LDS buffers with one barrier per tile; the next tile's global loads are in flight during two steps.  Row
 // strides are padded (K: 272 B, V: 320 B) so the 16-byte K reads and the
 // transposing V reads of a wave hit distinct LDS banks.
 #include "mfma_common.h"
@@ -74,6 +74,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSumBound = 4096.0f;   // a lane's exponential sum over a half that moves the reference
 constexpr int kStageRows = kBN * 16 / kThreads;   // 16-byte chunks per thread per tile and tensor
+constexpr int kBufferWord3 = 0x00020000;          // buffer descriptor word 3 for raw 32-bit loads (gfx9 family)
 
 struct Smem {
   __hip_bfloat16 k[3][kBN * kKStr];
@@ -201,24 +202,38 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   uint4 kbuf[kStageRows], vbuf[kStageRows];
   float4 tbuf[kStageRows][2];
 
-  // Branch-free: rows past Nk read row Nk-1 (always valid when a tile exists) and are zeroed.
+  // K/V rows of a tile are read through buffer descriptors whose range ends
+  // at the tile's last key below Nk: rows at or past Nk read as zero in
+  // hardware, with no clamping, predication or per-tile vector arithmetic
+  // (the descriptor is scalar; each thread's byte offset is fixed).
   // K rotated on load with half-split pairs needs chunks c and c + 8 of one
   // row in one thread: then thread t takes chunks (t & 7) and (t & 7) + 8 of
   // row t >> 3 (8 threads per 256-byte row, still coalesced).
   static_assert(kStageRows == 2 && kThreads / 8 == kBN, "half-split K staging covers one row per thread");
   const int hr = tid >> 3, hc = tid & 7;
+  const uint32_t voff = sr * (kD * 2) + sc * 16;       // bytes of chunk sc of row sr within a tile
+  constexpr uint32_t kRowStep = (kThreads / 16) * kD * 2;
+  auto tile_rsrc = [&](const __hip_bfloat16* base, int key0) {
+    // (readfirstlane keeps the wave-uniform row count scalar: a vector clamp
+    // would make the descriptor divergent)
+    const int rows = __builtin_amdgcn_readfirstlane(min(kBN, max(0, a.Nk - key0)));
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (long long)key0 * kD), (short)0, rows * kD * 2,
+                                             kBufferWord3);
+  };
+  auto ld16 = [](__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(w.x, w.y, w.z, w.w);
+  };
   auto issue_loads = [&](int key0) {
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kg, key0), rv = tile_rsrc(vg, key0);
 #pragma unroll
     for (int i = 0; i < kStageRows; ++i) {
-      const int key = key0 + sr + (kThreads / 16) * i;
-      const bool in = key < a.Nk;
-      const int kc = in ? key : a.Nk - 1;
-      const uint4 vw = *reinterpret_cast<const uint4*>(vg + (long long)kc * kD + sc * 8);
-      vbuf[i] = in ? vw : make_uint4(0, 0, 0, 0);
+      vbuf[i] = ld16(rv, voff + i * kRowStep);
       if (!(ROT_K && HALF)) {
-        const uint4 kw = *reinterpret_cast<const uint4*>(kg + (long long)kc * kD + sc * 8);
-        kbuf[i] = in ? kw : make_uint4(0, 0, 0, 0);
+        kbuf[i] = ld16(rk, voff + i * kRowStep);
         if (ROT_K) {
+          const int key = key0 + sr + (kThreads / 16) * i;
+          const int kc = key < a.Nk ? key : a.Nk - 1;    // rows past Nk are zero: any valid angle
           const float4* t = tab4 + ((a.k_rope0 + kc * a.rope_step) * (kD / 2) + sc * 4) / 2;
           tbuf[i][0] = t[0];
           tbuf[i][1] = t[1];
@@ -227,13 +242,9 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
     }
     if (ROT_K && HALF) {
       const int key = key0 + hr;
-      const bool in = key < a.Nk;
-      const int kc = in ? key : a.Nk - 1;
+      const int kc = key < a.Nk ? key : a.Nk - 1;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const uint4 kw = *reinterpret_cast<const uint4*>(kg + (long long)kc * kD + (hc + 8 * i) * 8);
-        kbuf[i] = in ? kw : make_uint4(0, 0, 0, 0);
-      }
+      for (int i = 0; i < 2; ++i) kbuf[i] = ld16(rk, hr * (kD * 2) + (hc + 8 * i) * 16);
       const float4* t = tab4 + ((a.k_rope0 + kc * a.rope_step) * (kD / 2) + hc * 8) / 2;   // pairs 8hc .. 8hc+7
 #pragma unroll
       for (int q = 0; q < 4; ++q) tbuf[q >> 1][q & 1] = t[q];
@@ -417,7 +428,8 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   // Tile t+1 goes into LDS buffer (t+1) % 3 at the end of step 2t; that buffer
   // last served tile t-2, whose last reader (PV of step 2t-2) every wave has
   // passed at the barrier closing step 2t-2.  Past the last tile the store
-  // writes stale registers into an unused buffer and the loads re-read row Nk-1.
+  // writes stale registers into an unused buffer and the loads, whose range
+  // is empty, return zeros without touching memory.
   auto tile_io = [&](int next_buf, int t) {
     store_lds(next_buf);
     __syncthreads();
