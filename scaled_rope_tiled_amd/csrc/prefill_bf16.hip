@@ -74,7 +74,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSumBound = 4096.0f;   // a lane's exponential sum over a half that moves the reference
 constexpr int kStageRows = kBN * 16 / kThreads;   // 16-byte chunks per thread per tile and tensor
-constexpr int kBufferWord3 = 0x00020000;          // buffer descriptor word 3 for raw 32-bit loads (gfx9 family)
+constexpr int kBufferWord3 = 0x00020000;
+constexpr uint32_t kOnesBf16x2 = 0x3f803f80u;     // bf16 pair (1, 1)          // buffer descriptor word 3 for raw 32-bit loads (gfx9 family)
 
 struct Smem {
   __hip_bfloat16 k[3][kBN * kKStr];
@@ -345,9 +346,11 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   float alpha_prev = 1.f, d_prev = 0.f;
   bool need_prev = false;
 
-  // exponentials of one half into packed bf16 P^T; returns this lane's sum
+  // exponentials of one half into packed bf16 P^T; returns this lane's sum of
+  // the rounded probabilities (the weights PV applies), two per v_dot2 with
+  // (1, 1), in two independent chains
   auto exps = [&](const f32x16& sv, bf16x8 (&pout)[2]) {
-    float lsum = 0.f;
+    float part[2] = {0.f, 0.f};
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       uint32_t w[4];
@@ -355,12 +358,12 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
       for (int i = 0; i < 4; ++i) {
         const float p0 = __builtin_amdgcn_exp2f(sv[half * 8 + 2 * i]);
         const float p1 = __builtin_amdgcn_exp2f(sv[half * 8 + 2 * i + 1]);
-        lsum += p0 + p1;
         w[i] = pack2(p0, p1);
+        part[half] = dot2_bf16(w[i], kOnesBf16x2, part[half]);
       }
       pout[half] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
     }
-    return lsum;
+    return part[0] + part[1];
   };
 
   // One pipeline step on half h = 2t + kb: scores of half h arrive in s_in,
@@ -395,9 +398,11 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
     }
 
     // matrix work of this step (the QK of the half after the last one reads a
-    // buffer holding stale data; its result is never used)
-    qk(qbuf, qkb, s_out);
+    // buffer holding stale data; its result is never used).  PV goes first: its
+    // operands are ready, so its V reads and MFMAs cover the K reads of QK,
+    // whose dependent chain then overlaps this half's softmax.
     if (HAS_PV) pv(p_in, pbuf, pkb);
+    qk(qbuf, qkb, s_out);
 
     // online softmax of half h against the current reference
     float lsum = exps(s_in, p_out);
