@@ -44,8 +44,8 @@
 //   every term below it, far from bf16/fp32 overflow.
 //
 // Pipeline: the key range is walked in 32-key halves.  Step h issues PV of
-// half h-1 and QK of half h+1 (matrix work) next to the softmax of half h
-// (VALU work that depends on neither), as one basic block, so a wave's
+// half h-1 and then QK of half h+1 (matrix work) next to the softmax of half
+// h (VALU work that depends on neither), as one basic block, so a wave's
 // exponentials overlap its own MFMAs as well as the other wave's on the SIMD.
 //
 // Staging: each thread moves two 16-byte chunks of K and of V per 64-key tile
@@ -74,8 +74,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSumBound = 4096.0f;   // a lane's exponential sum over a half that moves the reference
 constexpr int kStageRows = kBN * 16 / kThreads;   // 16-byte chunks per thread per tile and tensor
-constexpr int kBufferWord3 = 0x00020000;
-constexpr uint32_t kOnesBf16x2 = 0x3f803f80u;     // bf16 pair (1, 1)          // buffer descriptor word 3 for raw 32-bit loads (gfx9 family)
+constexpr int kBufferWord3 = 0x00020000;          // buffer descriptor word 3 for raw 32-bit loads (gfx9 family)
+constexpr uint32_t kOnesBf16x2 = 0x3f803f80u;     // bf16 pair (1, 1)
 
 struct Smem {
   __hip_bfloat16 k[3][kBN * kKStr];
