@@ -51,9 +51,11 @@
 // Staging: each thread moves two 16-byte chunks of K and of V per 64-key tile
 // (16 threads per 256-byte row: fully coalesced) with buffer loads whose
 // descriptor range ends at Nk, rotating K in fp32 on the way when asked.
-// Tiles rotate through three LDS buffers with one barrier per tile; the next tile's global loads are in flight during two steps.  Row
-// strides are padded (K: 272 B, V: 320 B) so the 16-byte K reads and the
-// transposing V reads of a wave hit distinct LDS banks.
+// Tiles rotate through three LDS buffers with one barrier per tile; a tile's
+// global loads are in flight during two steps and its LDS stores sit at the
+// start of the step before the barrier that publishes it.  Row strides are
+// padded (K: 272 B, V: 320 B) so the 16-byte K reads and the transposing V
+// reads of a wave hit distinct LDS banks.
 #include "mfma_common.h"
 
 #include <type_traits>
@@ -430,14 +432,17 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
     }
     l_run += lsum;
   };
-  // Tile t+1 goes into LDS buffer (t+1) % 3 at the end of step 2t; that buffer
-  // last served tile t-2, whose last reader (PV of step 2t-2) every wave has
-  // passed at the barrier closing step 2t-2.  Past the last tile the store
-  // writes stale registers into an unused buffer and the loads, whose range
-  // is empty, return zeros without touching memory.
-  auto tile_io = [&](int next_buf, int t) {
+  // Tile t+1 goes into LDS buffer (t+1) % 3 at the start of step 2t, from
+  // registers loaded two steps earlier; the loads of tile t+2 are issued into
+  // the freed registers right after.  That buffer last served tile t-2,
+  // whose last reader (PV of step 2t-2) every wave has passed at the barrier
+  // closing step 2t-2; the barrier closing step 2t publishes tile t+1, first
+  // read in step 2t+1.  Spreading the stores into the step's instruction
+  // stream keeps them from bunching up in front of the barrier.  Past the
+  // last tile the stores write stale registers into an unused buffer and the
+  // loads, whose range is empty, return zeros without touching memory.
+  auto tile_store = [&](int next_buf, int t) {
     store_lds(next_buf);
-    __syncthreads();
     issue_loads(tile_key0(t + 2));
   };
   using T = std::true_type;
@@ -452,15 +457,17 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
     issue_loads(tile_key0(1));
     qk(0, K0{}, s_a);
     const int key00 = tile_key0(0);
+    tile_store(1, 0);
     step(F{}, 0, K1{}, 0, K0{}, key00, s_a, s_b, p_b, p_a);
-    tile_io(1, 0);
+    __syncthreads();
     step(T{}, 1, K0{}, 0, K0{}, key00 + 32, s_b, s_a, p_a, p_b);
     int cur = 1;                           // buffer of tile t = t % 3
     for (int t = 1; t < ntiles; ++t) {
       const int prev = cur == 0 ? 2 : cur - 1, next = cur == 2 ? 0 : cur + 1;
       const int key0 = tile_key0(t);
+      tile_store(next, t);
       step(T{}, cur, K1{}, prev, K1{}, key0, s_a, s_b, p_b, p_a);
-      tile_io(next, t);
+      __syncthreads();
       step(T{}, next, K0{}, cur, K0{}, key0 + 32, s_b, s_a, p_a, p_b);
       cur = next;
     }
