@@ -216,7 +216,8 @@ def bench_backward(srt, torch, w, steps, warmup):
     """Gradients of the prefill workload (dq, dk, dv from out, lse and dO):
     delta, dk/dv and dq launches.  Algorithmic flops: the five products of
     the backward pass (S, dP, dV, dK, dQ), 10 D per kept pair per query head;
-    the kernels recompute S and dP in both the dk/dv and the dq kernel (14 D)."""
+    the kernels recompute S and dP in both the dk/dv and the dq kernel (14 D).
+    The timed call includes rotating q and k once into the workspace."""
     import synth
     D = w.D
     q = synth.randn((w.B, w.Hq, w.N, D), torch.bfloat16, w.seed, synth.Q_ID, "cuda")
@@ -230,7 +231,8 @@ def bench_backward(srt, torch, w, steps, warmup):
     dq = torch.empty(q.shape, dtype=torch.float32, device="cuda")
     dk = torch.empty(k.shape, dtype=torch.float32, device="cuda")
     dv = torch.empty(v.shape, dtype=torch.float32, device="cuda")
-    ws = torch.empty(w.B * w.Hq * w.N * 4, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(srt.attn_backward_workspace_size(torch.bfloat16, w.B, w.Hq, w.Hkv, w.N, w.N, D,
+                                                      srt.ROTATE_Q | srt.ROTATE_K), dtype=torch.uint8, device="cuda")
     fn = lambda: srt.attn_backward(q, k, v, out, do, lse, table=table, workspace=ws, dq=dq, dk=dk, dv=dv)
     for _ in range(warmup):
         fn()

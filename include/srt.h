@@ -247,9 +247,15 @@ int srt_attn_decode_splitk(const void* q, const void* k_cache, const void* v_cac
 
 /*
  * srt_attn_backward_workspace_size - bytes of workspace srt_attn_backward
- * needs: delta = rowsum(dO * O), fp32 [B][Hq][Nq].
+ * needs for these arguments: delta = rowsum(dO * O), fp32 [B][Hq][Nq], and
+ * for BF16 a rotated copy of q ([B][Hq][Nq][D], with SRT_ROTATE_Q) and of k
+ * ([B][Hkv][Nk][D], with SRT_ROTATE_K), each region 256-byte aligned.  The
+ * rotated copies are made once per call, so the kernels stage tiles that need
+ * no rotation.  Returns SRT_ERR_INVALID for a bad dtype, negative sizes or
+ * unknown flags.
  */
-int srt_attn_backward_workspace_size(int B, int Hq, int Nq, size_t* bytes_out_host);
+int srt_attn_backward_workspace_size(int dtype, int B, int Hq, int Hkv, int Nq, int Nk, int D, int rope_flags,
+                                     size_t* bytes_out_host);
 
 /*
  * srt_attn_backward - gradients of srt_attn_prefill with respect to q, k, v.
@@ -271,7 +277,8 @@ int srt_attn_backward_workspace_size(int B, int Hq, int Nq, size_t* bytes_out_ho
  * q, out, dout: [B][Hq][Nq][D]; k, v: [B][Hkv][Nk][D]; all contiguous, dtype
  * (BF16 with D = 128 on the matrix cores, F32 with D = 64).  lse: [B][Hq][Nq]
  * fp32.  dq: [B][Hq][Nq][D], dk, dv: [B][Hkv][Nk][D], fp32 device buffers,
- * overwritten.  workspace: >= srt_attn_backward_workspace_size bytes.
+ * overwritten.  workspace: >= srt_attn_backward_workspace_size bytes for the
+ * same dtype, sizes and flags, 16-byte aligned (SRT_ERR_WORKSPACE if smaller).
  */
 int srt_attn_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
                       const float* lse, int dtype, int B, int Hq, int Hkv, int Nq, int Nk, int D,

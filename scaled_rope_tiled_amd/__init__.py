@@ -15,6 +15,7 @@ HIP stream; every step of the computation runs in the library's kernels.
     attn_decode_splitk(q, k_cache, v_cache, ...)      -> (out, lse)
     attn_ring_prefill(q, k, v, num_devices=, partition=, ...) -> (out, lse)
     attn_backward(q, k, v, out, dout, lse, ...)      -> (dq, dk, dv) fp32
+    attn_backward_workspace_size(dtype, B, Hq, Hkv, Nq, Nk, D, rope_flags) -> bytes
 """
 from __future__ import annotations
 
@@ -35,7 +36,7 @@ BAND_LOW, BAND_MID, BAND_HIGH = 0, 1, 2
 
 __all__ = ["rope_inv_freq", "rope_inv_freq_dynamic_ntk", "rope_inv_freq_factors", "rope_cos_sin", "rope_apply", "attn_prefill", "attn_merge_states",
            "attn_decode_splitk", "attn_decode_workspace_size", "attn_ring_prefill", "attn_ring_workspace_size",
-           "attn_backward", "NONE", "PI", "NTK", "YARN",
+           "attn_backward", "attn_backward_workspace_size", "NONE", "PI", "NTK", "YARN",
            "ROTATE_Q", "ROTATE_K", "PAIR_HALF", "PAIRING_INTERLEAVED", "PAIRING_HALF", "lib"]
 
 
@@ -311,6 +312,16 @@ def attn_ring_prefill(q, k, v, *, num_devices: int, partition="contiguous", devi
     return out, lse
 
 
+def attn_backward_workspace_size(dtype: torch.dtype, B: int, Hq: int, Hkv: int, Nq: int, Nk: int, D: int,
+                                 rope_flags: int) -> int:
+    """Bytes of workspace attn_backward needs (delta, and rotated q / k copies for bf16)."""
+    n = C.c_size_t()
+    _lib.check(lib().srt_attn_backward_workspace_size(_dt(torch.empty(0, dtype=dtype)), B, Hq, Hkv, Nq, Nk, D,
+                                                      int(rope_flags),
+                                                      C.byref(n)), "attn_backward_workspace_size")
+    return n.value
+
+
 def attn_backward(q, k, v, out, dout, lse, *, sm_scale: float | None = None, causal: bool = True,
                   q_pos0: int = 0, k_pos0: int = 0, table: torch.Tensor | None = None,
                   rope_flags: int | None = None, window: int = 0, sink: int = 0,
@@ -331,10 +342,9 @@ def attn_backward(q, k, v, out, dout, lse, *, sm_scale: float | None = None, cau
         raise ValueError("lse must be fp32")
     if rope_flags is None:
         rope_flags = (ROTATE_Q | ROTATE_K) if table is not None else 0
-    n = C.c_size_t()
-    _lib.check(lib().srt_attn_backward_workspace_size(B, Hq, Nq, C.byref(n)), "attn_backward_workspace_size")
+    need = attn_backward_workspace_size(q.dtype, B, Hq, Hkv, Nq, Nk, D, rope_flags)
     if workspace is None:
-        workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     dq = torch.empty(q.shape, dtype=torch.float32, device=q.device) if dq is None else dq
     dk = torch.empty(k.shape, dtype=torch.float32, device=q.device) if dk is None else dk
     dv = torch.empty(v.shape, dtype=torch.float32, device=q.device) if dv is None else dv

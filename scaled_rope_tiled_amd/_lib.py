@@ -40,7 +40,8 @@ SIGNATURES = {
                                c_int, c_int, c_int, c_int, c_int, c_void_p,
                                c_int, c_float, c_void_p, c_ll, c_int, c_int, c_int,
                                c_void_p, c_size_t, c_void_p, c_void_p, c_void_p],
-    "srt_attn_backward_workspace_size": [c_int, c_int, c_int, C.POINTER(c_size_t)],
+    "srt_attn_backward_workspace_size": [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                         C.POINTER(c_size_t)],
     "srt_attn_backward": [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int,
                           c_int, c_int, c_int, c_int, c_int, c_int,
                           c_ll, c_ll, c_int, c_int, c_int, c_float,

@@ -298,10 +298,37 @@ int srt_attn_decode_splitk(const void* q, const void* k_cache, const void* v_cac
   return hip_status(srt::launch_decode(a, (hipStream_t)stream), "attn_decode_splitk launch");
 }
 
-int srt_attn_backward_workspace_size(int B, int Hq, int Nq, size_t* bytes_out) {
+namespace {
+// Backward workspace: delta, then the rotated q and k copies (bf16 only), each 256-byte aligned.
+struct BwdWorkspace {
+  size_t delta, q_rot, k_rot, total;   // offsets of the regions (q_rot / k_rot: 0 when absent) and the size
+};
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+BwdWorkspace bwd_workspace(int dtype, int B, int Hq, int Hkv, int Nq, int Nk, int D, int rope_flags) {
+  BwdWorkspace w{0, 0, 0, 0};
+  size_t off = round256((size_t)B * Hq * Nq * sizeof(float));
+  if (dtype == SRT_BF16 && (rope_flags & SRT_ROTATE_Q) && (size_t)B * Nq > 0) {
+    w.q_rot = off;
+    off += round256((size_t)B * Hq * Nq * D * 2);
+  }
+  if (dtype == SRT_BF16 && (rope_flags & SRT_ROTATE_K) && (size_t)B * Nk > 0) {
+    w.k_rot = off;
+    off += round256((size_t)B * Hkv * Nk * D * 2);
+  }
+  w.total = off;
+  return w;
+}
+}  // namespace
+
+int srt_attn_backward_workspace_size(int dtype, int B, int Hq, int Hkv, int Nq, int Nk, int D, int rope_flags,
+                                     size_t* bytes_out) {
   if (!bytes_out) return fail(SRT_ERR_INVALID, "attn_backward_workspace_size: NULL output");
-  if (B < 0 || Hq < 1 || Nq < 0) return fail(SRT_ERR_INVALID, "attn_backward_workspace_size: bad sizes");
-  *bytes_out = (size_t)B * Hq * Nq * sizeof(float);
+  if (!valid_dtype(dtype)) return fail(SRT_ERR_INVALID, "attn_backward_workspace_size: bad dtype");
+  if (B < 0 || Hq < 1 || Hkv < 1 || Nq < 0 || Nk < 0 || D < 2)
+    return fail(SRT_ERR_INVALID, "attn_backward_workspace_size: bad sizes");
+  if (rope_flags & ~(SRT_ROTATE_Q | SRT_ROTATE_K | SRT_PAIR_HALF))
+    return fail(SRT_ERR_INVALID, "attn_backward_workspace_size: bad rope_flags");
+  *bytes_out = bwd_workspace(dtype, B, Hq, Hkv, Nq, Nk, D, rope_flags).total;
   return ok();
 }
 
@@ -340,11 +367,30 @@ int srt_attn_backward(const void* q, const void* k, const void* v, const void* o
   if (misaligned16(q) || misaligned16(k) || misaligned16(v) || misaligned16(out) || misaligned16(dout) ||
       misaligned16(dq) || misaligned16(dk) || misaligned16(dv) || misaligned16(lse) || misaligned16(table_dev))
     return fail(SRT_ERR_INVALID, "attn_backward: tensors must be 16-byte aligned");
-  const size_t need = (size_t)B * Hq * Nq * sizeof(float);
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(SRT_ERR_WORKSPACE, "attn_backward: workspace %zu bytes, need %zu", workspace_bytes, need);
+  const BwdWorkspace ws = bwd_workspace(dtype, B, Hq, Hkv, Nq, Nk, D, rope_flags);
+  if (ws.total > 0 && (!workspace || workspace_bytes < ws.total))
+    return fail(SRT_ERR_WORKSPACE, "attn_backward: workspace %zu bytes, need %zu", workspace_bytes, ws.total);
+  if (misaligned16(workspace)) return fail(SRT_ERR_INVALID, "attn_backward: workspace not 16-byte aligned");
   srt::BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse; a.delta = (float*)workspace;
+  // rotate q and k once into the workspace ([LC] §2.4: each row by its own position)
+  const bool half_pairs = (rope_flags & SRT_PAIR_HALF) != 0;
+  if (ws.q_rot) {
+    void* qr = (char*)workspace + ws.q_rot;
+    const srt::PosMap map{q_pos0, srt::kContiguous, 1, Nq};
+    const hipError_t e = srt::launch_rope_apply(q, qr, true, half_pairs, (long long)B * Hq, Nq, D, map, table_dev,
+                                                (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "attn_backward: rotating q");
+    a.q_rot = qr;
+  }
+  if (ws.k_rot) {
+    void* kr = (char*)workspace + ws.k_rot;
+    const srt::PosMap map{k_pos0, srt::kContiguous, 1, Nk};
+    const hipError_t e = srt::launch_rope_apply(k, kr, true, half_pairs, (long long)B * Hkv, Nk, D, map, table_dev,
+                                                (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "attn_backward: rotating k");
+    a.k_rot = kr;
+  }
   a.table = table_dev; a.dq = dq; a.dk = dk; a.dv = dv;
   a.q_pos0 = q_pos0; a.k_pos0 = k_pos0;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.D = D;

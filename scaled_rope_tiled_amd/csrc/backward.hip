@@ -12,7 +12,10 @@
 // Three launches: delta (HBM-bound), dk/dv (a workgroup owns a block of keys
 // of one KV head and walks the query tiles of every query head of its GQA
 // group that can see them) and dq (a workgroup owns query rows, like the
-// forward kernel, and walks the visible key tiles).  bf16 kernels (D = 128)
+// forward kernel, and walks the visible key tiles; two workgroups per CU).
+// The entry point rotates q and k once into its workspace, so the tiles the
+// kernels stage need no rotation (every key block would otherwise rotate each
+// q tile again, and every query block each k tile).  bf16 kernels (D = 128)
 // use v_mfma_f32_32x32x16_bf16 for all five products; fp32 kernels (D = 64)
 // keep every product in fp32 on the vector ALUs.  Gradients are written in
 // fp32.
@@ -504,15 +507,16 @@ __global__ void __launch_bounds__(kKVThreads) bwd_dkdv_bf16_kernel(BwdArgs a) {
   const int sr = tid >> 3, sc = tid & 7;
   Stage st;
   float l2v = 0.f, dlv = 0.f;
+  // q tiles come from the copy the entry point rotated once (always present with ROTATE_Q)
+  const __hip_bfloat16* qsrc = reinterpret_cast<const __hip_bfloat16*>(a.q_rot ? a.q_rot : a.q);
   auto issue = [&](int it) {
     const int g = it / ntq, t = t0 + it % ntq;
     const int h = hk * G + g;
     const long long hrow = ((long long)b * a.Hq + h) * a.Nq;
     const long long r = (long long)t * 32 + sr;
     const bool ok = r < a.Nq;
-    stage_load<HALF>(st, reinterpret_cast<const __hip_bfloat16*>(a.q) + hrow * kD,
-                     reinterpret_cast<const __hip_bfloat16*>(a.dout) + hrow * kD, r, ok, (a.rope_flags & 1) != 0,
-                     tab4, a.q_pos0 + r, sc);
+    stage_load<HALF>(st, qsrc + hrow * kD, reinterpret_cast<const __hip_bfloat16*>(a.dout) + hrow * kD, r, ok,
+                     false, tab4, a.q_pos0 + r, sc);
     if (tid < 32) {
       const long long rr = (long long)t * 32 + tid;
       l2v = rr < a.Nq ? a.lse[hrow + rr] * kLog2e : 0.f;
@@ -520,7 +524,7 @@ __global__ void __launch_bounds__(kKVThreads) bwd_dkdv_bf16_kernel(BwdArgs a) {
     }
   };
   auto store = [&](int buf) {
-    stage_store<HALF>(st, sm.q[buf], kTStr, sm.o[buf], kTStr, sr, sc, (a.rope_flags & 1) != 0);
+    stage_store<HALF>(st, sm.q[buf], kTStr, sm.o[buf], kTStr, sr, sc, false);
     if (tid < 32) {
       sm.l2[buf][tid] = l2v;
       sm.dl[buf][tid] = dlv;
@@ -598,7 +602,7 @@ struct DqSmem {
 };
 
 template <bool HALF>
-__global__ void __launch_bounds__(kQThreads) bwd_dq_bf16_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(kQThreads, 2) bwd_dq_bf16_kernel(BwdArgs a) {
   __shared__ DqSmem sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -664,13 +668,16 @@ __global__ void __launch_bounds__(kQThreads) bwd_dq_bf16_kernel(BwdArgs a) {
 
   const int sr = tid >> 3, sc = tid & 7;
   Stage st;
+  // k tiles come from the copy the entry point rotated once (always present with ROTATE_K)
+  const __hip_bfloat16* ksrc =
+      a.k_rot ? reinterpret_cast<const __hip_bfloat16*>(a.k_rot) + ((long long)b * a.Hkv + hk) * a.Nk * kD : kg;
   auto issue = [&](int t) {
     const int key0 = tile_key0(t);
     const long long r = key0 + sr;
-    stage_load<HALF>(st, kg, vg, r, r < a.Nk, (a.rope_flags & 2) != 0, tab4, a.k_pos0 + r, sc);
+    stage_load<HALF>(st, ksrc, vg, r, r < a.Nk, false, tab4, a.k_pos0 + r, sc);
   };
   auto store = [&](int buf) {
-    stage_store<HALF>(st, sm.k[buf], kTStr, sm.v[buf], kRStr, sr, sc, (a.rope_flags & 2) != 0);
+    stage_store<HALF>(st, sm.k[buf], kTStr, sm.v[buf], kRStr, sr, sc, false);
   };
   const int gj = lane & 15;
   const int gd = ((lane >> 4) & 1) * 16 + 4 * (gj & 3);

@@ -103,6 +103,8 @@ struct BwdArgs {
   const void* dout;       // upstream gradient [B][Hq][Nq][D] dtype
   const float* lse;       // forward lse [B][Hq][Nq]
   float* delta;           // workspace [B][Hq][Nq]: sum_d dO * O
+  const void* q_rot;      // bf16: copy of q already rotated, set whenever ROTATE_Q (staged tiles are not rotated)
+  const void* k_rot;      // the same for k (ROTATE_K)
   const float* table;
   float* dq;              // [B][Hq][Nq][D] fp32
   float* dk;              // [B][Hkv][Nk][D] fp32
