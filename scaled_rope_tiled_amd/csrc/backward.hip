@@ -446,17 +446,17 @@ __device__ inline void store_grad(float* dst, f32x16 (&acc)[4], float scale, boo
 
 // ---- dk / dv: a workgroup of 4 waves owns 128 keys of one KV head; wave w
 // its 32 keys (rotated k~ and v in registers, the B operands of S = q~ k~^T and
-// dP = dO V^T).  Query tiles of 32 rows (q~ rotated on load, dO, lse, delta)
-// are staged in LDS, double-buffered, for every query head of the group.
+// dP = dO V^T).  Query tiles of 32 rows (q~, dO, lse, delta) are staged in
+// LDS, triple-buffered, for every query head of the group.
 constexpr int kKVWaves = 4;
 constexpr int kKVThreads = 64 * kKVWaves;
 constexpr int kKVKeys = 32 * kKVWaves;
 
 struct DkdvSmem {
-  __hip_bfloat16 q[2][32 * kTStr];
-  __hip_bfloat16 o[2][32 * kTStr];
-  float l2[2][32];
-  float dl[2][32];
+  __hip_bfloat16 q[3][32 * kTStr];
+  __hip_bfloat16 o[3][32 * kTStr];
+  float l2[3][32];
+  float dl[3][32];
 };
 
 template <bool HALF>
@@ -533,19 +533,25 @@ __global__ void __launch_bounds__(kKVThreads) bwd_dkdv_bf16_kernel(BwdArgs a) {
 
   const int gj = lane & 15;
   const int gd = ((lane >> 4) & 1) * 16 + 4 * (gj & 3);
-  if (nit > 0) {
-    issue(0);
-    store(0);
-    __syncthreads();
-  }
-  for (int it = 0; it < nit; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < nit) issue(it + 1);
+  // Software pipeline over the query tiles: step i issues S and dP of tile
+  // i+1 (matrix work that depends on nothing pending) next to the softmax of
+  // tile i, then dV and dK of tile i.  Tile i sits in LDS buffer i % 3: tile
+  // i+2 is stored at the start of step i into the buffer tile i-1 used (every
+  // wave finished step i-1 at the barrier closing it) from registers loaded
+  // one step earlier, and the barrier closing step i publishes it for step
+  // i+1.
+  auto sdp = [&](int buf, f32x16& s, f32x16& dp) {
+    s = mma_rows(lds_off(&sm.q[buf][l32 * kTStr + hl * 8]), kreg);
+    dp = mma_rows(lds_off(&sm.o[buf][l32 * kTStr + hl * 8]), vreg);
+  };
+  f32x16 s_a, dp_a, s_b, dp_b;
+  auto step = [&](int it, f32x16& s, f32x16& dp, f32x16& s_nx, f32x16& dp_nx) {
+    const int buf = it % 3;
+    if (it + 2 < nit) store((it + 2) % 3);
+    if (it + 3 < nit) issue(it + 3);
+    sdp((it + 1) % 3, s_nx, dp_nx);     // past the last tile: stale buffer, result unused
     const int t = t0 + it % ntq;
     const int qt0 = t * 32;
-    // S = q~ k~^T and dP = dO V^T: lane = key, rows = 16 of the tile's queries
-    const f32x16 s = mma_rows(lds_off(&sm.q[buf][l32 * kTStr + hl * 8]), kreg);
-    const f32x16 dp = mma_rows(lds_off(&sm.o[buf][l32 * kTStr + hl * 8]), vreg);
     float p[16], ds[16];
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
@@ -580,8 +586,24 @@ __global__ void __launch_bounds__(kKVThreads) bwd_dkdv_bf16_kernel(BwdArgs a) {
     // dV^T += dO^T P and dK~^T += q~^T dS (transposing reads of the row-major tiles)
     mma_tr(dvacc, lds_off(&sm.o[buf][(hl * 4 + (gj >> 2)) * kTStr + gd]), pb);
     mma_tr(dkacc, lds_off(&sm.q[buf][(hl * 4 + (gj >> 2)) * kTStr + gd]), dsb);
-    if (it + 1 < nit) store(buf ^ 1);
     __syncthreads();
+  };
+  if (nit > 0) {
+    issue(0);
+    store(0);
+    if (nit > 1) {
+      issue(1);
+      store(1);
+    }
+    if (nit > 2) issue(2);
+    __syncthreads();
+    sdp(0, s_a, dp_a);
+    int it = 0;
+    for (; it + 1 < nit; it += 2) {
+      step(it, s_a, dp_a, s_b, dp_b);
+      step(it + 1, s_b, dp_b, s_a, dp_a);
+    }
+    if (it < nit) step(it, s_a, dp_a, s_b, dp_b);
   }
   if (!key_ok) return;
   const long long krow = ((long long)b * a.Hkv + hk) * a.Nk + key;
