@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the RoPE-scaled tiled attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload yarn_32k_bf16]
 
 Prints ONE JSON line.  The headline ``value`` is causal prefill TFLOP/s on the
 YaRN 32K workload (B=1, 32 query / 8 KV heads, D=128, N=32768, bf16, base
@@ -47,7 +47,7 @@ sys.path.insert(0, ROOT)
 METRIC = "causal prefill attn TFLOP/s + 128K decode GB/s, % of MI355X roofline"
 PEAK_BF16_TFLOPS = 2516.6       # 256 CU x 2.4 GHz x 4096 flop/clk/CU, dense
 PEAK_HBM_GBS = 8000.0
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_c3_yarn32k_counters.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_yarn32k_counters.json")
 PREFILL_SRC = os.path.join(ROOT, "scaled_rope_tiled_amd", "csrc", "prefill_bf16.hip")
 
 
@@ -425,7 +425,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c3", choices=["c2", "c3"])
+    ap.add_argument("--workload", default="yarn_32k_bf16", choices=["gqa_8k_bf16", "yarn_32k_bf16"])
     ap.add_argument("--rotate-k-on-load", action="store_true",
                     help="rotate K inside the prefill kernel at every tile load (default: once, with rope_apply)")
     ap.add_argument("--no-extras", action="store_true", help="skip the decode and ring legs")
@@ -452,9 +452,9 @@ def main():
     w = synth.WORKLOADS[args.workload]
     if args.only:
         if args.only == "decode":
-            r = bench_decode(srt, torch, synth.WORKLOADS["c5"], args.steps, args.warmup)
+            r = bench_decode(srt, torch, synth.WORKLOADS["decode_128k_bf16"], args.steps, args.warmup)
         elif args.only == "ring":
-            r = bench_ring(srt, torch, synth.WORKLOADS["c4"], args.steps, args.warmup)
+            r = bench_ring(srt, torch, synth.WORKLOADS["ntk_128k_ring_bf16"], args.steps, args.warmup)
         elif args.only == "window":
             r = bench_window(srt, torch, w, 4096, 4, args.steps, args.warmup, float("nan"))
         else:
@@ -480,9 +480,9 @@ def main():
             "roofline": roof}
     if not args.no_extras:
         torch.cuda.empty_cache()
-        line["decode"] = bench_decode(srt, torch, synth.WORKLOADS["c5"], max(5, args.steps), args.warmup)
+        line["decode"] = bench_decode(srt, torch, synth.WORKLOADS["decode_128k_bf16"], max(5, args.steps), args.warmup)
         torch.cuda.empty_cache()
-        line["ring"] = bench_ring(srt, torch, synth.WORKLOADS["c4"], max(2, args.steps // 5), 1)
+        line["ring"] = bench_ring(srt, torch, synth.WORKLOADS["ntk_128k_ring_bf16"], max(2, args.steps // 5), 1)
         torch.cuda.empty_cache()
         line["window"] = bench_window(srt, torch, w, 4096, 4, args.steps, args.warmup, p["kernel_ms"])
         torch.cuda.empty_cache()

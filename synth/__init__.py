@@ -70,17 +70,17 @@ class Workload:
 
 
 WORKLOADS = {
-    "c1": Workload("c1_tiny_fp32", 1, 1, 1, 1, 512, 64, torch.float32, Rope(NONE, 10000.0),
+    "tiny_fp32": Workload("tiny_fp32", 1, 1, 1, 1, 512, 64, torch.float32, Rope(NONE, 10000.0),
                    note="B=1 H=1 N=512 D=64 fp32 causal, plain RoPE base 1e4"),
-    "c2": Workload("c2_gqa_8k_bf16", 2, 1, 32, 8, 8192, 128, torch.bfloat16, Rope(NONE, 500000.0),
+    "gqa_8k_bf16": Workload("gqa_8k_bf16", 2, 1, 32, 8, 8192, 128, torch.bfloat16, Rope(NONE, 500000.0),
                    note="GQA 32/8 D=128 N=8192 bf16 causal, RoPE base 5e5 unscaled"),
-    "c3": Workload("c3_yarn_32k_bf16", 3, 1, 32, 8, 32768, 128, torch.bfloat16,
+    "yarn_32k_bf16": Workload("yarn_32k_bf16", 3, 1, 32, 8, 32768, 128, torch.bfloat16,
                    Rope(YARN, 10000.0, 16.0, 2048.0, 1.0, 32.0),
                    note="GQA 32/8 D=128 N=32768 bf16 causal, YaRN base 1e4 L=2048 s=16 a=1 b=32"),
-    "c4": Workload("c4_ntk_128k_ring_bf16", 4, 1, 32, 8, 131072, 128, torch.bfloat16,
+    "ntk_128k_ring_bf16": Workload("ntk_128k_ring_bf16", 4, 1, 32, 8, 131072, 128, torch.bfloat16,
                    Rope(NTK, 10000.0, 16.0), kind="ring", chunks=8,
                    note="GQA 32/8 D=128 N=131072 bf16 causal, NTK 8K->128K, 8 K/V chunks merged by LSE"),
-    "c5": Workload("c5_decode_128k_bf16", 5, 16, 32, 8, 131072, 128, torch.bfloat16,
+    "decode_128k_bf16": Workload("decode_128k_bf16", 5, 16, 32, 8, 131072, 128, torch.bfloat16,
                    Rope(PI, 10000.0, 16.0), kind="decode", splits=64,
                    note="decode B=16 GQA 32/8 D=128, 131072-position bf16 cache, PI s=16, 64 splits"),
 }

@@ -24,10 +24,10 @@ def _run(srt, rp, B, Hq, Hkv, Nq, Nk, D, *, causal=True, q_pos0=0, k_pos0=0, see
     return f64(o), f64(l), ro, rl
 
 
-def test_c1_full_parity():
+def test_tiny_fp32_full_parity():
     """B=1, H=1, N=512, D=64, fp32, causal, plain RoPE base 1e4, scale 1/sqrt(D), seed 1."""
     srt = need_gpu()
-    w = synth.WORKLOADS["c1"]
+    w = synth.WORKLOADS["tiny_fp32"]
     o, l, ro, rl = _run(srt, w.rope, w.B, w.Hq, w.Hkv, w.N, w.N, w.D, seed=w.seed)
     assert max_abs(o, ro) <= TOL
     assert max_abs(l, rl) <= TOL

@@ -60,7 +60,7 @@ def _check_rows(w, q, k, v, o, l, ranges):
     return worst_o, worst_l
 
 
-@pytest.mark.parametrize("name", ["c2", "c3"])
+@pytest.mark.parametrize("name", ["gqa_8k_bf16", "yarn_32k_bf16"])
 def test_prefill_full_size(name):
     srt = need_gpu()
     w = synth.WORKLOADS[name]
@@ -83,7 +83,7 @@ def test_ring_128k_full_size(partition):
     shards of 16384, and zig-zag shards (chunks r and 15 - r of 8192)."""
     srt = need_gpu()
     from oracle import ring as R
-    w = synth.WORKLOADS["c4"]
+    w = synth.WORKLOADS["ntk_128k_ring_bf16"]
     q, k, v = _inputs(w)
     table, _ = device_table(srt, w.rope, w.D, w.N)
     pos = torch.from_numpy(R.partition_positions(w.N, w.chunks, partition)).cuda()
@@ -100,14 +100,14 @@ def test_ring_128k_full_size(partition):
     C = w.N // w.chunks
     ranges = _row_ranges(w.N, w.seed, chunk=C // 2 if partition == "zigzag" else C, n_random=8)
     wo, wl = _check_rows(w, q, k, v, o, l, ranges)
-    print(f"c4 ring {partition}: max|dO|={wo:.3g} max|dlse|={wl:.3g}", flush=True)
+    print(f"ntk 128k ring {partition}: max|dO|={wo:.3g} max|dlse|={wl:.3g}", flush=True)
     assert wo <= TOL and wl <= TOL
 
 
 def test_decode_full_size():
     """B=16 sequences, 131072-position rotated cache (PI s=16), 64 splits; sampled (b, kv head) groups."""
     srt = need_gpu()
-    w = synth.WORKLOADS["c5"]
+    w = synth.WORKLOADS["decode_128k_bf16"]
     D, N = w.D, w.N
     q = synth.randn((w.B, w.Hq, D), w.dtype, w.seed, synth.Q_ID, "cuda")
     k = synth.randn((w.B, w.Hkv, N, D), w.dtype, w.seed, synth.K_ID, "cuda")
@@ -126,5 +126,5 @@ def test_decode_full_size():
                           sm_scale=w.sm_scale, theta=th, mscale=ms)
         worst_o = max(worst_o, max_abs(f64(o[b, hs]), ro[0]))
         worst_l = max(worst_l, max_abs(f64(l[b, hs]), rl[0]))
-    print(f"c5 decode: max|dO|={worst_o:.3g} max|dlse|={worst_l:.3g}", flush=True)
+    print(f"decode 128k: max|dO|={worst_o:.3g} max|dlse|={worst_l:.3g}", flush=True)
     assert worst_o <= TOL and worst_l <= TOL

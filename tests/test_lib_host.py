@@ -68,7 +68,7 @@ def test_inv_freq_matches_oracle(srt, case):
     assert abs(ms - oms) <= 1e-15
 
 
-def test_c3_band_classification_exact(srt):
+def test_yarn_32k_band_classification_exact(srt):
     _, _, band = srt.rope_inv_freq(srt.YARN, 10000.0, 16.0, 2048.0, 1.0, 32.0, 128)
     assert list(np.flatnonzero(band == 2)) == list(range(17))
     assert list(np.flatnonzero(band == 1)) == list(range(17, 41))

@@ -129,7 +129,7 @@ def test_yarn_two_pages_agree(D, base, L, s, alpha, beta):
     assert msc == pytest.approx(0.1 * math.log(s) + 1.0, rel=1e-15)
 
 
-def test_yarn_bands_c3_exact():
+def test_yarn_bands_32k_workload_exact():
     """Band of every pair at D=128, b=1e4, L=2048, alpha=1, beta=32 (exact).
 
     Inverting r(d) = L / (2 pi b^(2d/D)) against the thresholds gives the band
