@@ -381,14 +381,55 @@ __device__ inline void mma_tr(f32x16 (&acc)[4], uint32_t x_lane, const bf16x8 (&
   }
 }
 
-// acc = X[rows][d] R[d][cols] with X a 32-row tile in LDS (16-byte row reads) and R in registers.
-__device__ inline f32x16 mma_rows(uint32_t x_lane, const bf16x8 (&r)[8]) {
-  f32x16 acc;
+
+// acc1 += X1^T B1 and acc2 += X2^T B2 (as mma_tr), the two interleaved with
+// each step's transposing reads issued one step ahead.
+__device__ inline void mma_tr2(f32x16 (&acc1)[4], uint32_t x1, const bf16x8 (&b1)[2], f32x16 (&acc2)[4],
+                               uint32_t x2, const bf16x8 (&b2)[2]) {
+  auto rd = [](uint32_t x, int half, int db) {
+    const i16x4 lo = lds_read_tr(x + ((half * 16) * kTStr + db * 32) * 2);
+    const i16x4 hi = lds_read_tr(x + ((half * 16 + 8) * kTStr + db * 32) * 2);
+    return __builtin_bit_cast(bf16x8, (__attribute__((__vector_size__(8 * sizeof(short)))) short){
+                                          lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+  };
+  bf16x8 a1 = rd(x1, 0, 0), a2 = rd(x2, 0, 0);
 #pragma unroll
-  for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+  for (int st = 0; st < 8; ++st) {
+    const int half = st >> 2, db = st & 3;
+    bf16x8 n1 = a1, n2 = a2;
+    if (st < 7) {
+      n1 = rd(x1, (st + 1) >> 2, (st + 1) & 3);
+      n2 = rd(x2, (st + 1) >> 2, (st + 1) & 3);
+    }
+    acc1[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1[half], acc1[db], 0, 0, 0);
+    acc2[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, b2[half], acc2[db], 0, 0, 0);
+    a1 = n1;
+    a2 = n2;
+  }
+}
+
+// acc1 = X1[rows][d] R1[d][cols] and acc2 = X2 R2, X1 and X2 32-row tiles in
+// LDS (16-byte row reads), R1 and R2 in registers; the two independent chains
+// are interleaved and each d-step's LDS operands are read one step ahead, so a
+// pair of MFMAs waits on reads issued a pair earlier instead of each MFMA on
+// its own read.
+__device__ inline void mma_rows2(uint32_t x1, const bf16x8 (&r1)[8], f32x16& acc1, uint32_t x2,
+                                 const bf16x8 (&r2)[8], f32x16& acc2) {
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read16(x_lane + ks * 32), r[ks], acc, 0, 0, 0);
-  return acc;
+  for (int j = 0; j < 16; ++j) { acc1[j] = 0.f; acc2[j] = 0.f; }
+  bf16x8 a1 = lds_read16(x1), a2 = lds_read16(x2);
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    bf16x8 n1 = a1, n2 = a2;
+    if (ks < 7) {
+      n1 = lds_read16(x1 + (ks + 1) * 32);
+      n2 = lds_read16(x2 + (ks + 1) * 32);
+    }
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, r1[ks], acc1, 0, 0, 0);
+    acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, r2[ks], acc2, 0, 0, 0);
+    a1 = n1;
+    a2 = n2;
+  }
 }
 
 __device__ inline void pack16(const float (&x)[16], bf16x8 (&out)[2]) {
@@ -541,8 +582,8 @@ __global__ void __launch_bounds__(kKVThreads) bwd_dkdv_bf16_kernel(BwdArgs a) {
   // one step earlier, and the barrier closing step i publishes it for step
   // i+1.
   auto sdp = [&](int buf, f32x16& s, f32x16& dp) {
-    s = mma_rows(lds_off(&sm.q[buf][l32 * kTStr + hl * 8]), kreg);
-    dp = mma_rows(lds_off(&sm.o[buf][l32 * kTStr + hl * 8]), vreg);
+    mma_rows2(lds_off(&sm.q[buf][l32 * kTStr + hl * 8]), kreg, s, lds_off(&sm.o[buf][l32 * kTStr + hl * 8]), vreg,
+              dp);
   };
   f32x16 s_a, dp_a, s_b, dp_b;
   auto step = [&](int it, f32x16& s, f32x16& dp, f32x16& s_nx, f32x16& dp_nx) {
@@ -584,8 +625,8 @@ __global__ void __launch_bounds__(kKVThreads) bwd_dkdv_bf16_kernel(BwdArgs a) {
     pack16(p, pb);
     pack16(ds, dsb);
     // dV^T += dO^T P and dK~^T += q~^T dS (transposing reads of the row-major tiles)
-    mma_tr(dvacc, lds_off(&sm.o[buf][(hl * 4 + (gj >> 2)) * kTStr + gd]), pb);
-    mma_tr(dkacc, lds_off(&sm.q[buf][(hl * 4 + (gj >> 2)) * kTStr + gd]), dsb);
+    mma_tr2(dvacc, lds_off(&sm.o[buf][(hl * 4 + (gj >> 2)) * kTStr + gd]), pb, dkacc,
+            lds_off(&sm.q[buf][(hl * 4 + (gj >> 2)) * kTStr + gd]), dsb);
     __syncthreads();
   };
   if (nit > 0) {
@@ -713,8 +754,9 @@ __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_bf16_kernel(BwdArgs a) {
     if (t + 1 < ntiles) issue(t + 1);
     const int key0 = tile_key0(t);
     // S^T = k~ q~^T and dP^T = V dO^T: lane = query, rows = 16 of the tile's keys
-    const f32x16 s = mma_rows(lds_off(&sm.k[buf][l32 * kTStr + hl * 8]), qreg);
-    const f32x16 dp = mma_rows(lds_off(&sm.v[buf][l32 * kRStr + hl * 8]), doreg);
+    f32x16 s, dp;
+    mma_rows2(lds_off(&sm.k[buf][l32 * kTStr + hl * 8]), qreg, s, lds_off(&sm.v[buf][l32 * kRStr + hl * 8]), doreg,
+              dp);
     float p[16], ds[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(s[j], c2, -lse2));
