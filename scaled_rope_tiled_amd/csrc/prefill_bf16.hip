@@ -51,7 +51,8 @@
 // Staging: each thread moves two 16-byte chunks of K and of V per 64-key tile
 // (16 threads per 256-byte row: fully coalesced) with buffer loads whose
 // descriptor range ends at Nk, rotating K in fp32 on the way when asked.
-// Tiles rotate through three LDS buffers with one barrier per tile; a tile's
+// Tiles rotate through three LDS buffers with one barrier per tile (the loop
+// takes three tiles per trip so that buffer indices are constants); a tile's
 // global loads are in flight during two steps and its LDS stores sit at the
 // start of the step before the barrier that publishes it.  Row strides are
 // padded (K: 272 B, V: 320 B) so the 16-byte K reads and the transposing V
@@ -84,7 +85,9 @@ struct Smem {
   __hip_bfloat16 v[3][kBN * kVStr];
 };
 
-template <bool ROT_K, bool HALF>
+// ROT_K: rotate K on its way into LDS; HALF: half-split pairs; WIN: sliding
+// window and sinks (without it, the window tests fold away).
+template <bool ROT_K, bool HALF, bool WIN>
 __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a) {
   __shared__ Smem sm;
 
@@ -184,7 +187,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   int nsk = 0, shift = 0, ntiles = (kend + kBN - 1) / kBN;
   int csink = 0;                                  // keys c < csink are sinks
   long long wave_lo_lim = -(1LL << 40);           // keys >= this are in every row's window
-  if (a.window > 0) {
+  if (WIN) {
     const long long lo = a.q_pos0 + (long long)qt * (kBM * RB) - a.window + 1 - a.k_pos0;
     csink = (int)min((long long)kend, max(0LL, (long long)a.sink - a.k_pos0));
     nsk = (csink + kBN - 1) / kBN;
@@ -193,11 +196,18 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
     ntiles = nsk + max(0, ntiles - tstart);
     wave_lo_lim = a.q_pos0 + wrow0 + (kBM - 1) - a.window + 1 - a.k_pos0;
   }
-  auto tile_key0 = [&](int t) { return (t < nsk ? t : t + shift) * kBN; };
+  auto tile_key0 = [&](int t) { return WIN ? (t < nsk ? t : t + shift) * kBN : t * kBN; };
   // keys of a tile starting at key0 are all visible to every row of this wave iff
   // key0 + kBN <= Nk and k_pos0 + key0 + kBN - 1 <= q_pos0 + wrow0 (and, with a
   // window, the tile lies in every row's window or among the sinks)
   const long long wave_free_lim = a.causal ? (a.q_pos0 + wrow0 - a.k_pos0 + 1) : (long long)a.Nk;
+  // The same tests in 32-bit scalar form: a 32-key half starting at key0h
+  // evaluates the per-score mask iff key0h > mask_hi (it reaches past the
+  // diagonal of the wave's first row or past Nk) or key0h < mask_lo while
+  // reaching past the sinks (it starts before some row's window).  The
+  // clamps to the int range keep both tests exact for 0 <= key0h < Nk.
+  const int mask_hi = (int)max((long long)INT_MIN, min(wave_free_lim, (long long)a.Nk) - 32);
+  const int mask_lo = (int)max((long long)INT_MIN, min((long long)INT_MAX, wave_lo_lim));
 
   // ---- staging assignment: chunk sc (16 bytes = dims 8sc..8sc+7) of rows sr and sr + 32
   const int sc = tid & 15;
@@ -286,7 +296,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
     long long lim = a.causal ? (a.q_pos0 + wrow0 + l32 - a.k_pos0) : (long long)a.Nk - 1;
     lim = lim < (long long)a.Nk - 1 ? lim : (long long)a.Nk - 1;
     klim = (int)(lim < -1 ? -1 : lim);
-    long long lo = a.window > 0 ? a.q_pos0 + wrow0 + l32 - a.window + 1 - a.k_pos0 : -(1LL << 30);
+    long long lo = WIN ? a.q_pos0 + wrow0 + l32 - a.window + 1 - a.k_pos0 : -(1LL << 30);
     lo = lo < -(1LL << 30) ? -(1LL << 30) : lo;
     klo = (int)(lo > (1LL << 30) ? (1LL << 30) : lo);
   }
@@ -302,6 +312,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   // the same decisions.  Rows that see no key at all need no reference.
   float m_run = 0.f;
   bool mset = !(klim >= 0 && (klim >= klo || csink > 0));
+  bool all_set = __builtin_amdgcn_ballot_w64(!mset) == 0;    // wave-uniform: every lane has its reference
   float l_run = 0.f;             // this lane's partial sum (its 16 keys of every 32)
   f32x16 negm;
 #pragma unroll
@@ -315,9 +326,13 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   const uint32_t k_lane = lds_off(&sm.k[0][l32 * kKStr + hl * 8]);
   const uint32_t v_lane = lds_off(&sm.v[0][(hl * 4 + (gj >> 2)) * kVStr + gd]);
   // S^T = K Q^T: 8 d-steps of one 32x32x16 MFMA
-  auto qk = [&](int buf, auto kb, f32x16& acc) {
+  auto qk = [&](auto bufc, auto kb, f32x16& acc) {
     constexpr int KB = decltype(kb)::value;
-    const uint32_t kl = opaque(k_lane + buf * (kBN * kKStr * 2)) + KB * 32 * kKStr * 2;
+    uint32_t kl;
+    if constexpr (std::is_same_v<decltype(bufc), int>)
+      kl = opaque(k_lane + bufc * (kBN * kKStr * 2)) + KB * 32 * kKStr * 2;
+    else
+      kl = k_lane + decltype(bufc)::value * (kBN * kKStr * 2) + KB * 32 * kKStr * 2;
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read16(kl), qreg[0], negm, 0, 0, 0);
 #pragma unroll
     for (int ks = 1; ks < 8; ++ks) {
@@ -375,7 +390,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   // MFMAs with its VALU softmax.  A reference moved at the end of step h-1
   // is applied at the start of step h: to O (after PV(h-2), before PV(h-1))
   // and to the scores of half h, whose QK was issued before the move.
-  auto step = [&](auto has_pv, int qbuf, auto qkb, int pbuf, auto pkb, int key0h, f32x16& s_in, f32x16& s_out,
+  auto step = [&](auto has_pv, auto qbuf, auto qkb, int pbuf, auto pkb, int key0h, f32x16& s_in, f32x16& s_out,
                   const bf16x8 (&p_in)[2], bf16x8 (&p_out)[2]) {
     constexpr bool HAS_PV = decltype(has_pv)::value;
     if (need_prev) {
@@ -388,14 +403,14 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
 #pragma unroll
       for (int j = 0; j < 16; ++j) s_in[j] -= d_prev;
     }
-    if ((long long)key0h + 32 > wave_free_lim || key0h + 32 > a.Nk ||
-        ((long long)key0h < wave_lo_lim && key0h + 32 > csink)) {
+    if (key0h > mask_hi || (WIN && key0h < mask_lo && key0h + 32 > csink)) {
       const int base = key0h + hl * 4;
       const int rel = klim - base, rlo = klo - base, rsk = csink - base;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int cj = (j >> 2) * 8 + (j & 3);
-        s_in[j] = (cj <= rel && (cj >= rlo || cj < rsk)) ? s_in[j] : -INFINITY;
+        const bool vis = WIN ? (cj <= rel && (cj >= rlo || cj < rsk)) : cj <= rel;
+        s_in[j] = vis ? s_in[j] : -INFINITY;
       }
     }
 
@@ -408,7 +423,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
 
     // online softmax of half h against the current reference
     float lsum = exps(s_in, p_out);
-    need_prev = __any(lsum > kSumBound || !mset);
+    need_prev = (__builtin_amdgcn_ballot_w64(lsum > kSumBound) != 0) | !all_set;
     if (need_prev) {
       float mx = fmaxf(fmaxf(s_in[0], s_in[1]), s_in[2]);
 #pragma unroll
@@ -416,6 +431,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
       mx = pair_max(fmaxf(mx, s_in[15]));
       const bool first = !mset && mx > -INFINITY;
       mset = mset || first;
+      all_set = __builtin_amdgcn_ballot_w64(!mset) == 0;
       const float d = (first || mx > 0.f) ? mx : 0.f;
       m_run += d;
       d_prev = d;
@@ -449,27 +465,58 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   using F = std::false_type;
   using K0 = std::integral_constant<int, 0>;
   using K1 = std::integral_constant<int, 1>;
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
 
   if (ntiles > 0) {
     issue_loads(tile_key0(0));
     store_lds(0);
     __syncthreads();
     issue_loads(tile_key0(1));
-    qk(0, K0{}, s_a);
+    qk(B0{}, K0{}, s_a);
     const int key00 = tile_key0(0);
     tile_store(1, 0);
-    step(F{}, 0, K1{}, 0, K0{}, key00, s_a, s_b, p_b, p_a);
+    step(F{}, B0{}, K1{}, 0, K0{}, key00, s_a, s_b, p_b, p_a);
     __syncthreads();
-    step(T{}, 1, K0{}, 0, K0{}, key00 + 32, s_b, s_a, p_a, p_b);
-    int cur = 1;                           // buffer of tile t = t % 3
-    for (int t = 1; t < ntiles; ++t) {
-      const int prev = cur == 0 ? 2 : cur - 1, next = cur == 2 ? 0 : cur + 1;
+    step(T{}, B1{}, K0{}, 0, K0{}, key00 + 32, s_b, s_a, p_a, p_b);
+    // Tile t lives in LDS buffer t % 3.  Three tiles per trip keep every
+    // buffer index a compile-time constant, so K operand addresses are one
+    // base register plus immediate offsets and no buffer arithmetic is left
+    // in the loop.
+    auto tile = [&](auto curc, int t) {
+      constexpr int C = decltype(curc)::value;
+      using CUR = std::integral_constant<int, C>;
+      using PRV = std::integral_constant<int, C == 0 ? 2 : C - 1>;
+      using NXT = std::integral_constant<int, C == 2 ? 0 : C + 1>;
       const int key0 = tile_key0(t);
-      tile_store(next, t);
-      step(T{}, cur, K1{}, prev, K1{}, key0, s_a, s_b, p_b, p_a);
+      tile_store(NXT::value, t);
+      step(T{}, CUR{}, K1{}, PRV::value, K1{}, key0, s_a, s_b, p_b, p_a);
       __syncthreads();
-      step(T{}, next, K0{}, cur, K0{}, key0 + 32, s_b, s_a, p_a, p_b);
-      cur = next;
+      step(T{}, NXT{}, K0{}, C, K0{}, key0 + 32, s_b, s_a, p_a, p_b);
+    };
+    int t = 1;
+    if constexpr (ROT_K) {
+      // (rotating K on the way in needs the registers the unrolled walk
+      // would take: one tile per trip, buffer indices at run time)
+      int cur = 1;
+      for (; t < ntiles; ++t) {
+        const int prev = cur == 0 ? 2 : cur - 1, next = cur == 2 ? 0 : cur + 1;
+        const int key0 = tile_key0(t);
+        tile_store(next, t);
+        step(T{}, cur, K1{}, prev, K1{}, key0, s_a, s_b, p_b, p_a);
+        __syncthreads();
+        step(T{}, next, K0{}, cur, K0{}, key0 + 32, s_b, s_a, p_a, p_b);
+        cur = next;
+      }
+    } else {
+      for (; t + 2 < ntiles; t += 3) {
+        tile(B1{}, t);
+        tile(B2{}, t + 1);
+        tile(B0{}, t + 2);
+      }
+      if (t < ntiles) tile(B1{}, t);
+      if (t + 1 < ntiles) tile(B2{}, t + 1);
     }
     if (need_prev) {
 #pragma unroll
@@ -478,7 +525,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
         for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha_prev;
     }
     // the last step, 2(ntiles-1)+1, left P of the last half in p_b
-    pv(p_b, cur == 0 ? 2 : cur - 1, K1{});
+    pv(p_b, (ntiles - 1) % 3, K1{});
   }
 
   // ---- epilogue: combine the two lane halves' sums, normalise, write O and lse
@@ -517,14 +564,19 @@ hipError_t launch_prefill_bf16_d128(const PrefillArgs& a, hipStream_t stream) {
   const int quads = G > 4 ? G / 4 : 1;
   const dim3 grid(a.Hkv * quads, (a.Nq + rows_per_wg - 1) / rows_per_wg, a.B), block(kThreads);
   const bool rot_k = (a.rope_flags & 2) != 0, half = (a.rope_flags & 4) != 0;
-  if (rot_k && half)
-    hipLaunchKernelGGL((prefill_bf16_kernel<true, true>), grid, block, 0, stream, a);
-  else if (rot_k)
-    hipLaunchKernelGGL((prefill_bf16_kernel<true, false>), grid, block, 0, stream, a);
-  else if (half)
-    hipLaunchKernelGGL((prefill_bf16_kernel<false, true>), grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL((prefill_bf16_kernel<false, false>), grid, block, 0, stream, a);
+  const bool win = a.window > 0;
+  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, block, 0, stream, a); };
+  if (win) {
+    if (rot_k && half) go(prefill_bf16_kernel<true, true, true>);
+    else if (rot_k) go(prefill_bf16_kernel<true, false, true>);
+    else if (half) go(prefill_bf16_kernel<false, true, true>);
+    else go(prefill_bf16_kernel<false, false, true>);
+  } else {
+    if (rot_k && half) go(prefill_bf16_kernel<true, true, false>);
+    else if (rot_k) go(prefill_bf16_kernel<true, false, false>);
+    else if (half) go(prefill_bf16_kernel<false, true, false>);
+    else go(prefill_bf16_kernel<false, false, false>);
+  }
   return hipGetLastError();
 }
 
