@@ -56,12 +56,6 @@ __device__ inline void rotate_chunk_pair(uint4& w1, uint4& w2, const float4 (&t)
 
 __device__ inline bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(bf16x8, w); }
 
-// c + a.lo * b.lo + a.hi * b.hi for packed bf16 pairs, fp32 accumulate (v_dot2_f32_bf16)
-__device__ inline float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, a), __builtin_bit_cast(b2_t, b), c, false);
-}
-
 // LDS operands are addressed with 32-bit LDS byte addresses.  `opaque` hides a
 // step's base address from the loop optimisers, so every read of the step is
 // that one base register plus an immediate offset (no per-read arithmetic).

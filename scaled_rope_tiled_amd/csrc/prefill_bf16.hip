@@ -78,7 +78,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSumBound = 4096.0f;   // a lane's exponential sum over a half that moves the reference
 constexpr int kStageRows = kBN * 16 / kThreads;   // 16-byte chunks per thread per tile and tensor
 constexpr int kBufferWord3 = 0x00020000;          // buffer descriptor word 3 for raw 32-bit loads (gfx9 family)
-constexpr uint32_t kOnesBf16x2 = 0x3f803f80u;     // bf16 pair (1, 1)
 
 struct Smem {
   __hip_bfloat16 k[3][kBN * kKStr];
@@ -363,9 +362,10 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   float alpha_prev = 1.f, d_prev = 0.f;
   bool need_prev = false;
 
-  // exponentials of one half into packed bf16 P^T; returns this lane's sum of
-  // the rounded probabilities (the weights PV applies), two per v_dot2 with
-  // (1, 1), in two independent chains
+  // exponentials of one half into packed bf16 P^T; returns this lane's fp32
+  // sum of the probabilities, in two independent chains of adds (a v_dot2
+  // over the packed pairs is one instruction per two terms, but it competes
+  // with the matrix cores, adds do not)
   auto exps = [&](const f32x16& sv, bf16x8 (&pout)[2]) {
     float part[2] = {0.f, 0.f};
 #pragma unroll
@@ -376,7 +376,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
         const float p0 = __builtin_amdgcn_exp2f(sv[half * 8 + 2 * i]);
         const float p1 = __builtin_amdgcn_exp2f(sv[half * 8 + 2 * i + 1]);
         w[i] = pack2(p0, p1);
-        part[half] = dot2_bf16(w[i], kOnesBf16x2, part[half]);
+        part[half] += p0 + p1;
       }
       pout[half] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
     }
