@@ -287,28 +287,40 @@ constexpr int kRStr = kD + 8;     // 272 B: rows read only as 16-byte row chunks
 
 // Load 8 d-chunks of one row (d = ks * 16 + hl * 8 + 0..7) and rotate them
 // (interleaved pairs in-chunk; half-split pairs chunk ks with ks + 4).
+// With scale != 1 the values are multiplied by it before the one rounding to
+// bf16 (through the table when rotating).
 template <bool HALF>
 __device__ inline void load_row_rotated(const __hip_bfloat16* row, bool ok, bool rotate, const float4* tab4,
-                                        long long pos, int hl, bf16x8 (&out)[8]) {
+                                        long long pos, int hl, bf16x8 (&out)[8], float scale = 1.f) {
   uint4 w[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks)
     w[ks] = ok ? *reinterpret_cast<const uint4*>(row + ks * 16 + hl * 8) : make_uint4(0, 0, 0, 0);
+  auto sc4 = [&](float4 t) { return make_float4(t.x * scale, t.y * scale, t.z * scale, t.w * scale); };
   if (ok && rotate) {
     if (HALF) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int d0 = ks * 16 + hl * 8;
         const float4* t = tab4 + (pos * (kD / 2) + d0) / 2;
-        const float4 tt[4] = {t[0], t[1], t[2], t[3]};
+        const float4 tt[4] = {sc4(t[0]), sc4(t[1]), sc4(t[2]), sc4(t[3])};
         rotate_chunk_pair(w[ks], w[ks + 4], tt);
       }
     } else {
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const float4* t = tab4 + (pos * (kD / 2) + (ks * 16 + hl * 8) / 2) / 2;
-        w[ks] = rotate_chunk(w[ks], t[0], t[1]);
+        w[ks] = rotate_chunk(w[ks], sc4(t[0]), sc4(t[1]));
       }
+    }
+  } else if (scale != 1.f) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const uint32_t in[4] = {w[ks].x, w[ks].y, w[ks].z, w[ks].w};
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = pack2(bf_lo(in[i]) * scale, bf_hi(in[i]) * scale);
+      w[ks] = make_uint4(o[0], o[1], o[2], o[3]);
     }
   }
 #pragma unroll
@@ -427,6 +439,24 @@ __device__ inline void mma_rows2(uint32_t x1, const bf16x8 (&r1)[8], f32x16& acc
     }
     acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, r1[ks], acc1, 0, 0, 0);
     acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, r2[ks], acc2, 0, 0, 0);
+    a1 = n1;
+    a2 = n2;
+  }
+}
+
+// mma_rows2 with the accumulators starting at c1 and c2 instead of zero.
+__device__ inline void mma_rows2c(uint32_t x1, const bf16x8 (&r1)[8], f32x16& acc1, const f32x16& c1, uint32_t x2,
+                                  const bf16x8 (&r2)[8], f32x16& acc2, const f32x16& c2) {
+  bf16x8 a1 = lds_read16(x1), a2 = lds_read16(x2);
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    bf16x8 n1 = a1, n2 = a2;
+    if (ks < 7) {
+      n1 = lds_read16(x1 + (ks + 1) * 32);
+      n2 = lds_read16(x2 + (ks + 1) * 32);
+    }
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, r1[ks], ks == 0 ? c1 : acc1, 0, 0, 0);
+    acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, r2[ks], ks == 0 ? c2 : acc2, 0, 0, 0);
     a1 = n1;
     a2 = n2;
   }
@@ -654,8 +684,10 @@ __global__ void __launch_bounds__(kKVThreads) bwd_dkdv_bf16_kernel(BwdArgs a) {
 
 // ---- dq: a workgroup of 4 waves owns one KV head and 32 * (4 / HPW) query
 // rows of HPW = min(G, 4) query heads (as the forward kernel); wave w holds
-// rotated q and dO of its 32 rows in registers and walks 32-key tiles of
-// rotated k and v staged in LDS.
+// rotated q (pre-multiplied by sm_scale log2(e), as in the forward) and dO of
+// its 32 rows in registers and walks 32-key tiles of rotated k and v staged in
+// LDS.  The S^T accumulator starts at -lse log2(e) and the dP^T accumulator at
+// -delta, so P = exp2(S^T) and dS = P (dP - delta) = P dP^T.
 constexpr int kQWaves = 4;
 constexpr int kQThreads = 64 * kQWaves;
 
@@ -664,7 +696,7 @@ struct DqSmem {
   __hip_bfloat16 v[2][32 * kRStr];
 };
 
-template <bool HALF>
+template <bool HALF, bool WIN>
 __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_bf16_kernel(BwdArgs a) {
   __shared__ DqSmem sm;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -689,15 +721,22 @@ __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_bf16_kernel(BwdArgs a) {
   const __hip_bfloat16* kg = reinterpret_cast<const __hip_bfloat16*>(a.k) + ((long long)b * a.Hkv + hk) * a.Nk * kD;
   const __hip_bfloat16* vg = reinterpret_cast<const __hip_bfloat16*>(a.v) + ((long long)b * a.Hkv + hk) * a.Nk * kD;
 
+  const float c2 = a.sm_scale * kLog2e;
   bf16x8 qreg[8], doreg[8];
   load_row_rotated<HALF>(reinterpret_cast<const __hip_bfloat16*>(a.q) + qrow * kD, row_ok, (a.rope_flags & 1) != 0,
-                         tab4, qpos, hl, qreg);
+                         tab4, qpos, hl, qreg, c2);
   load_row_rotated<HALF>(reinterpret_cast<const __hip_bfloat16*>(a.dout) + qrow * kD, row_ok, false, tab4, 0, hl,
                          doreg);
-  const float c2 = a.sm_scale * kLog2e;
+  // Rows past Nq have q = dO = 0, so S^T = dP^T = 0 and dS = 0.  A row with no
+  // visible key (lse = -inf) only meets masked halves, where P is forced to 0.
   const float lse2 = row_ok ? a.lse[qrow] * kLog2e : 0.f;
   const float dl = row_ok ? a.delta[qrow] : 0.f;
-  f32x16 dqacc[4];
+  f32x16 negl, negd, dqacc[4];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    negl[j] = -lse2;
+    negd[j] = -dl;
+  }
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -708,7 +747,7 @@ __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_bf16_kernel(BwdArgs a) {
   if (a.causal) kend = (int)max(0LL, min((long long)a.Nk, a.q_pos0 + wg_row_last - a.k_pos0 + 1));
   int nsk = 0, shift = 0, ntiles = (kend + 31) / 32, csink = 0;
   long long wave_lo_lim = -(1LL << 40);
-  if (a.causal && a.window > 0) {
+  if (WIN) {
     const long long lo = a.q_pos0 + (long long)qt * (32 * RB) - a.window + 1 - a.k_pos0;
     csink = (int)min((long long)kend, max(0LL, (long long)a.sink - a.k_pos0));
     nsk = (csink + 31) / 32;
@@ -717,67 +756,99 @@ __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_bf16_kernel(BwdArgs a) {
     ntiles = nsk + max(0, ntiles - tstart);
     wave_lo_lim = a.q_pos0 + wrow0 + 31 - a.window + 1 - a.k_pos0;
   }
-  auto tile_key0 = [&](int t) { return (t < nsk ? t : t + shift) * 32; };
+  auto tile_key0 = [&](int t) { return WIN ? (t < nsk ? t : t + shift) * 32 : t * 32; };
+  // a 32-key tile at key0 needs the per-score mask iff key0 > mask_hi (past the
+  // diagonal of the wave's first row, or past Nk) or, with a window, it starts
+  // before some row's window while reaching past the sinks
   const long long wave_free_lim = a.causal ? (a.q_pos0 + wrow0 - a.k_pos0 + 1) : (long long)a.Nk;
+  const int mask_hi = (int)max((long long)INT_MIN, min(wave_free_lim, (long long)a.Nk) - 32);
+  const int mask_lo = (int)max((long long)INT_MIN, min((long long)INT_MAX, wave_lo_lim));
   int klim, klo;
   {
     long long lim = a.causal ? (qpos - a.k_pos0) : (long long)a.Nk - 1;
     lim = lim < (long long)a.Nk - 1 ? lim : (long long)a.Nk - 1;
     klim = (int)(lim < -1 ? -1 : lim);
-    long long lo = (a.causal && a.window > 0) ? qpos - a.window + 1 - a.k_pos0 : -(1LL << 30);
+    long long lo = WIN ? qpos - a.window + 1 - a.k_pos0 : -(1LL << 30);
     lo = lo < -(1LL << 30) ? -(1LL << 30) : lo;
     klo = (int)(lo > (1LL << 30) ? (1LL << 30) : lo);
   }
 
-  const int sr = tid >> 3, sc = tid & 7;
-  Stage st;
-  // k tiles come from the copy the entry point rotated once (always present with ROTATE_K)
+  // staging: thread t moves 16-byte chunk t & 15 of rows t >> 4 and (t >> 4) + 16
+  // of a k and a v tile (16 threads per 256-byte row), through buffer
+  // descriptors whose range ends at Nk (rows past it read as zero)
   const __hip_bfloat16* ksrc =
       a.k_rot ? reinterpret_cast<const __hip_bfloat16*>(a.k_rot) + ((long long)b * a.Hkv + hk) * a.Nk * kD : kg;
-  auto issue = [&](int t) {
-    const int key0 = tile_key0(t);
-    const long long r = key0 + sr;
-    stage_load<HALF>(st, ksrc, vg, r, r < a.Nk, false, tab4, a.k_pos0 + r, sc);
+  const int sc = tid & 15, sr = tid >> 4;
+  const uint32_t soff = sr * (kD * 2) + sc * 16;
+  uint4 kb[2], vb[2];
+  auto issue = [&](int key0) {
+    const int bytes = min(32, max(0, a.Nk - key0)) * (kD * 2);
+    const __amdgpu_buffer_rsrc_t rk = raw_buffer(ksrc + (long long)key0 * kD, bytes);
+    const __amdgpu_buffer_rsrc_t rv = raw_buffer(vg + (long long)key0 * kD, bytes);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      kb[i] = buffer_ld16(rk, soff + i * 16 * (kD * 2));
+      vb[i] = buffer_ld16(rv, soff + i * 16 * (kD * 2));
+    }
   };
   auto store = [&](int buf) {
-    stage_store<HALF>(st, sm.k[buf], kTStr, sm.v[buf], kRStr, sr, sc, false);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      *reinterpret_cast<uint4*>(&sm.k[buf][(sr + 16 * i) * kTStr + sc * 8]) = kb[i];
+      *reinterpret_cast<uint4*>(&sm.v[buf][(sr + 16 * i) * kRStr + sc * 8]) = vb[i];
+    }
   };
   const int gj = lane & 15;
   const int gd = ((lane >> 4) & 1) * 16 + 4 * (gj & 3);
-  if (ntiles > 0) {
-    issue(0);
-    store(0);
-    __syncthreads();
-  }
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) issue(t + 1);
+  const uint32_t k_row = lds_off(&sm.k[0][l32 * kTStr + hl * 8]);
+  const uint32_t v_row = lds_off(&sm.v[0][l32 * kRStr + hl * 8]);
+  const uint32_t k_tr = lds_off(&sm.k[0][(hl * 4 + (gj >> 2)) * kTStr + gd]);
+  constexpr uint32_t kKBuf = 32 * kTStr * 2, kVBuf = 32 * kRStr * 2;
+
+  // One 32-key tile in LDS buffer BUF (a compile-time constant: the loop takes
+  // two tiles per trip).  The loads of the next tile were issued a tile
+  // earlier; they go to the other buffer, which every wave left at the barrier
+  // closing the previous tile.  Past the last tile the loads and stores only
+  // touch the unused buffer.
+  auto tile = [&](auto bufc, int t) {
+    constexpr int BUF = decltype(bufc)::value;
     const int key0 = tile_key0(t);
-    // S^T = k~ q~^T and dP^T = V dO^T: lane = query, rows = 16 of the tile's keys
+    issue(tile_key0(t + 1));
+    // S^T = k~ q~^T - lse and dP^T = V dO^T - delta: lane = query, rows = 16 of the tile's keys
     f32x16 s, dp;
-    mma_rows2(lds_off(&sm.k[buf][l32 * kTStr + hl * 8]), qreg, s, lds_off(&sm.v[buf][l32 * kRStr + hl * 8]), doreg,
-              dp);
-    float p[16], ds[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(s[j], c2, -lse2));
-    if ((long long)key0 + 32 > wave_free_lim || key0 + 32 > a.Nk ||
-        ((long long)key0 < wave_lo_lim && key0 + 32 > csink)) {
+    mma_rows2c(k_row + BUF * kKBuf, qreg, s, negl, v_row + BUF * kVBuf, doreg, dp, negd);
+    if (key0 > mask_hi || (WIN && key0 < mask_lo && key0 + 32 > csink)) {
       const int base = key0 + hl * 4;
       const int rel = klim - base, rlo = klo - base, rsk = csink - base;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int cj = (j >> 2) * 8 + (j & 3);
-        p[j] = (cj <= rel && (cj >= rlo || cj < rsk)) ? p[j] : 0.f;
+        const bool vis = WIN ? (cj <= rel && (cj >= rlo || cj < rsk)) : cj <= rel;
+        s[j] = vis ? s[j] : -INFINITY;
       }
     }
+    float ds[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) ds[j] = p[j] * (dp[j] - dl);
+    for (int j = 0; j < 16; ++j) ds[j] = __builtin_amdgcn_exp2f(s[j]) * dp[j];
     bf16x8 dsb[2];
     pack16(ds, dsb);
     // dq~^T += k~^T dS^T (transposing reads of the row-major k~ tile)
-    mma_tr(dqacc, lds_off(&sm.k[buf][(hl * 4 + (gj >> 2)) * kTStr + gd]), dsb);
-    if (t + 1 < ntiles) store(buf ^ 1);
+    mma_tr(dqacc, k_tr + BUF * kKBuf, dsb);
+    store(BUF ^ 1);
     __syncthreads();
+  };
+  if (ntiles > 0) {
+    issue(tile_key0(0));
+    store(0);
+    __syncthreads();
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    int t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+      tile(B0{}, t);
+      tile(B1{}, t + 1);
+    }
+    if (t < ntiles) tile(B0{}, t);
   }
   if (!row_ok) return;
   store_grad<HALF>(a.dq + qrow * kD, dqacc, a.sm_scale, (a.rope_flags & 1) != 0, tab2, qpos, hl);
@@ -838,8 +909,14 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
     const int rows_per_wg = 32 * (kQWaves / HPW);
     const int quads = G > 4 ? G / 4 : 1;
     const dim3 gq(a.Hkv * quads, (a.Nq + rows_per_wg - 1) / rows_per_wg, a.B);
-    if (half) hipLaunchKernelGGL(bwd_dq_bf16_kernel<true>, gq, dim3(kQThreads), 0, stream, a);
-    else hipLaunchKernelGGL(bwd_dq_bf16_kernel<false>, gq, dim3(kQThreads), 0, stream, a);
+    const bool win = a.causal && a.window > 0;
+    if (win) {
+      if (half) hipLaunchKernelGGL((bwd_dq_bf16_kernel<true, true>), gq, dim3(kQThreads), 0, stream, a);
+      else hipLaunchKernelGGL((bwd_dq_bf16_kernel<false, true>), gq, dim3(kQThreads), 0, stream, a);
+    } else {
+      if (half) hipLaunchKernelGGL((bwd_dq_bf16_kernel<true, false>), gq, dim3(kQThreads), 0, stream, a);
+      else hipLaunchKernelGGL((bwd_dq_bf16_kernel<false, false>), gq, dim3(kQThreads), 0, stream, a);
+    }
     return hipGetLastError();
   }
   if (a.D != 64) return hipErrorInvalidValue;

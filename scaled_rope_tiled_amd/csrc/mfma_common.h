@@ -76,6 +76,19 @@ __device__ inline i16x4 lds_read_tr(uint32_t addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)addr);
 }
 
+// Raw buffer descriptor over `bytes` bytes from `base`: 32-bit byte offsets,
+// and loads at or past `bytes` return zero without touching memory.  The
+// size is made wave-uniform (readfirstlane) so the descriptor stays scalar.
+constexpr int kRawBufferWord3 = 0x00020000;   // descriptor word 3 for raw 32-bit loads (gfx9 family)
+__device__ inline __amdgpu_buffer_rsrc_t raw_buffer(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, __builtin_amdgcn_readfirstlane(bytes),
+                                           kRawBufferWord3);
+}
+__device__ inline uint4 buffer_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(w.x, w.y, w.z, w.w);
+}
+
 // Lanes l and l ^ 32 hold the same query (different keys).  v_permlane32_swap
 // of a value with itself leaves the lower half's values in the first result and
 // the upper half's in the second, in every lane, so their max / sum combines
