@@ -524,13 +524,13 @@ constexpr int kKVThreads = 64 * kKVWaves;
 constexpr int kKVKeys = 32 * kKVWaves;
 
 struct DkdvSmem {
-  __hip_bfloat16 q[3][32 * kTStr];
-  __hip_bfloat16 o[3][32 * kTStr];
+  alignas(16) __hip_bfloat16 q[3][32 * kTStr];
+  alignas(16) __hip_bfloat16 o[3][32 * kTStr];
   float l2[3][32];
   float dl[3][32];
 };
 
-template <bool HALF>
+template <bool HALF, bool WIN>
 __global__ void __launch_bounds__(kKVThreads) bwd_dkdv_bf16_kernel(BwdArgs a) {
   __shared__ DkdvSmem sm;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -564,38 +564,62 @@ __global__ void __launch_bounds__(kKVThreads) bwd_dkdv_bf16_kernel(BwdArgs a) {
   const long long kp_last = a.k_pos0 + min(a.Nk, wg_k0 + kKVKeys) - 1;
   long long r_lo = 0, r_hi = a.Nq;
   if (a.causal) r_lo = max(0LL, min((long long)a.Nq, kp_first - a.q_pos0));
-  if (a.causal && a.window > 0 && kp_first >= a.sink)
-    r_hi = max(0LL, min((long long)a.Nq, kp_last + a.window - a.q_pos0));
+  if (WIN && kp_first >= a.sink) r_hi = max(0LL, min((long long)a.Nq, kp_last + a.window - a.q_pos0));
   const int t0 = (int)(r_lo / 32);
   const int ntq = r_hi > r_lo ? (int)((r_hi + 31) / 32) - t0 : 0;
   const int nit = G * ntq;
 
-  // the wave's keys: all visible to a tile's rows iff the tile lies inside the
-  // causal triangle, inside every window (or the keys are all sinks) and in Nq
+  // The wave's keys are all visible to every row of query tile t (no per-score
+  // mask) iff tm_lo <= t <= tm_hi: the tile lies inside the causal triangle
+  // (q_pos0 + 32 t >= last key position), inside Nq and, with a window and
+  // keys that are not all sinks, inside every row's window.
   const long long kw_first = a.k_pos0 + wk0, kw_last = kw_first + 31;
   const bool is_sink = kpos < a.sink;
+  auto cdiv = [](long long x, long long y) { return x >= 0 ? (x + y - 1) / y : -((-x) / y); };
+  long long tlo = a.causal ? cdiv(kw_last - a.q_pos0, 32) : 0, thi = a.Nq / 32 - 1;
+  if (WIN && kw_last >= a.sink) thi = min(thi, cdiv(a.window - 31 + kw_first - a.q_pos0, 32) - 1);
+  const int tm_lo = (int)max((long long)INT_MIN, min((long long)INT_MAX, tlo));
+  const int tm_hi = (int)max((long long)INT_MIN, min((long long)INT_MAX, thi));
 
-  const int sr = tid >> 3, sc = tid & 7;
-  Stage st;
-  float l2v = 0.f, dlv = 0.f;
-  // q tiles come from the copy the entry point rotated once (always present with ROTATE_Q)
+  // staging: thread t moves 16-byte chunk t & 15 of rows t >> 4 and (t >> 4) + 16
+  // of a q~ and a dO tile (16 threads per 256-byte row) through buffer
+  // descriptors whose range ends at Nq; threads 0..31 move lse and delta
   const __hip_bfloat16* qsrc = reinterpret_cast<const __hip_bfloat16*>(a.q_rot ? a.q_rot : a.q);
-  auto issue = [&](int it) {
-    const int g = it / ntq, t = t0 + it % ntq;
-    const int h = hk * G + g;
-    const long long hrow = ((long long)b * a.Hq + h) * a.Nq;
-    const long long r = (long long)t * 32 + sr;
-    const bool ok = r < a.Nq;
-    stage_load<HALF>(st, qsrc + hrow * kD, reinterpret_cast<const __hip_bfloat16*>(a.dout) + hrow * kD, r, ok,
-                     false, tab4, a.q_pos0 + r, sc);
+  const __hip_bfloat16* dog = reinterpret_cast<const __hip_bfloat16*>(a.dout);
+  const int sc = tid & 15, sr = tid >> 4;
+  const uint32_t soff = sr * (kD * 2) + sc * 16;
+  uint4 qb[2], ob[2];
+  float l2v = 0.f, dlv = 0.f;
+  // tiles are walked head by head (g), then row tile t = t0 .. t0 + ntq - 1;
+  // (ig, itq) is the next tile to load; past the last one the range is empty
+  int ig = 0, itq = t0;
+  auto issue = [&]() {
+    const long long hrow = ((long long)b * a.Hq + hk * G + ig) * a.Nq + (long long)itq * 32;
+    const int rows = ig < G ? min(32, max(0, a.Nq - itq * 32)) : 0;
+    const __amdgpu_buffer_rsrc_t rq = raw_buffer(qsrc + hrow * kD, rows * (kD * 2));
+    const __amdgpu_buffer_rsrc_t ro = raw_buffer(dog + hrow * kD, rows * (kD * 2));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      qb[i] = buffer_ld16(rq, soff + i * 16 * (kD * 2));
+      ob[i] = buffer_ld16(ro, soff + i * 16 * (kD * 2));
+    }
     if (tid < 32) {
-      const long long rr = (long long)t * 32 + tid;
-      l2v = rr < a.Nq ? a.lse[hrow + rr] * kLog2e : 0.f;
-      dlv = rr < a.Nq ? a.delta[hrow + rr] : 0.f;
+      const __amdgpu_buffer_rsrc_t rl = raw_buffer(a.lse + hrow, rows * 4);
+      const __amdgpu_buffer_rsrc_t rd = raw_buffer(a.delta + hrow, rows * 4);
+      l2v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, tid * 4, 0, 0)) * kLog2e;
+      dlv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, tid * 4, 0, 0));
+    }
+    if (++itq == t0 + ntq) {
+      itq = t0;
+      ++ig;
     }
   };
   auto store = [&](int buf) {
-    stage_store<HALF>(st, sm.q[buf], kTStr, sm.o[buf], kTStr, sr, sc, false);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      *reinterpret_cast<uint4*>(&sm.q[buf][(sr + 16 * i) * kTStr + sc * 8]) = qb[i];
+      *reinterpret_cast<uint4*>(&sm.o[buf][(sr + 16 * i) * kTStr + sc * 8]) = ob[i];
+    }
     if (tid < 32) {
       sm.l2[buf][tid] = l2v;
       sm.dl[buf][tid] = dlv;
@@ -610,19 +634,21 @@ __global__ void __launch_bounds__(kKVThreads) bwd_dkdv_bf16_kernel(BwdArgs a) {
   // i+2 is stored at the start of step i into the buffer tile i-1 used (every
   // wave finished step i-1 at the barrier closing it) from registers loaded
   // one step earlier, and the barrier closing step i publishes it for step
-  // i+1.
+  // i+1.  Past the last tile the stores fill an unused buffer and the loads,
+  // whose range is empty, return zeros.
   auto sdp = [&](int buf, f32x16& s, f32x16& dp) {
     mma_rows2(lds_off(&sm.q[buf][l32 * kTStr + hl * 8]), kreg, s, lds_off(&sm.o[buf][l32 * kTStr + hl * 8]), vreg,
               dp);
   };
   f32x16 s_a, dp_a, s_b, dp_b;
-  auto step = [&](int it, f32x16& s, f32x16& dp, f32x16& s_nx, f32x16& dp_nx) {
-    const int buf = it % 3;
-    if (it + 2 < nit) store((it + 2) % 3);
-    if (it + 3 < nit) issue(it + 3);
-    sdp((it + 1) % 3, s_nx, dp_nx);     // past the last tile: stale buffer, result unused
-    const int t = t0 + it % ntq;
-    const int qt0 = t * 32;
+  int bcur = 0, bnext = 1, bfree = 2;      // buffers of tiles i, i+1, i+2
+  int ct = t0;                             // row tile of the current step
+  auto step = [&](f32x16& s, f32x16& dp, f32x16& s_nx, f32x16& dp_nx) {
+    const int buf = bcur;
+    store(bfree);
+    issue();
+    sdp(bnext, s_nx, dp_nx);     // past the last tile: stale buffer, result unused
+    const int t = ct;
     float p[16], ds[16];
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
@@ -636,16 +662,14 @@ __global__ void __launch_bounds__(kKVThreads) bwd_dkdv_bf16_kernel(BwdArgs a) {
         ds[j] = dp[j] - Dj[e];
       }
     }
-    const long long qp0 = a.q_pos0 + qt0;
-    const bool masked = (qt0 + 32 > a.Nq) || (a.causal && kw_last > qp0) ||
-                        (a.causal && a.window > 0 && kw_last >= a.sink && qp0 + 31 - kw_first >= a.window);
-    if (masked) {
+    if (t < tm_lo || t > tm_hi) {
+      const int qt0 = t * 32;
+      const long long relb = a.q_pos0 + qt0 - kpos;     // row r sees this lane's key iff 0 <= relb + r (< window)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int row = (j >> 2) * 8 + hl * 4 + (j & 3);
-        const long long rel = qp0 + row - kpos;
-        const bool vis = (qt0 + row < a.Nq) &&
-                         (!a.causal || (rel >= 0 && (a.window <= 0 || rel < a.window || is_sink)));
+        const long long rel = relb + row;
+        const bool vis = (qt0 + row < a.Nq) && (!a.causal || (rel >= 0 && (!WIN || rel < a.window || is_sink)));
         p[j] = vis ? p[j] : 0.f;
       }
     }
@@ -658,23 +682,26 @@ __global__ void __launch_bounds__(kKVThreads) bwd_dkdv_bf16_kernel(BwdArgs a) {
     mma_tr2(dvacc, lds_off(&sm.o[buf][(hl * 4 + (gj >> 2)) * kTStr + gd]), pb, dkacc,
             lds_off(&sm.q[buf][(hl * 4 + (gj >> 2)) * kTStr + gd]), dsb);
     __syncthreads();
+    if (++ct == t0 + ntq) ct = t0;
+    const int f = bcur;
+    bcur = bnext;
+    bnext = bfree;
+    bfree = f;
   };
   if (nit > 0) {
-    issue(0);
+    issue();
     store(0);
-    if (nit > 1) {
-      issue(1);
-      store(1);
-    }
-    if (nit > 2) issue(2);
+    issue();
+    store(1);
+    issue();
     __syncthreads();
     sdp(0, s_a, dp_a);
     int it = 0;
     for (; it + 1 < nit; it += 2) {
-      step(it, s_a, dp_a, s_b, dp_b);
-      step(it + 1, s_b, dp_b, s_a, dp_a);
+      step(s_a, dp_a, s_b, dp_b);
+      step(s_b, dp_b, s_a, dp_a);
     }
-    if (it < nit) step(it, s_a, dp_a, s_b, dp_b);
+    if (it < nit) step(s_a, dp_a, s_b, dp_b);
   }
   if (!key_ok) return;
   const long long krow = ((long long)b * a.Hkv + hk) * a.Nk + key;
@@ -692,8 +719,8 @@ constexpr int kQWaves = 4;
 constexpr int kQThreads = 64 * kQWaves;
 
 struct DqSmem {
-  __hip_bfloat16 k[2][32 * kTStr];
-  __hip_bfloat16 v[2][32 * kRStr];
+  alignas(16) __hip_bfloat16 k[2][32 * kTStr];
+  alignas(16) __hip_bfloat16 v[2][32 * kRStr];
 };
 
 template <bool HALF, bool WIN>
@@ -899,9 +926,15 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
     const int G = a.Hq / a.Hkv;
     if (!(G == 1 || G == 2 || G % 4 == 0)) return hipErrorInvalidValue;
     const dim3 gkv(a.Hkv, (a.Nk + kKVKeys - 1) / kKVKeys, a.B);
+    const bool win = a.causal && a.window > 0;
     if (a.Nk > 0) {
-      if (half) hipLaunchKernelGGL(bwd_dkdv_bf16_kernel<true>, gkv, dim3(kKVThreads), 0, stream, a);
-      else hipLaunchKernelGGL(bwd_dkdv_bf16_kernel<false>, gkv, dim3(kKVThreads), 0, stream, a);
+      if (win) {
+        if (half) hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<true, true>), gkv, dim3(kKVThreads), 0, stream, a);
+        else hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<false, true>), gkv, dim3(kKVThreads), 0, stream, a);
+      } else {
+        if (half) hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<true, false>), gkv, dim3(kKVThreads), 0, stream, a);
+        else hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<false, false>), gkv, dim3(kKVThreads), 0, stream, a);
+      }
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -909,7 +942,6 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
     const int rows_per_wg = 32 * (kQWaves / HPW);
     const int quads = G > 4 ? G / 4 : 1;
     const dim3 gq(a.Hkv * quads, (a.Nq + rows_per_wg - 1) / rows_per_wg, a.B);
-    const bool win = a.causal && a.window > 0;
     if (win) {
       if (half) hipLaunchKernelGGL((bwd_dq_bf16_kernel<true, true>), gq, dim3(kQThreads), 0, stream, a);
       else hipLaunchKernelGGL((bwd_dq_bf16_kernel<false, true>), gq, dim3(kQThreads), 0, stream, a);
