@@ -547,8 +547,12 @@ __global__ void __launch_bounds__(kKVThreads) bwd_dkdv_bf16_kernel(BwdArgs a) {
   const __hip_bfloat16* kg = reinterpret_cast<const __hip_bfloat16*>(a.k) + ((long long)b * a.Hkv + hk) * a.Nk * kD;
   const __hip_bfloat16* vg = reinterpret_cast<const __hip_bfloat16*>(a.v) + ((long long)b * a.Hkv + hk) * a.Nk * kD;
 
+  // k~ is held pre-multiplied by sm_scale log2(e), so S comes out in log2
+  // units; S starts at -lse log2(e) and dP at -delta (both staged negated), so
+  // P = exp2(S) and dS = P dP
+  const float c2 = a.sm_scale * kLog2e;
   bf16x8 kreg[8], vreg[8];
-  load_row_rotated<HALF>(kg + (long long)key * kD, key_ok, (a.rope_flags & 2) != 0, tab4, kpos, hl, kreg);
+  load_row_rotated<HALF>(kg + (long long)key * kD, key_ok, (a.rope_flags & 2) != 0, tab4, kpos, hl, kreg, c2);
   load_row_rotated<HALF>(vg + (long long)key * kD, key_ok, false, tab4, 0, hl, vreg);
 
   f32x16 dvacc[4], dkacc[4];
@@ -556,7 +560,6 @@ __global__ void __launch_bounds__(kKVThreads) bwd_dkdv_bf16_kernel(BwdArgs a) {
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int j = 0; j < 16; ++j) { dvacc[db][j] = 0.f; dkacc[db][j] = 0.f; }
-  const float c2 = a.sm_scale * kLog2e;
 
   // query rows [r_lo, r_hi) that can see some key of this workgroup
   const int wg_k0 = kblk * kKVKeys;
@@ -606,8 +609,8 @@ __global__ void __launch_bounds__(kKVThreads) bwd_dkdv_bf16_kernel(BwdArgs a) {
     if (tid < 32) {
       const __amdgpu_buffer_rsrc_t rl = raw_buffer(a.lse + hrow, rows * 4);
       const __amdgpu_buffer_rsrc_t rd = raw_buffer(a.delta + hrow, rows * 4);
-      l2v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, tid * 4, 0, 0)) * kLog2e;
-      dlv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, tid * 4, 0, 0));
+      l2v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, tid * 4, 0, 0)) * -kLog2e;
+      dlv = -__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, tid * 4, 0, 0));
     }
     if (++itq == t0 + ntq) {
       itq = t0;
@@ -637,8 +640,16 @@ __global__ void __launch_bounds__(kKVThreads) bwd_dkdv_bf16_kernel(BwdArgs a) {
   // i+1.  Past the last tile the stores fill an unused buffer and the loads,
   // whose range is empty, return zeros.
   auto sdp = [&](int buf, f32x16& s, f32x16& dp) {
-    mma_rows2(lds_off(&sm.q[buf][l32 * kTStr + hl * 8]), kreg, s, lds_off(&sm.o[buf][l32 * kTStr + hl * 8]), vreg,
-              dp);
+    f32x16 cl, cd;     // -lse log2(e) and -delta of the accumulator rows (queries)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const float4 L = *reinterpret_cast<const float4*>(&sm.l2[buf][g4 * 8 + hl * 4]);
+      const float4 Dl = *reinterpret_cast<const float4*>(&sm.dl[buf][g4 * 8 + hl * 4]);
+      cl[g4 * 4 + 0] = L.x; cl[g4 * 4 + 1] = L.y; cl[g4 * 4 + 2] = L.z; cl[g4 * 4 + 3] = L.w;
+      cd[g4 * 4 + 0] = Dl.x; cd[g4 * 4 + 1] = Dl.y; cd[g4 * 4 + 2] = Dl.z; cd[g4 * 4 + 3] = Dl.w;
+    }
+    mma_rows2c(lds_off(&sm.q[buf][l32 * kTStr + hl * 8]), kreg, s, cl, lds_off(&sm.o[buf][l32 * kTStr + hl * 8]),
+               vreg, dp, cd);
   };
   f32x16 s_a, dp_a, s_b, dp_b;
   int bcur = 0, bnext = 1, bfree = 2;      // buffers of tiles i, i+1, i+2
@@ -651,17 +662,7 @@ __global__ void __launch_bounds__(kKVThreads) bwd_dkdv_bf16_kernel(BwdArgs a) {
     const int t = ct;
     float p[16], ds[16];
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const float4 L = *reinterpret_cast<const float4*>(&sm.l2[buf][g4 * 8 + hl * 4]);
-      const float4 Dl = *reinterpret_cast<const float4*>(&sm.dl[buf][g4 * 8 + hl * 4]);
-      const float Lj[4] = {L.x, L.y, L.z, L.w}, Dj[4] = {Dl.x, Dl.y, Dl.z, Dl.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = g4 * 4 + e;
-        p[j] = __builtin_amdgcn_exp2f(fmaf(s[j], c2, -Lj[e]));
-        ds[j] = dp[j] - Dj[e];
-      }
-    }
+    for (int j = 0; j < 16; ++j) p[j] = __builtin_amdgcn_exp2f(s[j]);
     if (t < tm_lo || t > tm_hi) {
       const int qt0 = t * 32;
       const long long relb = a.q_pos0 + qt0 - kpos;     // row r sees this lane's key iff 0 <= relb + r (< window)
@@ -674,7 +675,7 @@ __global__ void __launch_bounds__(kKVThreads) bwd_dkdv_bf16_kernel(BwdArgs a) {
       }
     }
 #pragma unroll
-    for (int j = 0; j < 16; ++j) ds[j] *= p[j];
+    for (int j = 0; j < 16; ++j) ds[j] = p[j] * dp[j];
     bf16x8 pb[2], dsb[2];
     pack16(p, pb);
     pack16(ds, dsb);
