@@ -282,8 +282,12 @@ __global__ void __launch_bounds__(64) bwd_dkdv_f32_kernel(BwdArgs a) {
 // for O^T = V^T P^T.
 
 constexpr int kD = 128;
-constexpr int kTStr = kD + 24;    // 304 B: conflict-free 16-byte row reads and transposing reads
-constexpr int kRStr = kD + 8;     // 272 B: rows read only as 16-byte row chunks
+// Row strides of LDS tiles.  272 B makes the 16-byte row reads conflict-free
+// and 320 B the transposing reads; no stride does both.  Tiles read both ways
+// use 304 B (row reads conflict-free, transposing reads two-way in part):
+// storing such a tile twice, once per stride, measured slower.
+constexpr int kTStr = kD + 24;    // 304 B: tiles read as rows and transposed
+constexpr int kRStr = kD + 8;     // 272 B: tiles read only as 16-byte row chunks
 
 // Load 8 d-chunks of one row (d = ks * 16 + hl * 8 + 0..7) and rotate them
 // (interleaved pairs in-chunk; half-split pairs chunk ks with ks + 4).
