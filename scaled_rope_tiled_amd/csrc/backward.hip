@@ -11,8 +11,10 @@
 //
 // Three launches: delta (HBM-bound), dk/dv (a workgroup owns a block of keys
 // of one KV head and walks the query tiles of every query head of its GQA
-// group that can see them) and dq (a workgroup owns query rows, like the
-// forward kernel, and walks the visible key tiles; two workgroups per CU).
+// group that can see them; half its waves produce P and dV, the other half
+// dS and dK, exchanging P through LDS) and dq (a workgroup owns query rows,
+// like the forward kernel, and walks the visible key tiles; two workgroups
+// per CU).
 // The entry point rotates q and k once into its workspace, so the tiles the
 // kernels stage need no rotation (every key block would otherwise rotate each
 // q tile again, and every query block each k tile).  bf16 kernels (D = 128)
@@ -398,57 +400,11 @@ __device__ inline void mma_tr(f32x16 (&acc)[4], uint32_t x_lane, const bf16x8 (&
 }
 
 
-// acc1 += X1^T B1 and acc2 += X2^T B2 (as mma_tr), the two interleaved with
-// each step's transposing reads issued one step ahead.
-__device__ inline void mma_tr2(f32x16 (&acc1)[4], uint32_t x1, const bf16x8 (&b1)[2], f32x16 (&acc2)[4],
-                               uint32_t x2, const bf16x8 (&b2)[2]) {
-  auto rd = [](uint32_t x, int half, int db) {
-    const i16x4 lo = lds_read_tr(x + ((half * 16) * kTStr + db * 32) * 2);
-    const i16x4 hi = lds_read_tr(x + ((half * 16 + 8) * kTStr + db * 32) * 2);
-    return __builtin_bit_cast(bf16x8, (__attribute__((__vector_size__(8 * sizeof(short)))) short){
-                                          lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-  };
-  bf16x8 a1 = rd(x1, 0, 0), a2 = rd(x2, 0, 0);
-#pragma unroll
-  for (int st = 0; st < 8; ++st) {
-    const int half = st >> 2, db = st & 3;
-    bf16x8 n1 = a1, n2 = a2;
-    if (st < 7) {
-      n1 = rd(x1, (st + 1) >> 2, (st + 1) & 3);
-      n2 = rd(x2, (st + 1) >> 2, (st + 1) & 3);
-    }
-    acc1[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1[half], acc1[db], 0, 0, 0);
-    acc2[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, b2[half], acc2[db], 0, 0, 0);
-    a1 = n1;
-    a2 = n2;
-  }
-}
-
-// acc1 = X1[rows][d] R1[d][cols] and acc2 = X2 R2, X1 and X2 32-row tiles in
-// LDS (16-byte row reads), R1 and R2 in registers; the two independent chains
-// are interleaved and each d-step's LDS operands are read one step ahead, so a
-// pair of MFMAs waits on reads issued a pair earlier instead of each MFMA on
-// its own read.
-__device__ inline void mma_rows2(uint32_t x1, const bf16x8 (&r1)[8], f32x16& acc1, uint32_t x2,
-                                 const bf16x8 (&r2)[8], f32x16& acc2) {
-#pragma unroll
-  for (int j = 0; j < 16; ++j) { acc1[j] = 0.f; acc2[j] = 0.f; }
-  bf16x8 a1 = lds_read16(x1), a2 = lds_read16(x2);
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    bf16x8 n1 = a1, n2 = a2;
-    if (ks < 7) {
-      n1 = lds_read16(x1 + (ks + 1) * 32);
-      n2 = lds_read16(x2 + (ks + 1) * 32);
-    }
-    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, r1[ks], acc1, 0, 0, 0);
-    acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, r2[ks], acc2, 0, 0, 0);
-    a1 = n1;
-    a2 = n2;
-  }
-}
-
-// mma_rows2 with the accumulators starting at c1 and c2 instead of zero.
+// acc1 = c1 + X1[rows][d] R1[d][cols] and acc2 = c2 + X2 R2, X1 and X2 32-row
+// tiles in LDS (16-byte row reads), R1 and R2 in registers; the two
+// independent chains are interleaved and each d-step's LDS operands are read
+// one step ahead, so a pair of MFMAs waits on reads issued a pair earlier
+// instead of each MFMA on its own read.
 __device__ inline void mma_rows2c(uint32_t x1, const bf16x8 (&r1)[8], f32x16& acc1, const f32x16& c1, uint32_t x2,
                                   const bf16x8 (&r2)[8], f32x16& acc2, const f32x16& c2) {
   bf16x8 a1 = lds_read16(x1), a2 = lds_read16(x2);
@@ -463,6 +419,18 @@ __device__ inline void mma_rows2c(uint32_t x1, const bf16x8 (&r1)[8], f32x16& ac
     acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, r2[ks], ks == 0 ? c2 : acc2, 0, 0, 0);
     a1 = n1;
     a2 = n2;
+  }
+}
+
+// acc = c + X[rows][d] R[d][cols], one chain, each d-step's LDS operand read one step ahead.
+__device__ inline void mma_rows1c(uint32_t x, const bf16x8 (&r)[8], f32x16& acc, const f32x16& c) {
+  bf16x8 a = lds_read16(x);
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    bf16x8 n = a;
+    if (ks < 7) n = lds_read16(x + (ks + 1) * 32);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, r[ks], ks == 0 ? c : acc, 0, 0, 0);
+    a = n;
   }
 }
 
@@ -519,51 +487,46 @@ __device__ inline void store_grad(float* dst, f32x16 (&acc)[4], float scale, boo
           make_float4(acc[db][g4 * 4], acc[db][g4 * 4 + 1], acc[db][g4 * 4 + 2], acc[db][g4 * 4 + 3]);
 }
 
-// ---- dk / dv: a workgroup of 4 waves owns 128 keys of one KV head; wave w
-// its 32 keys (rotated k~ and v in registers, the B operands of S = q~ k~^T and
-// dP = dO V^T).  Query tiles of 32 rows (q~, dO, lse, delta) are staged in
-// LDS, triple-buffered, for every query head of the group.
-constexpr int kKVWaves = 4;
-constexpr int kKVThreads = 64 * kKVWaves;
-constexpr int kKVKeys = 32 * kKVWaves;
+constexpr int kKVKeys = 128;    // keys per dk/dv workgroup
 
-struct DkdvSmem {
-  alignas(16) __hip_bfloat16 q[3][32 * kTStr];
-  alignas(16) __hip_bfloat16 o[3][32 * kTStr];
-  float l2[3][32];
-  float dl[3][32];
+// ---- dk / dv with two roles: a workgroup of 8 waves owns 128 keys of one KV
+// head, four groups of 32.  Waves 0-3 ("P waves") hold k~ of their group
+// (pre-multiplied by sm_scale log2(e)) and accumulate dV; waves 4-7 ("dS
+// waves") hold v of the same group and accumulate dK.  Query tile i (32 rows
+// of one head, staged in LDS, four buffers) goes through
+//   P wave,  step i:   S(i+1) = q~ k~^T - lse next to P(i) = exp2(S(i)) (masked),
+//                      P(i) to LDS, dV^T += dO(i)^T P(i)
+//   dS wave, step i:   dP(i) = dO V^T - delta next to dS(i-1) = P(i-1) dP(i-1)
+//                      (P read back from LDS), dK~^T += q~(i-1)^T dS(i-1)
+// so every wave issues 16 MFMAs a step and two waves share each SIMD.
+constexpr int kKV2Waves = 8;
+constexpr int kKV2Threads = 64 * kKV2Waves;
+
+struct Dkdv2Smem {
+  alignas(16) __hip_bfloat16 q[4][32 * kTStr];
+  alignas(16) __hip_bfloat16 o[4][32 * kTStr];
+  alignas(16) float4 p[2][4][4][64];      // [step parity][key group][chunk of 4 floats][lane]
+  alignas(16) float l2[4][32];
+  alignas(16) float dl[4][32];
 };
 
+
 template <bool HALF, bool WIN>
-__global__ void __launch_bounds__(kKVThreads) bwd_dkdv_bf16_kernel(BwdArgs a) {
-  __shared__ DkdvSmem sm;
+__global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) {
+  __shared__ Dkdv2Smem sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave & 3, role = wave >> 2;
   const int l32 = lane & 31, hl = lane >> 5;
   const int hk = blockIdx.x, kblk = blockIdx.y, b = blockIdx.z;
   const int G = a.Hq / a.Hkv;
-  const int wk0 = kblk * kKVKeys + wave * 32;
+  const int wk0 = kblk * kKVKeys + grp * 32;
   const int key = wk0 + l32;
   const bool key_ok = key < a.Nk;
   const long long kpos = a.k_pos0 + key;
   const float4* tab4 = reinterpret_cast<const float4*>(a.table);
   const float2* tab2 = reinterpret_cast<const float2*>(a.table);
-  const __hip_bfloat16* kg = reinterpret_cast<const __hip_bfloat16*>(a.k) + ((long long)b * a.Hkv + hk) * a.Nk * kD;
-  const __hip_bfloat16* vg = reinterpret_cast<const __hip_bfloat16*>(a.v) + ((long long)b * a.Hkv + hk) * a.Nk * kD;
-
-  // k~ is held pre-multiplied by sm_scale log2(e), so S comes out in log2
-  // units; S starts at -lse log2(e) and dP at -delta (both staged negated), so
-  // P = exp2(S) and dS = P dP
   const float c2 = a.sm_scale * kLog2e;
-  bf16x8 kreg[8], vreg[8];
-  load_row_rotated<HALF>(kg + (long long)key * kD, key_ok, (a.rope_flags & 2) != 0, tab4, kpos, hl, kreg, c2);
-  load_row_rotated<HALF>(vg + (long long)key * kD, key_ok, false, tab4, 0, hl, vreg);
-
-  f32x16 dvacc[4], dkacc[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) { dvacc[db][j] = 0.f; dkacc[db][j] = 0.f; }
 
   // query rows [r_lo, r_hi) that can see some key of this workgroup
   const int wg_k0 = kblk * kKVKeys;
@@ -576,45 +539,25 @@ __global__ void __launch_bounds__(kKVThreads) bwd_dkdv_bf16_kernel(BwdArgs a) {
   const int ntq = r_hi > r_lo ? (int)((r_hi + 31) / 32) - t0 : 0;
   const int nit = G * ntq;
 
-  // The wave's keys are all visible to every row of query tile t (no per-score
-  // mask) iff tm_lo <= t <= tm_hi: the tile lies inside the causal triangle
-  // (q_pos0 + 32 t >= last key position), inside Nq and, with a window and
-  // keys that are not all sinks, inside every row's window.
-  const long long kw_first = a.k_pos0 + wk0, kw_last = kw_first + 31;
-  const bool is_sink = kpos < a.sink;
-  auto cdiv = [](long long x, long long y) { return x >= 0 ? (x + y - 1) / y : -((-x) / y); };
-  long long tlo = a.causal ? cdiv(kw_last - a.q_pos0, 32) : 0, thi = a.Nq / 32 - 1;
-  if (WIN && kw_last >= a.sink) thi = min(thi, cdiv(a.window - 31 + kw_first - a.q_pos0, 32) - 1);
-  const int tm_lo = (int)max((long long)INT_MIN, min((long long)INT_MAX, tlo));
-  const int tm_hi = (int)max((long long)INT_MIN, min((long long)INT_MAX, thi));
-
-  // staging: thread t moves 16-byte chunk t & 15 of rows t >> 4 and (t >> 4) + 16
-  // of a q~ and a dO tile (16 threads per 256-byte row) through buffer
-  // descriptors whose range ends at Nq; threads 0..31 move lse and delta
+  // staging: thread t moves 16-byte chunk t & 15 of row t >> 4 of a q~ and a
+  // dO tile through buffer descriptors whose range ends at Nq; threads 0..31
+  // move lse and delta (negated, so they can start the accumulators)
   const __hip_bfloat16* qsrc = reinterpret_cast<const __hip_bfloat16*>(a.q_rot ? a.q_rot : a.q);
   const __hip_bfloat16* dog = reinterpret_cast<const __hip_bfloat16*>(a.dout);
   const int sc = tid & 15, sr = tid >> 4;
   const uint32_t soff = sr * (kD * 2) + sc * 16;
-  uint4 qb[2], ob[2];
+  uint4 qb, ob;
   float l2v = 0.f, dlv = 0.f;
-  // tiles are walked head by head (g), then row tile t = t0 .. t0 + ntq - 1;
-  // (ig, itq) is the next tile to load; past the last one the range is empty
-  int ig = 0, itq = t0;
+  int ig = 0, itq = t0;      // next tile to load: head ig of the group, row tile itq
   auto issue = [&]() {
     const long long hrow = ((long long)b * a.Hq + hk * G + ig) * a.Nq + (long long)itq * 32;
     const int rows = ig < G ? min(32, max(0, a.Nq - itq * 32)) : 0;
-    const __amdgpu_buffer_rsrc_t rq = raw_buffer(qsrc + hrow * kD, rows * (kD * 2));
-    const __amdgpu_buffer_rsrc_t ro = raw_buffer(dog + hrow * kD, rows * (kD * 2));
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      qb[i] = buffer_ld16(rq, soff + i * 16 * (kD * 2));
-      ob[i] = buffer_ld16(ro, soff + i * 16 * (kD * 2));
-    }
+    qb = buffer_ld16(raw_buffer(qsrc + hrow * kD, rows * (kD * 2)), soff);
+    ob = buffer_ld16(raw_buffer(dog + hrow * kD, rows * (kD * 2)), soff);
     if (tid < 32) {
-      const __amdgpu_buffer_rsrc_t rl = raw_buffer(a.lse + hrow, rows * 4);
-      const __amdgpu_buffer_rsrc_t rd = raw_buffer(a.delta + hrow, rows * 4);
-      l2v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, tid * 4, 0, 0)) * -kLog2e;
-      dlv = -__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, tid * 4, 0, 0));
+      l2v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(raw_buffer(a.lse + hrow, rows * 4), tid * 4, 0, 0)) *
+            -kLog2e;
+      dlv = -__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(raw_buffer(a.delta + hrow, rows * 4), tid * 4, 0, 0));
     }
     if (++itq == t0 + ntq) {
       itq = t0;
@@ -622,77 +565,40 @@ __global__ void __launch_bounds__(kKVThreads) bwd_dkdv_bf16_kernel(BwdArgs a) {
     }
   };
   auto store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      *reinterpret_cast<uint4*>(&sm.q[buf][(sr + 16 * i) * kTStr + sc * 8]) = qb[i];
-      *reinterpret_cast<uint4*>(&sm.o[buf][(sr + 16 * i) * kTStr + sc * 8]) = ob[i];
-    }
+    *reinterpret_cast<uint4*>(&sm.q[buf][sr * kTStr + sc * 8]) = qb;
+    *reinterpret_cast<uint4*>(&sm.o[buf][sr * kTStr + sc * 8]) = ob;
     if (tid < 32) {
       sm.l2[buf][tid] = l2v;
       sm.dl[buf][tid] = dlv;
     }
   };
+  auto init_rows = [&](const float* src) {     // the 16 accumulator rows (queries) of this lane
+    f32x16 c;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const float4 x = *reinterpret_cast<const float4*>(&src[g4 * 8 + hl * 4]);
+      c[g4 * 4 + 0] = x.x; c[g4 * 4 + 1] = x.y; c[g4 * 4 + 2] = x.z; c[g4 * 4 + 3] = x.w;
+    }
+    return c;
+  };
 
   const int gj = lane & 15;
   const int gd = ((lane >> 4) & 1) * 16 + 4 * (gj & 3);
-  // Software pipeline over the query tiles: step i issues S and dP of tile
-  // i+1 (matrix work that depends on nothing pending) next to the softmax of
-  // tile i, then dV and dK of tile i.  Tile i sits in LDS buffer i % 3: tile
-  // i+2 is stored at the start of step i into the buffer tile i-1 used (every
-  // wave finished step i-1 at the barrier closing it) from registers loaded
-  // one step earlier, and the barrier closing step i publishes it for step
-  // i+1.  Past the last tile the stores fill an unused buffer and the loads,
-  // whose range is empty, return zeros.
-  auto sdp = [&](int buf, f32x16& s, f32x16& dp) {
-    f32x16 cl, cd;     // -lse log2(e) and -delta of the accumulator rows (queries)
+  const int tr_off = (hl * 4 + (gj >> 2)) * kTStr + gd;
+  bf16x8 breg[8];            // P waves: k~ (scaled); dS waves: v
+  f32x16 acc[4];             // P waves: dV^T; dS waves: dK~^T
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const float4 L = *reinterpret_cast<const float4*>(&sm.l2[buf][g4 * 8 + hl * 4]);
-      const float4 Dl = *reinterpret_cast<const float4*>(&sm.dl[buf][g4 * 8 + hl * 4]);
-      cl[g4 * 4 + 0] = L.x; cl[g4 * 4 + 1] = L.y; cl[g4 * 4 + 2] = L.z; cl[g4 * 4 + 3] = L.w;
-      cd[g4 * 4 + 0] = Dl.x; cd[g4 * 4 + 1] = Dl.y; cd[g4 * 4 + 2] = Dl.z; cd[g4 * 4 + 3] = Dl.w;
-    }
-    mma_rows2c(lds_off(&sm.q[buf][l32 * kTStr + hl * 8]), kreg, s, cl, lds_off(&sm.o[buf][l32 * kTStr + hl * 8]),
-               vreg, dp, cd);
-  };
-  f32x16 s_a, dp_a, s_b, dp_b;
-  int bcur = 0, bnext = 1, bfree = 2;      // buffers of tiles i, i+1, i+2
-  int ct = t0;                             // row tile of the current step
-  auto step = [&](f32x16& s, f32x16& dp, f32x16& s_nx, f32x16& dp_nx) {
-    const int buf = bcur;
-    store(bfree);
-    issue();
-    sdp(bnext, s_nx, dp_nx);     // past the last tile: stale buffer, result unused
-    const int t = ct;
-    float p[16], ds[16];
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) p[j] = __builtin_amdgcn_exp2f(s[j]);
-    if (t < tm_lo || t > tm_hi) {
-      const int qt0 = t * 32;
-      const long long relb = a.q_pos0 + qt0 - kpos;     // row r sees this lane's key iff 0 <= relb + r (< window)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int row = (j >> 2) * 8 + hl * 4 + (j & 3);
-        const long long rel = relb + row;
-        const bool vis = (qt0 + row < a.Nq) && (!a.causal || (rel >= 0 && (!WIN || rel < a.window || is_sink)));
-        p[j] = vis ? p[j] : 0.f;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) ds[j] = p[j] * dp[j];
-    bf16x8 pb[2], dsb[2];
-    pack16(p, pb);
-    pack16(ds, dsb);
-    // dV^T += dO^T P and dK~^T += q~^T dS (transposing reads of the row-major tiles)
-    mma_tr2(dvacc, lds_off(&sm.o[buf][(hl * 4 + (gj >> 2)) * kTStr + gd]), pb, dkacc,
-            lds_off(&sm.q[buf][(hl * 4 + (gj >> 2)) * kTStr + gd]), dsb);
-    __syncthreads();
-    if (++ct == t0 + ntq) ct = t0;
-    const int f = bcur;
-    bcur = bnext;
-    bnext = bfree;
-    bfree = f;
-  };
+    for (int j = 0; j < 16; ++j) acc[db][j] = 0.f;
+  if (role == 0) {
+    const __hip_bfloat16* kg = reinterpret_cast<const __hip_bfloat16*>(a.k) + ((long long)b * a.Hkv + hk) * a.Nk * kD;
+    load_row_rotated<HALF>(kg + (long long)key * kD, key_ok, (a.rope_flags & 2) != 0, tab4, kpos, hl, breg, c2);
+  } else {
+    const __hip_bfloat16* vg = reinterpret_cast<const __hip_bfloat16*>(a.v) + ((long long)b * a.Hkv + hk) * a.Nk * kD;
+    load_row_rotated<HALF>(vg + (long long)key * kD, key_ok, false, tab4, 0, hl, breg);
+  }
+
   if (nit > 0) {
     issue();
     store(0);
@@ -700,18 +606,85 @@ __global__ void __launch_bounds__(kKVThreads) bwd_dkdv_bf16_kernel(BwdArgs a) {
     store(1);
     issue();
     __syncthreads();
-    sdp(0, s_a, dp_a);
-    int it = 0;
-    for (; it + 1 < nit; it += 2) {
-      step(s_a, dp_a, s_b, dp_b);
-      step(s_b, dp_b, s_a, dp_a);
+    if (role == 0) {
+      // the wave's keys are all visible to every row of row tile t iff tm_lo <= t <= tm_hi
+      const long long kw_first = a.k_pos0 + wk0, kw_last = kw_first + 31;
+      const bool is_sink = kpos < a.sink;
+      auto cdiv = [](long long x, long long y) { return x >= 0 ? (x + y - 1) / y : -((-x) / y); };
+      long long tlo = a.causal ? cdiv(kw_last - a.q_pos0, 32) : 0, thi = a.Nq / 32 - 1;
+      if (WIN && kw_last >= a.sink) thi = min(thi, cdiv(a.window - 31 + kw_first - a.q_pos0, 32) - 1);
+      const int tm_lo = (int)max((long long)INT_MIN, min((long long)INT_MAX, tlo));
+      const int tm_hi = (int)max((long long)INT_MIN, min((long long)INT_MAX, thi));
+      f32x16 s_cur, s_nx;
+      mma_rows1c(lds_off(&sm.q[0][l32 * kTStr + hl * 8]), breg, s_cur, init_rows(sm.l2[0]));
+      int ct = t0;
+      for (int i = 0; i <= nit; ++i) {
+        store((i + 2) & 3);
+        issue();
+        if (i < nit) {
+          const int nb = (i + 1) & 3, cb = i & 3;
+          mma_rows1c(lds_off(&sm.q[nb][l32 * kTStr + hl * 8]), breg, s_nx, init_rows(sm.l2[nb]));   // stale past the end
+          float p[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) p[j] = __builtin_amdgcn_exp2f(s_cur[j]);
+          if (ct < tm_lo || ct > tm_hi) {
+            const int qt0 = ct * 32;
+            const long long relb = a.q_pos0 + qt0 - kpos;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const int row = (j >> 2) * 8 + hl * 4 + (j & 3);
+              const long long rel = relb + row;
+              const bool vis =
+                  (qt0 + row < a.Nq) && (!a.causal || (rel >= 0 && (!WIN || rel < a.window || is_sink)));
+              p[j] = vis ? p[j] : 0.f;
+            }
+          }
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            sm.p[i & 1][grp][c][lane] = make_float4(p[4 * c], p[4 * c + 1], p[4 * c + 2], p[4 * c + 3]);
+          bf16x8 pb[2];
+          pack16(p, pb);
+          // dV^T += dO^T P (transposing reads of the row-major dO tile)
+          mma_tr(acc, lds_off(&sm.o[cb][tr_off]), pb);
+          s_cur = s_nx;
+          if (++ct == t0 + ntq) ct = t0;
+        }
+        __syncthreads();
+      }
+    } else {
+      f32x16 dp_cur, dp_nx;
+      for (int i = 0; i <= nit; ++i) {
+        store((i + 2) & 3);
+        issue();
+        if (i < nit) {
+          const int cb = i & 3;
+          mma_rows1c(lds_off(&sm.o[cb][l32 * kTStr + hl * 8]), breg, dp_nx, init_rows(sm.dl[cb]));
+        }
+        if (i > 0) {
+          const int pb_ = (i - 1) & 3;
+          float ds[16];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float4 pv = sm.p[(i - 1) & 1][grp][c][lane];
+            ds[4 * c] = pv.x * dp_cur[4 * c];
+            ds[4 * c + 1] = pv.y * dp_cur[4 * c + 1];
+            ds[4 * c + 2] = pv.z * dp_cur[4 * c + 2];
+            ds[4 * c + 3] = pv.w * dp_cur[4 * c + 3];
+          }
+          bf16x8 dsb[2];
+          pack16(ds, dsb);
+          // dK~^T += q~^T dS (transposing reads of the row-major q~ tile)
+          mma_tr(acc, lds_off(&sm.q[pb_][tr_off]), dsb);
+        }
+        dp_cur = dp_nx;
+        __syncthreads();
+      }
     }
-    if (it < nit) step(s_a, dp_a, s_b, dp_b);
   }
   if (!key_ok) return;
   const long long krow = ((long long)b * a.Hkv + hk) * a.Nk + key;
-  store_grad<HALF>(a.dv + krow * kD, dvacc, 1.f, false, tab2, kpos, hl);
-  store_grad<HALF>(a.dk + krow * kD, dkacc, a.sm_scale, (a.rope_flags & 2) != 0, tab2, kpos, hl);
+  if (role == 0) store_grad<HALF>(a.dv + krow * kD, acc, 1.f, false, tab2, kpos, hl);
+  else store_grad<HALF>(a.dk + krow * kD, acc, a.sm_scale, (a.rope_flags & 2) != 0, tab2, kpos, hl);
 }
 
 // ---- dq: a workgroup of 4 waves owns one KV head and 32 * (4 / HPW) query
@@ -934,11 +907,11 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
     const bool win = a.causal && a.window > 0;
     if (a.Nk > 0) {
       if (win) {
-        if (half) hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<true, true>), gkv, dim3(kKVThreads), 0, stream, a);
-        else hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<false, true>), gkv, dim3(kKVThreads), 0, stream, a);
+        if (half) hipLaunchKernelGGL((bwd_dkdv2_bf16_kernel<true, true>), gkv, dim3(kKV2Threads), 0, stream, a);
+        else hipLaunchKernelGGL((bwd_dkdv2_bf16_kernel<false, true>), gkv, dim3(kKV2Threads), 0, stream, a);
       } else {
-        if (half) hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<true, false>), gkv, dim3(kKVThreads), 0, stream, a);
-        else hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<false, false>), gkv, dim3(kKVThreads), 0, stream, a);
+        if (half) hipLaunchKernelGGL((bwd_dkdv2_bf16_kernel<true, false>), gkv, dim3(kKV2Threads), 0, stream, a);
+        else hipLaunchKernelGGL((bwd_dkdv2_bf16_kernel<false, false>), gkv, dim3(kKV2Threads), 0, stream, a);
       }
       e = hipGetLastError();
       if (e != hipSuccess) return e;
