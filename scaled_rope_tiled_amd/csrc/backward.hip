@@ -606,6 +606,13 @@ __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) 
     store(1);
     issue();
     __syncthreads();
+    // Step i uses LDS buffers (i + 2) % 4 (staging), (i + 1) % 4, i % 4 and
+    // (i - 1) % 4 and P slot i % 2: four steps per trip keep them compile-time
+    // constants and let S / dP alternate between two register sets.
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using C2 = std::integral_constant<int, 2>;
+    using C3 = std::integral_constant<int, 3>;
     if (role == 0) {
       // the wave's keys are all visible to every row of row tile t iff tm_lo <= t <= tm_hi
       const long long kw_first = a.k_pos0 + wk0, kw_last = kw_first + 31;
@@ -615,70 +622,94 @@ __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) 
       if (WIN && kw_last >= a.sink) thi = min(thi, cdiv(a.window - 31 + kw_first - a.q_pos0, 32) - 1);
       const int tm_lo = (int)max((long long)INT_MIN, min((long long)INT_MAX, tlo));
       const int tm_hi = (int)max((long long)INT_MIN, min((long long)INT_MAX, thi));
-      f32x16 s_cur, s_nx;
-      mma_rows1c(lds_off(&sm.q[0][l32 * kTStr + hl * 8]), breg, s_cur, init_rows(sm.l2[0]));
+      f32x16 s_a, s_b;
+      mma_rows1c(lds_off(&sm.q[0][l32 * kTStr + hl * 8]), breg, s_a, init_rows(sm.l2[0]));
       int ct = t0;
-      for (int i = 0; i <= nit; ++i) {
-        store((i + 2) & 3);
+      // step i = R (mod 4) on tile i: S(i+1) into s_out next to P(i) from s_in
+      auto pstep = [&](auto rc, const f32x16& s_in, f32x16& s_out) {
+        constexpr int R = decltype(rc)::value;
+        constexpr int nb = (R + 1) & 3;
+        store((R + 2) & 3);
         issue();
-        if (i < nit) {
-          const int nb = (i + 1) & 3, cb = i & 3;
-          mma_rows1c(lds_off(&sm.q[nb][l32 * kTStr + hl * 8]), breg, s_nx, init_rows(sm.l2[nb]));   // stale past the end
-          float p[16];
+        mma_rows1c(lds_off(&sm.q[nb][l32 * kTStr + hl * 8]), breg, s_out, init_rows(sm.l2[nb]));   // stale past the end
+        float p[16];
 #pragma unroll
-          for (int j = 0; j < 16; ++j) p[j] = __builtin_amdgcn_exp2f(s_cur[j]);
-          if (ct < tm_lo || ct > tm_hi) {
-            const int qt0 = ct * 32;
-            const long long relb = a.q_pos0 + qt0 - kpos;
+        for (int j = 0; j < 16; ++j) p[j] = __builtin_amdgcn_exp2f(s_in[j]);
+        if (ct < tm_lo || ct > tm_hi) {
+          const int qt0 = ct * 32;
+          const long long relb = a.q_pos0 + qt0 - kpos;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-              const int row = (j >> 2) * 8 + hl * 4 + (j & 3);
-              const long long rel = relb + row;
-              const bool vis =
-                  (qt0 + row < a.Nq) && (!a.causal || (rel >= 0 && (!WIN || rel < a.window || is_sink)));
-              p[j] = vis ? p[j] : 0.f;
-            }
+          for (int j = 0; j < 16; ++j) {
+            const int row = (j >> 2) * 8 + hl * 4 + (j & 3);
+            const long long rel = relb + row;
+            const bool vis = (qt0 + row < a.Nq) && (!a.causal || (rel >= 0 && (!WIN || rel < a.window || is_sink)));
+            p[j] = vis ? p[j] : 0.f;
           }
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            sm.p[i & 1][grp][c][lane] = make_float4(p[4 * c], p[4 * c + 1], p[4 * c + 2], p[4 * c + 3]);
-          bf16x8 pb[2];
-          pack16(p, pb);
-          // dV^T += dO^T P (transposing reads of the row-major dO tile)
-          mma_tr(acc, lds_off(&sm.o[cb][tr_off]), pb);
-          s_cur = s_nx;
-          if (++ct == t0 + ntq) ct = t0;
         }
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          sm.p[R & 1][grp][c][lane] = make_float4(p[4 * c], p[4 * c + 1], p[4 * c + 2], p[4 * c + 3]);
+        bf16x8 pb[2];
+        pack16(p, pb);
+        // dV^T += dO^T P (transposing reads of the row-major dO tile)
+        mma_tr(acc, lds_off(&sm.o[R][tr_off]), pb);
+        if (++ct == t0 + ntq) ct = t0;
         __syncthreads();
+      };
+      int i = 0;
+      for (; i + 4 <= nit; i += 4) {
+        pstep(C0{}, s_a, s_b);
+        pstep(C1{}, s_b, s_a);
+        pstep(C2{}, s_a, s_b);
+        pstep(C3{}, s_b, s_a);
       }
+      if (i < nit) pstep(C0{}, s_a, s_b), ++i;
+      if (i < nit) pstep(C1{}, s_b, s_a), ++i;
+      if (i < nit) pstep(C2{}, s_a, s_b), ++i;
+      // step nit: the dS waves' last step; only the staging and the barrier
+      store((nit + 2) & 3);
+      issue();
+      __syncthreads();
     } else {
-      f32x16 dp_cur, dp_nx;
-      for (int i = 0; i <= nit; ++i) {
-        store((i + 2) & 3);
+      f32x16 dp_a, dp_b;
+      // step i = R (mod 4): dP(i) into dp_out (when i < nit) next to dS(i-1) from dp_in
+      auto dstep = [&](auto rc, const f32x16& dp_in, f32x16& dp_out, bool dp_active) {
+        constexpr int R = decltype(rc)::value;
+        store((R + 2) & 3);
         issue();
-        if (i < nit) {
-          const int cb = i & 3;
-          mma_rows1c(lds_off(&sm.o[cb][l32 * kTStr + hl * 8]), breg, dp_nx, init_rows(sm.dl[cb]));
-        }
-        if (i > 0) {
-          const int pb_ = (i - 1) & 3;
-          float ds[16];
+        if (dp_active) mma_rows1c(lds_off(&sm.o[R][l32 * kTStr + hl * 8]), breg, dp_out, init_rows(sm.dl[R]));
+        float ds[16];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const float4 pv = sm.p[(i - 1) & 1][grp][c][lane];
-            ds[4 * c] = pv.x * dp_cur[4 * c];
-            ds[4 * c + 1] = pv.y * dp_cur[4 * c + 1];
-            ds[4 * c + 2] = pv.z * dp_cur[4 * c + 2];
-            ds[4 * c + 3] = pv.w * dp_cur[4 * c + 3];
-          }
-          bf16x8 dsb[2];
-          pack16(ds, dsb);
-          // dK~^T += q~^T dS (transposing reads of the row-major q~ tile)
-          mma_tr(acc, lds_off(&sm.q[pb_][tr_off]), dsb);
+        for (int c = 0; c < 4; ++c) {
+          const float4 pv = sm.p[(R + 1) & 1][grp][c][lane];
+          ds[4 * c] = pv.x * dp_in[4 * c];
+          ds[4 * c + 1] = pv.y * dp_in[4 * c + 1];
+          ds[4 * c + 2] = pv.z * dp_in[4 * c + 2];
+          ds[4 * c + 3] = pv.w * dp_in[4 * c + 3];
         }
-        dp_cur = dp_nx;
+        bf16x8 dsb[2];
+        pack16(ds, dsb);
+        // dK~^T += q~^T dS (transposing reads of the row-major q~ tile)
+        mma_tr(acc, lds_off(&sm.q[(R + 3) & 3][tr_off]), dsb);
         __syncthreads();
+      };
+      // step 0: dP(0) only
+      store(2);
+      issue();
+      mma_rows1c(lds_off(&sm.o[0][l32 * kTStr + hl * 8]), breg, dp_a, init_rows(sm.dl[0]));
+      __syncthreads();
+      int i = 1;
+      for (; i + 3 < nit; i += 4) {
+        dstep(C1{}, dp_a, dp_b, true);
+        dstep(C2{}, dp_b, dp_a, true);
+        dstep(C3{}, dp_a, dp_b, true);
+        dstep(C0{}, dp_b, dp_a, true);
       }
+      // steps i .. nit (at most four; the last one has no new dP)
+      if (i <= nit) dstep(C1{}, dp_a, dp_b, i < nit), ++i;
+      if (i <= nit) dstep(C2{}, dp_b, dp_a, i < nit), ++i;
+      if (i <= nit) dstep(C3{}, dp_a, dp_b, i < nit), ++i;
+      if (i <= nit) dstep(C0{}, dp_b, dp_a, i < nit), ++i;
     }
   }
   if (!key_ok) return;
