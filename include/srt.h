@@ -248,10 +248,12 @@ int srt_attn_decode_splitk(const void* q, const void* k_cache, const void* v_cac
 /*
  * srt_attn_backward_workspace_size - bytes of workspace srt_attn_backward
  * needs for these arguments: delta = rowsum(dO * O), fp32 [B][Hq][Nq], and
- * for BF16 a rotated copy of q ([B][Hq][Nq][D], with SRT_ROTATE_Q) and of k
- * ([B][Hkv][Nk][D], with SRT_ROTATE_K), each region 256-byte aligned.  The
- * rotated copies are made once per call, so the kernels stage tiles that need
- * no rotation.  Returns SRT_ERR_INVALID for a bad dtype, negative sizes or
+ * for BF16 a copy of q ([B][Hq][Nq][D], rotated with SRT_ROTATE_Q, always
+ * multiplied by sm_scale log2(e) and rounded once exactly as the forward
+ * kernel forms its q, so the recomputed scores equal the forward's) and a
+ * rotated copy of k ([B][Hkv][Nk][D], with SRT_ROTATE_K), each region 256-byte
+ * aligned.  The copies are made once per call, so the kernels stage tiles that
+ * need no rotation.  Returns SRT_ERR_INVALID for a bad dtype, negative sizes or
  * unknown flags.
  */
 int srt_attn_backward_workspace_size(int dtype, int B, int Hq, int Hkv, int Nq, int Nk, int D, int rope_flags,

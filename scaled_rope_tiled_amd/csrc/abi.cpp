@@ -299,7 +299,8 @@ int srt_attn_decode_splitk(const void* q, const void* k_cache, const void* v_cac
 }
 
 namespace {
-// Backward workspace: delta, then the rotated q and k copies (bf16 only), each 256-byte aligned.
+// Backward workspace: delta, then (bf16 only) the scaled, rotated q copy and the rotated k copy, each 256-byte
+// aligned.
 struct BwdWorkspace {
   size_t delta, q_rot, k_rot, total;   // offsets of the regions (q_rot / k_rot: 0 when absent) and the size
 };
@@ -307,7 +308,7 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 BwdWorkspace bwd_workspace(int dtype, int B, int Hq, int Hkv, int Nq, int Nk, int D, int rope_flags) {
   BwdWorkspace w{0, 0, 0, 0};
   size_t off = round256((size_t)B * Hq * Nq * sizeof(float));
-  if (dtype == SRT_BF16 && (rope_flags & SRT_ROTATE_Q) && (size_t)B * Nq > 0) {
+  if (dtype == SRT_BF16 && (size_t)B * Nq > 0) {
     w.q_rot = off;
     off += round256((size_t)B * Hq * Nq * D * 2);
   }
@@ -376,10 +377,14 @@ int srt_attn_backward(const void* q, const void* k, const void* v, const void* o
   // rotate q and k once into the workspace ([LC] §2.4: each row by its own position)
   const bool half_pairs = (rope_flags & SRT_PAIR_HALF) != 0;
   if (ws.q_rot) {
+    // q~ = bf16(rotated q * sm_scale log2(e)), rounded once exactly as the forward kernel forms it, so the
+    // backward's scores (and P = exp2(S - lse)) are those the forward normalised
     void* qr = (char*)workspace + ws.q_rot;
     const srt::PosMap map{q_pos0, srt::kContiguous, 1, Nq};
-    const hipError_t e = srt::launch_rope_apply(q, qr, true, half_pairs, (long long)B * Hq, Nq, D, map, table_dev,
-                                                (hipStream_t)stream);
+    const bool rot_q = (rope_flags & SRT_ROTATE_Q) != 0;
+    const hipError_t e = srt::launch_rope_apply(q, qr, true, half_pairs && rot_q, (long long)B * Hq, Nq, D, map,
+                                                rot_q ? table_dev : nullptr, (hipStream_t)stream,
+                                                sm_scale * 1.44269504f);   // fp32 product, as the kernel forms it
     if (e != hipSuccess) return hip_status(e, "attn_backward: rotating q");
     a.q_rot = qr;
   }

@@ -29,6 +29,7 @@ namespace {
 using namespace mc;
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ inline void load8f(const void* base, long long idx8, bool bf16, float v[8]) {
   if (bf16) {
@@ -490,10 +491,14 @@ __device__ inline void store_grad(float* dst, f32x16 (&acc)[4], float scale, boo
 constexpr int kKVKeys = 128;    // keys per dk/dv workgroup
 
 // ---- dk / dv with two roles: a workgroup of 8 waves owns 128 keys of one KV
-// head, four groups of 32.  Waves 0-3 ("P waves") hold k~ of their group
-// (pre-multiplied by sm_scale log2(e)) and accumulate dV; waves 4-7 ("dS
-// waves") hold v of the same group and accumulate dK.  Query tile i (32 rows
-// of one head, staged in LDS, four buffers) goes through
+// head, four groups of 32.  Waves 0-3 ("P waves") hold k~ of their group and
+// accumulate dV; waves 4-7 ("dS waves") hold v of the same group and
+// accumulate dK.  The q~ tiles come from the entry point's copy of q, rotated
+// and multiplied by sm_scale log2(e) with the one rounding the forward kernel
+// applies, so S is the forward's score in log2 units and P = exp2(S - lse
+// log2(e)) is the very softmax the forward normalised; dK~ = sm_scale dS^T q~
+// then takes the factor ln 2.  Query tile i (32 rows of one head, staged in
+// LDS, four buffers) goes through
 //   P wave,  step i:   S(i+1) = q~ k~^T - lse next to P(i) = exp2(S(i)) (masked),
 //                      P(i) to LDS, dV^T += dO(i)^T P(i)
 //   dS wave, step i:   dP(i) = dO V^T - delta next to dS(i-1) = P(i-1) dP(i-1)
@@ -526,7 +531,6 @@ __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) 
   const long long kpos = a.k_pos0 + key;
   const float4* tab4 = reinterpret_cast<const float4*>(a.table);
   const float2* tab2 = reinterpret_cast<const float2*>(a.table);
-  const float c2 = a.sm_scale * kLog2e;
 
   // query rows [r_lo, r_hi) that can see some key of this workgroup
   const int wg_k0 = kblk * kKVKeys;
@@ -542,7 +546,7 @@ __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) 
   // staging: thread t moves 16-byte chunk t & 15 of row t >> 4 of a q~ and a
   // dO tile through buffer descriptors whose range ends at Nq; threads 0..31
   // move lse and delta (negated, so they can start the accumulators)
-  const __hip_bfloat16* qsrc = reinterpret_cast<const __hip_bfloat16*>(a.q_rot ? a.q_rot : a.q);
+  const __hip_bfloat16* qsrc = reinterpret_cast<const __hip_bfloat16*>(a.q_rot);
   const __hip_bfloat16* dog = reinterpret_cast<const __hip_bfloat16*>(a.dout);
   const int sc = tid & 15, sr = tid >> 4;
   const uint32_t soff = sr * (kD * 2) + sc * 16;
@@ -593,7 +597,7 @@ __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) 
     for (int j = 0; j < 16; ++j) acc[db][j] = 0.f;
   if (role == 0) {
     const __hip_bfloat16* kg = reinterpret_cast<const __hip_bfloat16*>(a.k) + ((long long)b * a.Hkv + hk) * a.Nk * kD;
-    load_row_rotated<HALF>(kg + (long long)key * kD, key_ok, (a.rope_flags & 2) != 0, tab4, kpos, hl, breg, c2);
+    load_row_rotated<HALF>(kg + (long long)key * kD, key_ok, (a.rope_flags & 2) != 0, tab4, kpos, hl, breg);
   } else {
     const __hip_bfloat16* vg = reinterpret_cast<const __hip_bfloat16*>(a.v) + ((long long)b * a.Hkv + hk) * a.Nk * kD;
     load_row_rotated<HALF>(vg + (long long)key * kD, key_ok, false, tab4, 0, hl, breg);
@@ -715,7 +719,7 @@ __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) 
   if (!key_ok) return;
   const long long krow = ((long long)b * a.Hkv + hk) * a.Nk + key;
   if (role == 0) store_grad<HALF>(a.dv + krow * kD, acc, 1.f, false, tab2, kpos, hl);
-  else store_grad<HALF>(a.dk + krow * kD, acc, a.sm_scale, (a.rope_flags & 2) != 0, tab2, kpos, hl);
+  else store_grad<HALF>(a.dk + krow * kD, acc, kLn2, (a.rope_flags & 2) != 0, tab2, kpos, hl);
 }
 
 // ---- dq: a workgroup of 4 waves owns one KV head and 32 * (4 / HPW) query

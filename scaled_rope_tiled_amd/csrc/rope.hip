@@ -50,10 +50,12 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
 }
 
 // One thread = 8 consecutive elements of one row = 4 pairs.
+// With a null table the rotation is the identity.  Every output is
+// multiplied by `scale` (through the table entries, one rounding to bf16).
 template <bool BF16>
 __global__ void __launch_bounds__(256) rope_apply_kernel(const void* __restrict__ x, void* y, long long groups,
                                                          int N, int D, PosMap map,
-                                                         const float4* __restrict__ table) {
+                                                         const float4* __restrict__ table, float scale) {
   const int vec_per_row = D / 8;
   const long long total = groups * (long long)N * vec_per_row;
   for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total;
@@ -62,10 +64,14 @@ __global__ void __launch_bounds__(256) rope_apply_kernel(const void* __restrict_
     const int j = (int)(e - row * vec_per_row);        // which 8-element chunk of the row
     const long long p = row_pos(map, row % N);
     // table row p, pairs 4j .. 4j+3 = two float4 of (cos, sin, cos, sin)
-    const float4* trow = table + (p * (D / 2) + 4 * j) / 2;
-    const float4 t0 = trow[0], t1 = trow[1];
-    const float c[4] = {t0.x, t0.z, t1.x, t1.z};
-    const float s[4] = {t0.y, t0.w, t1.y, t1.w};
+    float4 t0 = make_float4(1.f, 0.f, 1.f, 0.f), t1 = t0;
+    if (table) {
+      const float4* trow = table + (p * (D / 2) + 4 * j) / 2;
+      t0 = trow[0];
+      t1 = trow[1];
+    }
+    const float c[4] = {t0.x * scale, t0.z * scale, t1.x * scale, t1.z * scale};
+    const float s[4] = {t0.y * scale, t0.w * scale, t1.y * scale, t1.w * scale};
     float v[8];
     if (BF16) {
       const uint4 w = reinterpret_cast<const uint4*>(x)[e];
@@ -126,7 +132,7 @@ __device__ inline void store8(void* base, long long idx8, bool bf16, const float
 template <bool BF16>
 __global__ void __launch_bounds__(256) rope_apply_half_kernel(const void* __restrict__ x, void* y, long long groups,
                                                               int N, int D, PosMap map,
-                                                              const float4* __restrict__ table) {
+                                                              const float4* __restrict__ table, float scale) {
   const int per_row = D / 16;
   const long long total = groups * (long long)N * per_row;
   for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total;
@@ -141,7 +147,8 @@ __global__ void __launch_bounds__(256) rope_apply_half_kernel(const void* __rest
     load8(x, i2, BF16, b);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float4 t = trow[q];
+      const float4 tq = trow[q];
+      const float4 t = make_float4(tq.x * scale, tq.y * scale, tq.z * scale, tq.w * scale);
       // pairs 2q and 2q+1 of this thread: (cos, sin) = (t.x, t.y), (t.z, t.w)
       o1[2 * q] = a[2 * q] * t.x - b[2 * q] * t.y;
       o2[2 * q] = a[2 * q] * t.y + b[2 * q] * t.x;
@@ -170,25 +177,25 @@ hipError_t launch_rope_table(const Theta& th, int half, double mscale, long long
 }
 
 hipError_t launch_rope_apply(const void* x, void* y, bool bf16, bool half_pairs, long long groups, int N, int D,
-                             const PosMap& map, const float* table, hipStream_t stream) {
+                             const PosMap& map, const float* table, hipStream_t stream, float scale) {
   const float4* t = reinterpret_cast<const float4*>(table);
-  if (half_pairs) {
+  if (half_pairs && table) {
     const long long work = groups * (long long)N * (D / 16);
     if (bf16)
       hipLaunchKernelGGL(rope_apply_half_kernel<true>, dim3(grid_for(work, 256)), dim3(256), 0, stream, x, y, groups,
-                         N, D, map, t);
+                         N, D, map, t, scale);
     else
       hipLaunchKernelGGL(rope_apply_half_kernel<false>, dim3(grid_for(work, 256)), dim3(256), 0, stream, x, y,
-                         groups, N, D, map, t);
+                         groups, N, D, map, t, scale);
     return hipGetLastError();
   }
   const long long work = groups * (long long)N * (D / 8);
   if (bf16)
     hipLaunchKernelGGL(rope_apply_kernel<true>, dim3(grid_for(work, 256)), dim3(256), 0, stream, x, y, groups, N,
-                       D, map, t);
+                       D, map, t, scale);
   else
     hipLaunchKernelGGL(rope_apply_kernel<false>, dim3(grid_for(work, 256)), dim3(256), 0, stream, x, y, groups,
-                       N, D, map, t);
+                       N, D, map, t, scale);
   return hipGetLastError();
 }
 

@@ -30,8 +30,9 @@ struct PosMap {
 };
 
 // rows = B*H rows-groups of N rows each; row n of a group sits at position map(n).
+// A null table means no rotation; outputs are multiplied by scale (one rounding).
 hipError_t launch_rope_apply(const void* x, void* y, bool bf16, bool half_pairs, long long groups, int N, int D,
-                             const PosMap& map, const float* table, hipStream_t stream);
+                             const PosMap& map, const float* table, hipStream_t stream, float scale = 1.f);
 
 // ---------------------------------------------------------------- prefill
 struct PrefillArgs {
@@ -103,7 +104,8 @@ struct BwdArgs {
   const void* dout;       // upstream gradient [B][Hq][Nq][D] dtype
   const float* lse;       // forward lse [B][Hq][Nq]
   float* delta;           // workspace [B][Hq][Nq]: sum_d dO * O
-  const void* q_rot;      // bf16: copy of q already rotated, set whenever ROTATE_Q (staged tiles are not rotated)
+  const void* q_rot;      // bf16: q rotated (ROTATE_Q) and multiplied by sm_scale log2(e), rounded once as the
+                          // forward's q~ is, so the backward's S equals the forward's; always set for bf16
   const void* k_rot;      // the same for k (ROTATE_K)
   const float* table;
   float* dq;              // [B][Hq][Nq][D] fp32

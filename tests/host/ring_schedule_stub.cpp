@@ -23,7 +23,7 @@ static void name_ptr(const void* p, const char** name, long long* off) {
 }
 
 hipError_t launch_rope_apply(const void* x, void* y, bool bf16, bool half_pairs, long long groups, int N, int D,
-                             const PosMap& m, const float*, hipStream_t) {
+                             const PosMap& m, const float*, hipStream_t, float) {
   const char *nx, *ny;
   long long ox, oy;
   name_ptr(x, &nx, &ox);

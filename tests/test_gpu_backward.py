@@ -93,6 +93,18 @@ def test_backward_bf16_group_sizes(G):
     assert _rel_err(got, ref) <= 2e-2
 
 
+@pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
+@pytest.mark.parametrize("G,Nq", [(1, 1), (1, 32), (1, 64), (1, 96), (1, 128), (1, 160), (2, 96), (2, 160), (4, 33)])
+def test_backward_bf16_tile_counts(G, Nq, causal):
+    """Every residue of the query-tile count a dk/dv workgroup walks (1 to 5
+    tiles of one head, several heads), including a single query row."""
+    srt = need_gpu()
+    got, ref = _run(srt, dtype=torch.bfloat16, D=128, Hq=G, Hkv=1, Nq=Nq, Nk=max(Nq, 96), causal=causal,
+                    q_pos0=max(0, 96 - Nq) if causal else 0, seed=55)
+    _report(f"bf16 G={G} Nq={Nq} causal={causal}", got, ref)
+    assert _rel_err(got, ref) <= 2e-2
+
+
 def test_backward_bf16_2k():
     """2048 tokens, GQA 8/2: many tiles in both kernels."""
     srt = need_gpu()

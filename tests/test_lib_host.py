@@ -149,9 +149,11 @@ def test_abi_rejects_before_launch(srt):
     # delta (fp32 [B][Hq][Nq]), then for bf16 the rotated q and k copies, each region 256-byte aligned
     ws = lambda *args: (lib.srt_attn_backward_workspace_size(*args, C.byref(n)), n.value)
     assert ws(0, 2, 8, 2, 100, 50, 64, 3) == (0, 6400)
-    assert ws(1, 2, 8, 2, 100, 50, 128, 0) == (0, 6400)
-    assert ws(1, 2, 8, 2, 100, 50, 128, 1) == (0, 6400 + 2 * 8 * 100 * 128 * 2)
-    assert ws(1, 2, 8, 2, 100, 50, 128, 2) == (0, 6400 + 2 * 2 * 50 * 128 * 2)
+    qcopy = 2 * 8 * 100 * 128 * 2               # bf16 always keeps a scaled copy of q
+    assert ws(1, 2, 8, 2, 100, 50, 128, 0) == (0, 6400 + qcopy)
+    assert ws(1, 2, 8, 2, 100, 50, 128, 1) == (0, 6400 + qcopy)
+    assert ws(1, 2, 8, 2, 100, 50, 128, 2) == (0, 6400 + qcopy + 2 * 2 * 50 * 128 * 2)
+    assert ws(1, 2, 8, 2, 0, 50, 128, 3) == (0, 2 * 2 * 50 * 128 * 2)
     assert ws(1, 1, 1, 1, 3, 5, 128, 7) == (0, 256 + 768 + 1280)
     assert ws(1, 2, 8, 2, 100, 50, 128, 8)[0] == 1 and b"rope_flags" in lib.srt_last_error()
     assert ws(2, 2, 8, 2, 100, 50, 128, 0)[0] == 1
