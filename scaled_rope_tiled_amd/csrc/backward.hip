@@ -511,8 +511,7 @@ struct Dkdv2Smem {
   alignas(16) __hip_bfloat16 q[4][32 * kTStr];
   alignas(16) __hip_bfloat16 o[4][32 * kTStr];
   alignas(16) float4 p[2][4][4][64];      // [step parity][key group][chunk of 4 floats][lane]
-  alignas(16) float l2[4][32];
-  alignas(16) float dl[4][32];
+  alignas(16) float ld[4][64];            // [buffer][-lse log2(e) of the 32 rows, then -delta]
 };
 
 
@@ -551,30 +550,30 @@ __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) 
   const int sc = tid & 15, sr = tid >> 4;
   const uint32_t soff = sr * (kD * 2) + sc * 16;
   uint4 qb, ob;
-  float l2v = 0.f, dlv = 0.f;
-  int ig = 0, itq = t0;      // next tile to load: head ig of the group, row tile itq
+  float ldv = 0.f;           // wave 0: lane r < 32 -lse log2(e) of row r, lane 32 + r -delta of row r
+  // next tile to load: head ig of the group, row tile itq, first row hrow (all wave-uniform)
+  int ig = 0, itq = t0;
+  long long hrow = ((long long)b * a.Hq + hk * G) * a.Nq + (long long)t0 * 32;
   auto issue = [&]() {
-    const long long hrow = ((long long)b * a.Hq + hk * G + ig) * a.Nq + (long long)itq * 32;
     const int rows = ig < G ? min(32, max(0, a.Nq - itq * 32)) : 0;
     qb = buffer_ld16(raw_buffer(qsrc + hrow * kD, rows * (kD * 2)), soff);
     ob = buffer_ld16(raw_buffer(dog + hrow * kD, rows * (kD * 2)), soff);
-    if (tid < 32) {
-      l2v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(raw_buffer(a.lse + hrow, rows * 4), tid * 4, 0, 0)) *
-            -kLog2e;
-      dlv = -__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(raw_buffer(a.delta + hrow, rows * 4), tid * 4, 0, 0));
+    if (wave == 0) {
+      const float* src = lane < 32 ? a.lse + hrow : a.delta + hrow;
+      const float x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(raw_buffer(src, rows * 4), l32 * 4, 0, 0));
+      ldv = lane < 32 ? x * -kLog2e : -x;
     }
+    hrow += 32;
     if (++itq == t0 + ntq) {
       itq = t0;
       ++ig;
+      hrow += a.Nq - ntq * 32;
     }
   };
   auto store = [&](int buf) {
     *reinterpret_cast<uint4*>(&sm.q[buf][sr * kTStr + sc * 8]) = qb;
     *reinterpret_cast<uint4*>(&sm.o[buf][sr * kTStr + sc * 8]) = ob;
-    if (tid < 32) {
-      sm.l2[buf][tid] = l2v;
-      sm.dl[buf][tid] = dlv;
-    }
+    if (wave == 0) sm.ld[buf][lane] = ldv;
   };
   auto init_rows = [&](const float* src) {     // the 16 accumulator rows (queries) of this lane
     f32x16 c;
@@ -627,7 +626,7 @@ __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) 
       const int tm_lo = (int)max((long long)INT_MIN, min((long long)INT_MAX, tlo));
       const int tm_hi = (int)max((long long)INT_MIN, min((long long)INT_MAX, thi));
       f32x16 s_a, s_b;
-      mma_rows1c(lds_off(&sm.q[0][l32 * kTStr + hl * 8]), breg, s_a, init_rows(sm.l2[0]));
+      mma_rows1c(lds_off(&sm.q[0][l32 * kTStr + hl * 8]), breg, s_a, init_rows(&sm.ld[0][0]));
       int ct = t0;
       // step i = R (mod 4) on tile i: S(i+1) into s_out next to P(i) from s_in
       auto pstep = [&](auto rc, const f32x16& s_in, f32x16& s_out) {
@@ -635,7 +634,7 @@ __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) 
         constexpr int nb = (R + 1) & 3;
         store((R + 2) & 3);
         issue();
-        mma_rows1c(lds_off(&sm.q[nb][l32 * kTStr + hl * 8]), breg, s_out, init_rows(sm.l2[nb]));   // stale past the end
+        mma_rows1c(lds_off(&sm.q[nb][l32 * kTStr + hl * 8]), breg, s_out, init_rows(&sm.ld[nb][0]));   // stale past the end
         float p[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) p[j] = __builtin_amdgcn_exp2f(s_in[j]);
@@ -681,7 +680,7 @@ __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) 
         constexpr int R = decltype(rc)::value;
         store((R + 2) & 3);
         issue();
-        if (dp_active) mma_rows1c(lds_off(&sm.o[R][l32 * kTStr + hl * 8]), breg, dp_out, init_rows(sm.dl[R]));
+        if (dp_active) mma_rows1c(lds_off(&sm.o[R][l32 * kTStr + hl * 8]), breg, dp_out, init_rows(&sm.ld[R][32]));
         float ds[16];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -700,7 +699,7 @@ __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) 
       // step 0: dP(0) only
       store(2);
       issue();
-      mma_rows1c(lds_off(&sm.o[0][l32 * kTStr + hl * 8]), breg, dp_a, init_rows(sm.dl[0]));
+      mma_rows1c(lds_off(&sm.o[0][l32 * kTStr + hl * 8]), breg, dp_a, init_rows(&sm.ld[0][32]));
       __syncthreads();
       int i = 1;
       for (; i + 3 < nit; i += 4) {
