@@ -367,7 +367,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   // over the packed pairs is one instruction per two terms, but it competes
   // with the matrix cores, adds do not)
   auto exps = [&](const f32x16& sv, bf16x8 (&pout)[2]) {
-    float part[2] = {0.f, 0.f};
+    float part[2] = {-0.f, -0.f};   // (-0 + x folds to x)
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       uint32_t w[4];
