@@ -50,6 +50,16 @@ __device__ inline float dot2(uint32_t a, uint32_t b, float c) {
                                          false);
 }
 
+// Sum over the 8 lanes of a row group with DPP moves (no LDS traffic): swap
+// neighbours, swap pairs within the quad, then the half-row mirror pairs every
+// lane with one of the other quad.
+__device__ inline float sum8_dpp(float t) {
+  t += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, t), 0xB1, 0xF, 0xF, false));
+  t += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, t), 0x4E, 0xF, 0xF, false));
+  t += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, t), 0x141, 0xF, 0xF, false));
+  return t;
+}
+
 // Streaming load of the KV cache: every byte is read once per decode step, so
 // the loads are marked non-temporal (they bypass cache retention).  Measured
 // on the 128K cache: 6.39 TB/s against 5.91 TB/s with ordinary loads.
@@ -174,9 +184,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
         float t = 0.f;
 #pragma unroll
         for (int p = 0; p < 8; ++p) t = dot2(qp[j][p], kk[p], t);
-        t += __shfl_xor(t, 1, 8);
-        t += __shfl_xor(t, 2, 8);
-        t += __shfl_xor(t, 4, 8);
+        t = sum8_dpp(t);
         s[j] = valid[u] ? t : -INFINITY;
       }
       const uint32_t vv[8] = {vw[u][0].x, vw[u][0].y, vw[u][0].z, vw[u][0].w,
@@ -187,13 +195,13 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
 #pragma unroll
       for (int j = 0; j < G; ++j) {
         if (s[j] > m[j] + kLazy) {          // rare: raise the running max
-          const float sc = exp2f(m[j] - s[j]);
+          const float sc = __builtin_amdgcn_exp2f(m[j] - s[j]);
           l[j] *= sc;
 #pragma unroll
           for (int d = 0; d < 16; ++d) acc[j][d] *= sc;
           m[j] = s[j];
         }
-        const float p = valid[u] ? exp2f(s[j] - m[j]) : 0.f;
+        const float p = valid[u] ? __builtin_amdgcn_exp2f(s[j] - m[j]) : 0.f;
         l[j] += p;
 #pragma unroll
         for (int d = 0; d < 16; ++d) acc[j][d] = fmaf(p, vf[d], acc[j][d]);
