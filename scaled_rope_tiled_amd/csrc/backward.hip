@@ -334,55 +334,6 @@ __device__ inline void load_row_rotated(const __hip_bfloat16* row, bool ok, bool
   for (int ks = 0; ks < 8; ++ks) out[ks] = as_bf16x8(w[ks]);
 }
 
-// Staging of one 32-row tile: thread t moves chunks (t & 7) and (t & 7) + 8
-// of row t >> 3 of two tensors, the first rotated when asked.
-struct Stage {
-  uint4 x[2], y[2];
-  float4 t[4];
-};
-
-template <bool HALF>
-__device__ inline void stage_load(Stage& st, const __hip_bfloat16* xg, const __hip_bfloat16* yg, long long row,
-                                  bool ok, bool rotate, const float4* tab4, long long pos, int sc) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    st.x[i] = ok ? *reinterpret_cast<const uint4*>(xg + row * kD + (sc + 8 * i) * 8) : make_uint4(0, 0, 0, 0);
-    st.y[i] = ok ? *reinterpret_cast<const uint4*>(yg + row * kD + (sc + 8 * i) * 8) : make_uint4(0, 0, 0, 0);
-  }
-  if (ok && rotate) {
-    if (HALF) {
-      const float4* t = tab4 + (pos * (kD / 2) + sc * 8) / 2;     // pairs 8 sc .. 8 sc + 7
-#pragma unroll
-      for (int q = 0; q < 4; ++q) st.t[q] = t[q];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const float4* t = tab4 + (pos * (kD / 2) + (sc + 8 * i) * 4) / 2;   // pairs 4 chunk .. 4 chunk + 3
-        st.t[2 * i] = t[0];
-        st.t[2 * i + 1] = t[1];
-      }
-    }
-  }
-}
-
-template <bool HALF>
-__device__ inline void stage_store(Stage& st, __hip_bfloat16* xs, int xstr, __hip_bfloat16* ys, int ystr, int sr,
-                                   int sc, bool rotate) {
-  uint4 x0 = st.x[0], x1 = st.x[1];
-  if (rotate) {
-    if (HALF) {
-      rotate_chunk_pair(x0, x1, st.t);
-    } else {
-      x0 = rotate_chunk(x0, st.t[0], st.t[1]);
-      x1 = rotate_chunk(x1, st.t[2], st.t[3]);
-    }
-  }
-  *reinterpret_cast<uint4*>(xs + sr * xstr + sc * 8) = x0;
-  *reinterpret_cast<uint4*>(xs + sr * xstr + (sc + 8) * 8) = x1;
-  *reinterpret_cast<uint4*>(ys + sr * ystr + sc * 8) = st.y[0];
-  *reinterpret_cast<uint4*>(ys + sr * ystr + (sc + 8) * 8) = st.y[1];
-}
-
 // acc[db] += X^T[d][rows] B[rows][cols] over a 32-row tile X held row-major in
 // LDS (stride kTStr), B given as two 16-row k-steps in accumulator row order.
 __device__ inline void mma_tr(f32x16 (&acc)[4], uint32_t x_lane, const bf16x8 (&bk)[2]) {
