@@ -14,8 +14,9 @@
 // Lane layout: 8 lanes share one cache row.  Lane `sub` of a row loads the
 // 16-byte chunks sub and sub+8 (dims 8*sub..8*sub+7 and 64+8*sub..), so each
 // load instruction of a wave reads 8 whole 128-byte row halves.  The q.k dot
-// is 4 bf16 dot2 instructions per chunk and head, finished by a 3-step
-// butterfly inside the 8 lanes.  Each lane keeps a private online softmax over
+// is 4 bf16 dot2 instructions per chunk and head, finished by three DPP adds
+// inside the 8 lanes (no matrix cores run here, so the dot instructions
+// compete with nothing).  Each lane keeps a private online softmax over
 // its rows (running max m, sum l, accumulator of its 16 dims per head) and only
 // rescales when a score exceeds its running max by more than 2^8 (the result is
 // exact for any choice of m; the bound only keeps e^(s-m) <= 2^8).  Partial
