@@ -26,7 +26,7 @@ YARN_SMALL = synth.Rope(synth.YARN, 10000.0, 16.0, 64.0, 1.0, 32.0)
 
 
 def _run(srt, *, dtype, D, B=1, Hq=4, Hkv=2, Nq=150, Nk=150, q_pos0=0, k_pos0=0, causal=True, window=0, sink=0,
-         half=False, rotate=True, seed=51):
+         half=False, rotate=True, seed=51, sm_scale=None):
     q, k, v = qkv(B, Hq, Hkv, Nq, Nk, D, dtype, seed)
     do = synth.randn((B, Hq, Nq, D), dtype, seed, synth.DO_ID, "cuda")
     table, _ = device_table(srt, YARN_SMALL, D, max(q_pos0 + Nq, k_pos0 + Nk, 1))
@@ -39,9 +39,10 @@ def _run(srt, *, dtype, D, B=1, Hq=4, Hkv=2, Nq=150, Nk=150, q_pos0=0, k_pos0=0,
         k = srt.rope_apply(k, table, pos0=k_pos0, pairing=pairing)
         flags = 0
     kw = dict(causal=causal, q_pos0=q_pos0, k_pos0=k_pos0, window=window, sink=sink)
-    o, l = srt.attn_prefill(q, k, v, table=table, rope_flags=flags, **kw)
-    dq, dk, dv = srt.attn_backward(q, k, v, o, do, l, table=table, rope_flags=flags, **kw)
-    rq, rk, rv, _ = BW.attention_backward(f64(q), f64(k), f64(v), f64(do), sm_scale=1 / math.sqrt(D),
+    sm = 1 / math.sqrt(D) if sm_scale is None else sm_scale
+    o, l = srt.attn_prefill(q, k, v, table=table, rope_flags=flags, sm_scale=sm, **kw)
+    dq, dk, dv = srt.attn_backward(q, k, v, o, do, l, table=table, rope_flags=flags, sm_scale=sm, **kw)
+    rq, rk, rv, _ = BW.attention_backward(f64(q), f64(k), f64(v), f64(do), sm_scale=sm,
                                           theta=th if rotate else None, mscale=ms, pairing=pairing, **kw)
     return (f64(dq), f64(dk), f64(dv)), (rq, rk, rv)
 
@@ -73,8 +74,10 @@ def test_backward_fp32(kw):
 
 @pytest.mark.parametrize("kw", [dict(), dict(half=True), dict(window=100, sink=4), dict(window=70, sink=90),
                                 dict(q_pos0=300, k_pos0=340, Nq=130, Nk=257), dict(causal=False),
-                                dict(rotate=False), dict(B=2, Nq=64, Nk=64)],
-                         ids=["plain", "half", "window", "wide_sink", "offsets", "noncausal", "given", "batch"])
+                                dict(rotate=False), dict(B=2, Nq=64, Nk=64), dict(sm_scale=0.03),
+                                dict(sm_scale=0.2, rotate=False, Nq=96, Nk=96)],
+                         ids=["plain", "half", "window", "wide_sink", "offsets", "noncausal", "given", "batch",
+                              "scale_small", "scale_large_given"])
 def test_backward_bf16(kw):
     srt = need_gpu()
     base = dict(Nq=300, Nk=300)
