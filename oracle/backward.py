@@ -73,3 +73,56 @@ def attention_backward(q, k, v, dout, *, sm_scale: float, causal: bool = True, q
                 delta[b, h] = dl
             dk[b, hk] = dkt if theta is None else rotate_back(dkt, kpos, theta, mscale, pairing)
     return dq, dk, dv, delta
+
+
+def attention_backward_sampled(q, k, v, dout, *, hk: int, rows, keys, sm_scale: float, causal: bool = True,
+                               q_pos0: int = 0, k_pos0: int = 0, theta=None, mscale: float = 1.0, window: int = 0,
+                               sink: int = 0, pairing: str = "interleaved", b: int = 0):
+    """The same gradients as `attention_backward`, for batch b and KV head hk only, at chosen outputs:
+    dq at query rows `rows` of every query head of hk's group ([G][len(rows)][D]) and dk, dv at keys
+    `keys` of hk ([len(keys)][D] each).  Every needed row of P is formed whole from its row of S (so its
+    own lse and delta are exact); a key's gradients sum over exactly the rows that see it.  The cost is
+    one row of S per needed row: cheap for any row, and for keys that few rows see (the end of a
+    causal sequence), at any sequence length."""
+    rot = _A._rotator(pairing)
+    q, k, v, dout = _A._f64(q)[b], _A._f64(k)[b], _A._f64(v)[b], _A._f64(dout)[b]
+    Hq, Nq, D = q.shape
+    Hkv, Nk, _ = k.shape
+    g = Hq // Hkv
+    rows = np.asarray(rows, dtype=np.int64)
+    keys = np.asarray(keys, dtype=np.int64)
+    kpos = k_pos0 + np.arange(Nk)
+    kt = k[hk] if theta is None else rot(k[hk], kpos, theta, mscale)
+    vv = v[hk]
+    # rows that see any sampled key, plus the sampled rows
+    see = _A.visible(q_pos0 + np.arange(Nq), kpos[keys], causal=causal, window=window, sink=sink) if causal \
+        else np.ones((Nq, len(keys)), bool)
+    need = np.union1d(np.nonzero(see.any(axis=1))[0], rows)
+    dq = np.zeros((g, len(rows), D))
+    dkt = np.zeros((len(keys), D))
+    dv = np.zeros((len(keys), D))
+    for gi, h in enumerate(range(hk * g, (hk + 1) * g)):
+        for i in need:
+            qp = q_pos0 + i
+            qt = q[h, i] if theta is None else rot(q[h, i][None, :], np.array([qp]), theta, mscale)[0]
+            vis = _A.visible(np.array([qp]), kpos, causal=causal, window=window, sink=sink)[0] if causal \
+                else np.ones(Nk, bool)
+            if not vis.any():
+                continue
+            s = np.where(vis, sm_scale * (kt @ qt), -np.inf)
+            m = s[vis].max()
+            p = np.where(vis, np.exp(s - m), 0.0)
+            p /= p.sum()
+            o = p @ vv
+            do = dout[h, i]
+            dl = do @ o
+            ds = p * (vv @ do - dl)
+            sel = np.nonzero(rows == i)[0]
+            if len(sel):
+                dqt = sm_scale * (ds @ kt)
+                dq[gi, sel[0]] = dqt if theta is None else rotate_back(dqt[None, :], np.array([qp]), theta, mscale,
+                                                                       pairing)[0]
+            dv += p[keys, None] * do[None, :]
+            dkt += sm_scale * ds[keys, None] * qt[None, :]
+    dk = dkt if theta is None else rotate_back(dkt, kpos[keys], theta, mscale, pairing)
+    return dq, dk, dv

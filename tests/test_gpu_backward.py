@@ -126,3 +126,47 @@ def test_backward_empty():
     dv = torch.full(v.shape, float("nan"), device="cuda")
     _, dk, dv = srt.attn_backward(q, k, v, o, o, l, dk=dk, dv=dv)
     assert (dk == 0).all() and (dv == 0).all()
+
+
+def test_backward_yarn_32k_full_size_sampled():
+    """The benchmark's backward launch at full size (YaRN 32K, GQA 32/8, D=128): dq at sampled query rows
+    of every query head of the first and last KV group, dk and dv at the last 48 keys of those KV heads
+    (few rows see them, so the oracle forms exactly those rows of P), each against the oracle at those
+    entries; and, for each of the two KV heads, the sum of dv over all keys equals the sum of dO over the
+    group's rows (every row of P sums to one)."""
+    srt = need_gpu()
+    w = synth.WORKLOADS["yarn_32k_bf16"]
+    D, N, G = w.D, w.N, w.Hq // w.Hkv
+    q = synth.randn((w.B, w.Hq, N, D), torch.bfloat16, w.seed, synth.Q_ID, "cuda")
+    k = synth.randn((w.B, w.Hkv, N, D), torch.bfloat16, w.seed, synth.K_ID, "cuda")
+    v = synth.randn((w.B, w.Hkv, N, D), torch.bfloat16, w.seed, synth.V_ID, "cuda")
+    do = synth.randn((w.B, w.Hq, N, D), torch.bfloat16, w.seed, synth.DO_ID, "cuda")
+    table, _ = device_table(srt, w.rope, D, N)
+    out, lse = srt.attn_prefill(q, k, v, table=table)                     # as the benchmark
+    dq, dk, dv = srt.attn_backward(q, k, v, out, do, lse, table=table)
+    torch.cuda.synchronize()
+    th, ms, _ = oracle_freq(w.rope, D)
+    rng = np.random.default_rng(w.seed)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 63, 4095, N // 2, N - 2, N - 1], rng.integers(0, N, 7)]))
+    keys = np.arange(N - 48, N)
+    worst = 0.0
+    for hk in (0, w.Hkv - 1):
+        hs = slice(hk * G, (hk + 1) * G)
+        rdq, rdk, rdv = BW.attention_backward_sampled(
+            f64(q[:, hs]), f64(k[:, hk:hk + 1]), f64(v[:, hk:hk + 1]), f64(do[:, hs]), hk=0, rows=rows, keys=keys,
+            sm_scale=1 / math.sqrt(D), theta=th, mscale=ms)
+        got_dq = f64(dq[0, hs][:, torch.as_tensor(rows, device="cuda")])
+        got_dk = f64(dk[0, hk][torch.as_tensor(keys, device="cuda")])
+        got_dv = f64(dv[0, hk][torch.as_tensor(keys, device="cuda")])
+        for name, g, r in (("dq", got_dq, rdq), ("dk", got_dk, rdk), ("dv", got_dv, rdv)):
+            # dk, dv of the last keys are small (few rows see them): judged against their own scale
+            scale = max(1.0, float(np.abs(r).max())) if name == "dq" else float(np.abs(r).max())
+            e = max_abs(g, r) / scale
+            print(f"32K kv head {hk} {name}: max|err| {max_abs(g, r):.3g} max|ref| {np.abs(r).max():.3g}", flush=True)
+            worst = max(worst, e)
+        dv_sum = f64(dv[0, hk].sum(dim=0))
+        do_sum = f64(do[0, hs].float().sum(dim=(0, 1)))
+        rel = max_abs(dv_sum, do_sum) / float(np.abs(do_sum).max())
+        print(f"32K kv head {hk}: sum dv vs sum dO rel err {rel:.3g}", flush=True)
+        assert rel <= 1e-2
+    assert worst <= 2e-2

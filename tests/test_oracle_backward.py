@@ -108,3 +108,25 @@ def test_rotate_back_is_the_transpose():
         lhs = (fn(x, pos, th, 1.3) * g).sum(axis=1)
         rhs = (x * BW.rotate_back(g, pos, th, 1.3, pairing)).sum(axis=1)
         np.testing.assert_allclose(lhs, rhs, atol=1e-12)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(causal=False), dict(window=9, sink=2), dict(q_pos0=3, k_pos0=11),
+                                dict(pairing="half"), dict(rotate=False)],
+                         ids=["causal", "noncausal", "window", "masked_rows", "half", "given"])
+def test_sampled_backward_equals_full(kw):
+    """attention_backward_sampled (the form full-size GPU tests use) returns exactly the entries of the full
+    oracle backward at the chosen rows and keys, GQA 4/2, YaRN rotation."""
+    kw = dict(kw)
+    rotate = kw.pop("rotate", True)
+    rng = np.random.default_rng(7)
+    B, Hq, Hkv, N, D = 1, 4, 2, 40, 8
+    q, k, v, do = (rng.standard_normal(s) for s in [(B, Hq, N, D), (B, Hkv, N, D), (B, Hkv, N, D), (B, Hq, N, D)])
+    th, ms, _ = rope.inv_freq(rope.YARN, 10000.0, 4.0, 16.0, 1.0, 32.0, D)
+    rk = dict(theta=th if rotate else None, mscale=ms if rotate else 1.0)
+    full = BW.attention_backward(q, k, v, do, sm_scale=0.3, **rk, **kw)
+    rows, keys = [0, 7, 23, 39], [0, 1, 20, 39]
+    for hk in range(Hkv):
+        dq, dk, dv = BW.attention_backward_sampled(q, k, v, do, hk=hk, rows=rows, keys=keys, sm_scale=0.3, **rk, **kw)
+        np.testing.assert_allclose(dq, full[0][0, 2 * hk:2 * hk + 2][:, rows], atol=1e-12)
+        np.testing.assert_allclose(dk, full[1][0, hk][keys], atol=1e-12)
+        np.testing.assert_allclose(dv, full[2][0, hk][keys], atol=1e-12)
