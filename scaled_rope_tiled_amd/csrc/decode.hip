@@ -160,7 +160,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
   const uint4* kg = reinterpret_cast<const uint4*>(a.k) + row_base * (kD / 8);
   const uint4* vg = reinterpret_cast<const uint4*>(a.v) + row_base * (kD / 8);
 
-  constexpr int kUnroll = G >= 8 ? 1 : 2;   // rows per lane in flight (G = 8 keeps 8 heads of state)
+  constexpr int kUnroll = G >= 8 ? 1 : 4;   // rows per lane in flight (G = 8 keeps 8 heads of state)
   for (int r0 = lo; r0 < hi; r0 += kRowsPerIter * kUnroll) {
     uint4 kw[kUnroll][2], vw[kUnroll][2];
     bool valid[kUnroll];
