@@ -193,3 +193,28 @@ def test_factors_match_oracle(srt):
     bad[5] = float("nan")
     with pytest.raises(SrtError):
         srt.rope_inv_freq_factors(1e4, bad, 128)
+
+
+def test_empty_problems_return_ok_without_pointers(srt):
+    """An empty problem (no row, no sequence) is a successful no-op: every entry
+    point returns SRT_OK before it looks at a pointer or touches the device, so
+    NULL pointers and a null stream are accepted (this runs with no GPU)."""
+    lib = srt.lib()
+    assert lib.srt_rope_apply(None, None, 1, 1, 4, 0, 128, 0, None, 0, 0, None) == 0
+    assert lib.srt_rope_apply(None, None, 0, 0, 4, 16, 128, 0, None, 0, 0, None) == 0
+    # prefill: no query row (Nq = 0), then no batch
+    assert lib.srt_attn_prefill(None, None, None, 1, 1, 4, 2, 0, 64, 128, 0, 0, 0, 0, 1, 0, 0, 0.1,
+                                None, 0, 0, None, 1, 0, None, 0, None) == 0
+    assert lib.srt_attn_prefill(None, None, None, 1, 0, 4, 2, 64, 64, 128, 0, 0, 0, 0, 1, 0, 0, 0.1,
+                                None, 0, 0, None, 1, 0, None, 0, None) == 0
+    assert lib.srt_attn_merge_states(None, None, None, None, 0, 0, None, 1, 0, None, 0, 1, 4, 0, 128, None) == 0
+    assert lib.srt_attn_decode_splitk(None, None, None, 1, 0, 32, 8, 1024, 128, None, 64, 0.1, None, 0, 0, 0, 0,
+                                      None, 0, None, None, None) == 0
+    assert lib.srt_attn_ring_prefill(None, None, None, 1, 1, 32, 8, 0, 128, 8, 0, -1, 0, 0, 0.1, None, 0, 0,
+                                     None, 0, None, None, None) == 0
+    assert lib.srt_attn_backward(None, None, None, None, None, None, 1, 0, 8, 2, 64, 64, 128, 0, 0, 1, 0, 0, 0.1,
+                                 None, 0, 0, None, 0, None, None, None, None) == 0
+    # sizes are still validated first: a negative size is an error even when the problem is empty
+    assert lib.srt_attn_prefill(None, None, None, 1, 1, 4, 2, -1, 64, 128, 0, 0, 0, 0, 1, 0, 0, 0.1,
+                                None, 0, 0, None, 1, 0, None, 0, None) == 1
+    assert lib.srt_attn_merge_states(None, None, None, None, 0, 0, None, 1, 0, None, 0, 1, -4, 0, 128, None) == 1
