@@ -22,3 +22,18 @@ def test_window_pairs_match_oracle(N, W, S):
 def test_flops_of_the_32k_workload():
     # 4 D flops per kept pair per query head: 4 * 128 * 32 * N (N + 1) / 2 at N = 32768
     assert bench.prefill_flops(1, 32, 32768, 32768, 128) == 4.0 * 128 * 32 * 32768 * 32769 / 2
+
+
+def test_more_than_one_gpu_is_refused():
+    """The benchmark runs on one GPU: --gpus above 1 exits with status 2 and a
+    message, before anything touches a device."""
+    import json
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "8"], capture_output=True,
+                       text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"]
