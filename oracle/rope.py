@@ -67,9 +67,12 @@ def inv_freq(method: int, base: float, s: float = 1.0, L: float = 0.0,
     * PI:   theta' = theta / s        ("Long Context..." §4.2: m -> m/s is the
                                        same as theta -> theta/s).
     * NTK:  theta' = (b')^(-2d/D) with b' = b s^(D/(D-2))  (§5.2, §5.4).
-    * YARN: r_d = L theta_d / (2 pi) with the ORIGINAL base (§6.2, §6.6);
-            w = ramp(r_d); theta' = (1-w) theta/s + w theta;
-            mscale = 0.1 ln s + 1 (§6.3, §6.4 fold it into cos/sin).
+    * YARN: the number of turns pair d makes within the training length,
+            r_d = L theta_d / (2 pi) (§6.2; the ORIGINAL base, as §6.2 and
+            "8.3 长上下文技术" §8.3.3 both state), sets the interpolation
+            weight gamma_d = ramp(r_d) and theta'_d = gamma_d theta_d +
+            (1 - gamma_d) theta_d / s (§6.2); mscale = 0.1 ln s + 1 (§6.3,
+            folded into cos/sin by §6.4).
     band: YARN labels each pair by "8.3 长上下文技术" §8.3.3: high if
     r > beta (gamma = 1), low if r < alpha (gamma = 1/s), mid otherwise.
     The other methods have no bands; they are labelled by what their rule
@@ -89,11 +92,10 @@ def inv_freq(method: int, base: float, s: float = 1.0, L: float = 0.0,
     if method == YARN:
         if not beta > alpha:
             raise ValueError("YaRN needs beta > alpha")
-        wavelen = 2.0 * math.pi / theta
-        r = L / wavelen
-        w = yarn_ramp(r, alpha, beta)
-        theta_p = (1.0 - w) * (theta / s) + w * theta
-        band = np.where(r > beta, BAND_HIGH, np.where(r < alpha, BAND_LOW, BAND_MID)).astype(np.int8)
+        turns = L * theta / (2.0 * math.pi)          # r_d: turns of pair d over the training length
+        gamma = yarn_ramp(turns, alpha, beta)        # 1: keep theta_d (many turns); 0: theta_d / s (few)
+        theta_p = gamma * theta + (1.0 - gamma) * (theta / s)
+        band = np.where(turns > beta, BAND_HIGH, np.where(turns < alpha, BAND_LOW, BAND_MID)).astype(np.int8)
         return theta_p, yarn_mscale(s), band
     raise ValueError(f"unknown rope method {method}")
 
