@@ -25,7 +25,13 @@ same line carries:
     tokens (flops of the kept pairs only), and its time against full causal;
   * ``backward``: dq, dk, dv of the same prefill, TFLOP/s of the five
     backward products;
-  * ``cpu_baseline``: the fp64 oracle on the host cores, on a bounded sample.
+  * ``gqa_8k``: the GQA 8K prefill (B=1, 32/8 heads, D=128, N=8192, base
+    5e5, unscaled), same launch, against the bf16 peak;
+  * ``cpu_baseline`` (top level for the headline, and inside each leg): the
+    fp64 oracle on the host cores, on a bounded sample of that leg's
+    workload, run in a pool of single-threaded worker processes before the
+    GPU is touched;
+  * ``library``: path and SHA-256 of the libsrt.so that was loaded.
 
 FLOPs count only (query, key) pairs the causal mask keeps, 4*D per pair per
 query head.  Decode bytes count K and V once plus q, out, lse and the split-K
@@ -47,7 +53,12 @@ sys.path.insert(0, ROOT)
 METRIC = "causal prefill attn TFLOP/s + 128K decode GB/s, % of MI355X roofline"
 PEAK_BF16_TFLOPS = 2516.6       # 256 CU x 2.4 GHz x 4096 flop/clk/CU, dense
 PEAK_HBM_GBS = 8000.0
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_yarn32k_counters.json")
+# rocprofv3 counters of the prefill kernel, one file per workload; a file is
+# used only for the workload, launch flags and kernel source it was taken on
+COUNTER_FILES = {"yarn_32k_bf16": os.path.join(ROOT, "profiles", "prefill_bf16_yarn32k_counters.json"),
+                 "gqa_8k_bf16": os.path.join(ROOT, "profiles", "prefill_bf16_gqa8k_counters.json")}
+BENCH_ROPE_FLAGS = 1            # the timed launch: q rotated on load, K rotated once by rope_apply
+LIB_PATH = os.path.join(ROOT, "scaled_rope_tiled_amd", "libsrt.so")
 PREFILL_SRC = os.path.join(ROOT, "scaled_rope_tiled_amd", "csrc", "prefill_bf16.hip")
 
 
@@ -85,8 +96,7 @@ def _sha(path: str) -> str:
 
 def _ensure_built():
     """Build libsrt.so only when it is absent (a built library is used as is)."""
-    lib = os.environ.get("SRT_LIB", os.path.join(ROOT, "scaled_rope_tiled_amd", "libsrt.so"))
-    if not os.path.exists(lib):
+    if not os.path.exists(LIB_PATH):
         import __graft_entry__
         __graft_entry__.build()
 
@@ -161,13 +171,17 @@ def bench_prefill(srt, torch, w, steps, warmup, prerotate_k=False):
             "tflops_step": flops / (ms_step * 1e-3) / 1e12, "tflops_kernel": flops / (kernel_ms * 1e-3) / 1e12}
 
 
-def traffic_from_counters():
+def traffic_from_counters(workload: str, rope_flags: int):
     """HBM bytes per launch and MFMA busy fraction of the prefill kernel from
-    committed rocprofv3 counters, if they were taken on this kernel source."""
-    if not os.path.exists(COUNTERS_FILE):
-        return None, None, "no counter file"
-    with open(COUNTERS_FILE) as f:
+    committed rocprofv3 counters, if they were taken on this workload, with
+    these launch flags, on this kernel source."""
+    path = COUNTER_FILES.get(workload)
+    if path is None or not os.path.exists(path):
+        return None, None, "no counter file for this workload"
+    with open(path) as f:
         c = json.load(f)
+    if c.get("workload") != workload or c.get("rope_flags") != rope_flags:
+        return None, None, "counter file taken on another workload or launch"
     if c.get("source_sha256") != _sha(PREFILL_SRC):
         return None, None, "kernel changed since the counters were taken"
     fetch = c["fetch_kib_per_dispatch"] * 1024.0 * c["fetch_scale"]
@@ -366,46 +380,141 @@ def bench_ring(srt, torch, w, steps, warmup):
 
 
 # ----------------------------------------------------------------------------- CPU baseline (oracle)
+#
+# The oracle (fp64 numpy, unchanged) timed on the host cores, in a pool of
+# single-threaded worker processes, one (query-row block, KV group) or one
+# decode (sequence, KV group) per task.  Each task draws its own N(0,1) inputs
+# (fp64; values differ from the GPU draw, and the oracle's time does not
+# depend on them) and times only the oracle call.  The rate is the work done
+# over the workers' busy time shared among them: work / (sum of task times /
+# workers).  The pool is started from a process that has not touched the GPU
+# and is shut down before any GPU work.
 
-def cpu_baseline(w, budget_s: float):
-    """The fp64 oracle on the host cores over a bounded sample of the prefill
-    workload: query rows taken from the end of the sequence (the longest rows),
-    one KV group of 4 query heads at a time, until the time budget is spent.
-    Inputs are drawn on the CPU with the same recipe (values differ from the
-    GPU draw; the rate does not depend on them)."""
-    import numpy as np
-    import torch
-    import synth
-    from oracle import attention as OA
-    from oracle import rope as OR
+def _oracle_worker_init(*_):
+    """One BLAS thread per worker process (set before numpy is first imported)."""
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS"):
+        os.environ[var] = "1"
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
     except Exception:
-        cores = os.cpu_count()
-    D, N = w.D, w.N
-    rp = w.rope
-    th, ms, _ = OR.inv_freq(rp.method, rp.base, rp.s, rp.L, rp.alpha, rp.beta, D)
-    G = w.Hq // w.Hkv
-    block = 256
+        pass
+
+
+def _oracle_rows_task(t):
+    """Query rows [r0, r1) of G heads of one KV group, each against all its
+    visible keys (keys [0, r1), causal)."""
+    import numpy as np
+    from oracle import attention as OA
+    seed, D, G, r0, r1, theta, mscale, sm = t
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((1, 1, r1, D))
+    v = rng.standard_normal((1, 1, r1, D))
+    q = rng.standard_normal((1, G, r1 - r0, D))
     t0 = time.perf_counter()
-    flops = 0.0
-    rows_done = 0
-    hk = 0
-    k = synth.randn((1, 1, N, D), torch.bfloat16, w.seed, synth.K_ID).float().numpy()
-    v = synth.randn((1, 1, N, D), torch.bfloat16, w.seed, synth.V_ID).float().numpy()
-    q = synth.randn((1, G, N, D), torch.bfloat16, w.seed, synth.Q_ID).float().numpy()
-    r_hi = N
-    while time.perf_counter() - t0 < budget_s and r_hi > 0:
-        rows = np.arange(max(0, r_hi - block), r_hi)
-        OA.attention(q, k, v, sm_scale=w.sm_scale, causal=True, theta=th, mscale=ms, rows=rows, block=block)
-        flops += 4.0 * D * G * float(np.sum(rows + 1))
-        rows_done += G * len(rows)
-        r_hi -= block
-    el = time.perf_counter() - t0
-    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{rows_done} query rows (the last {N - r_hi} rows of {G} heads of one KV group, "
-                      f"each against all its visible keys) of {w.name}, {el:.1f} s, fp64 numpy"}
+    OA.attention(q, k, v, sm_scale=sm, causal=True, q_pos0=r0, k_pos0=0, theta=theta, mscale=mscale)
+    dt = time.perf_counter() - t0
+    pairs = G * ((r0 + 1 + r1) * (r1 - r0) // 2)
+    return dt, 4.0 * D * pairs, G * (r1 - r0)
+
+
+def _oracle_decode_task(t):
+    """One sequence's query heads of one KV group against its whole rotated cache."""
+    import numpy as np
+    from oracle import attention as OA
+    seed, N, D, G, theta, mscale, sm = t
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((1, 1, N, D))
+    v = rng.standard_normal((1, 1, N, D))
+    q = rng.standard_normal((1, G, D))
+    t0 = time.perf_counter()
+    OA.decode(q, k, v, sm_scale=sm, theta=theta, mscale=mscale)
+    dt = time.perf_counter() - t0
+    return dt, 2.0 * N * D * 2, 1          # bytes: the group's bf16 K and V rows, read once
+
+
+def _run_pool(pool, workers, tasks, fn, budget_s):
+    """Run tasks (in the given order) with `workers` in flight until the time
+    budget is spent; returns (busy seconds, work, units, tasks done, wall)."""
+    import concurrent.futures as cf
+    t0 = time.perf_counter()
+    it = iter(tasks)
+    inflight = set()
+    busy = work = units = 0.0
+    done = 0
+    for _ in range(workers):
+        t = next(it, None)
+        if t is None:
+            break
+        inflight.add(pool.submit(fn, t))
+    while inflight:
+        fin, inflight = cf.wait(inflight, return_when=cf.FIRST_COMPLETED)
+        for f in fin:
+            dt, wk, un = f.result()
+            busy += dt
+            work += wk
+            units += un
+            done += 1
+            if time.perf_counter() - t0 < budget_s:
+                t = next(it, None)
+                if t is not None:
+                    inflight.add(pool.submit(fn, t))
+    return busy, work, units, done, time.perf_counter() - t0
+
+
+def _row_block_tasks(w, th, ms, block, seed):
+    """Row blocks of one KV group spread evenly over the whole sequence, in a
+    seeded random order, so that a budget cut keeps the row-length mix."""
+    import numpy as np
+    G = w.Hq // w.Hkv
+    starts = np.arange(0, w.N, block)
+    order = np.random.default_rng(seed).permutation(len(starts))
+    return [(seed * 7919 + int(i), w.D, G, int(starts[i]), int(min(w.N, starts[i] + block)), th, ms, w.sm_scale)
+            for i in order]
+
+
+def cpu_baselines(legs, budget_s):
+    """Oracle rates of the prefill, ring and decode legs, in one worker pool."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    import numpy as np
+    import synth
+    from oracle import rope as OR
+    from oracle import attention as OA
+    workers = max(1, min(16, os.cpu_count() or 1))
+    res = {}
+    ctx = mp.get_context("spawn")
+    with cf.ProcessPoolExecutor(max_workers=workers, mp_context=ctx, initializer=_oracle_worker_init) as pool:
+        # start the workers (interpreter start-up is not the oracle's time)
+        list(pool.map(_oracle_worker_init, range(workers)))
+        for leg, (wname, share) in legs.items():
+            w = synth.WORKLOADS[wname]
+            rp = w.rope
+            th, ms, _ = OR.inv_freq(rp.method, rp.base, rp.s, rp.L, rp.alpha, rp.beta, w.D)
+            b = budget_s * share
+            G = w.Hq // w.Hkv
+            if w.kind == "decode":
+                tasks = [(w.seed * 7919 + i, w.N, w.D, G, th, ms, w.sm_scale) for i in range(w.B * w.Hkv)]
+                busy, work, units, done, wall = _run_pool(pool, workers, tasks, _oracle_decode_task, b)
+                rate = work / (busy / workers) / 1e9
+                total = 2.0 * w.B * w.Hkv * w.N * w.D * 2
+                res[leg] = {"value": round(rate, 4), "unit": "GB/s", "cores": workers, "kind": "oracle",
+                            "sample": f"{int(done)} of the {w.B * w.Hkv} (sequence, KV group) decode problems of "
+                                      f"{w.name} ({G} query heads against {w.N} cached keys each), fp64 numpy, "
+                                      f"{workers} single-threaded worker processes, {wall:.1f} s wall",
+                            "full_config_s_extrapolated": round(total / (rate * 1e9), 2)}
+            else:
+                tasks = _row_block_tasks(w, th, ms, 256, w.seed)
+                busy, work, units, done, wall = _run_pool(pool, workers, tasks, _oracle_rows_task, b)
+                rate = work / (busy / workers) / 1e12
+                total = 4.0 * w.D * w.B * w.Hq * (w.N * (w.N + 1) // 2)
+                res[leg] = {"value": round(rate, 6), "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+                            "sample": f"{int(units)} query rows ({int(done)} blocks of 256 rows x {G} heads of one "
+                                      f"KV group, spread over all {w.N} positions, each row against all its "
+                                      f"visible keys) of {w.name}, fp64 numpy, {workers} single-threaded worker "
+                                      f"processes, {wall:.1f} s wall",
+                            "full_config_s_extrapolated": round(total / (rate * 1e12), 1)}
+    return res
 
 
 # ----------------------------------------------------------------------------- copy calibration
@@ -420,6 +529,16 @@ def copy_calibration(torch, nbytes: int, reps: int):
     print(json.dumps({"copy_bytes": nbytes, "reps": reps}))
 
 
+def prefill_leg(p, w, traffic=None, mfma_util=None, traffic_note=None):
+    """Roofline fields of one prefill measurement (kernel time from HIP events)."""
+    return {"bound": "mfma", "achieved": round(p["tflops_kernel"], 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(p["tflops_kernel"] / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic, "traffic_note": traffic_note,
+            "mfma_busy_from_counters": None if mfma_util is None else round(mfma_util, 4),
+            "kernel": "prefill_bf16_kernel", "kernel_ms": round(p["kernel_ms"], 4),
+            "alg_flops_per_launch": p["flops"]}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -428,11 +547,12 @@ def main():
     ap.add_argument("--workload", default="yarn_32k_bf16", choices=["gqa_8k_bf16", "yarn_32k_bf16"])
     ap.add_argument("--rotate-k-on-load", action="store_true",
                     help="rotate K inside the prefill kernel at every tile load (default: once, with rope_apply)")
-    ap.add_argument("--no-extras", action="store_true", help="skip the decode and ring legs")
+    ap.add_argument("--no-extras", action="store_true", help="skip the decode, ring, window, backward and 8K legs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-budget", type=float, default=24.0,
+                    help="seconds of oracle time over all legs (split among them)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
-    ap.add_argument("--only", choices=["decode", "ring", "window", "backward"], default=None,
+    ap.add_argument("--only", choices=["decode", "ring", "window", "backward", "gqa_8k"], default=None,
                     help="run one extra leg alone and print its JSON (for profiling that leg's kernels)")
     args = ap.parse_args()
 
@@ -440,6 +560,21 @@ def main():
         print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1 (the multi-GPU ring is "
                                    "not built: its per-device share is the ring leg's device_ms)"}))
         sys.exit(2)
+    if "SRT_LIB" in os.environ:
+        print(json.dumps({"error": "SRT_LIB is set: the benchmark measures only the in-tree library "
+                                   "scaled_rope_tiled_amd/libsrt.so"}))
+        sys.exit(2)
+
+    # oracle baselines first: their worker processes start before this process touches the GPU
+    cpu = {}
+    if not args.no_cpu_baseline and not args.only and not args.copy_calibration:
+        legs = {"headline": (args.workload, 0.3)}
+        if not args.no_extras:
+            legs.update({"gqa_8k": ("gqa_8k_bf16", 0.2), "ring": ("ntk_128k_ring_bf16", 0.25),
+                         "decode": ("decode_128k_bf16", 0.25)})
+            if args.workload == "gqa_8k_bf16":
+                del legs["gqa_8k"]
+        cpu = cpu_baselines(legs, args.cpu_budget)
 
     import torch
     if args.copy_calibration:
@@ -447,7 +582,9 @@ def main():
         return
     _ensure_built()
     import scaled_rope_tiled_amd as srt
+    from scaled_rope_tiled_amd import _lib
     import synth
+    library = {"path": os.path.relpath(_lib.LIB_PATH, ROOT), "sha256": _sha(_lib.LIB_PATH)}
 
     w = synth.WORKLOADS[args.workload]
     if args.only:
@@ -457,18 +594,16 @@ def main():
             r = bench_ring(srt, torch, synth.WORKLOADS["ntk_128k_ring_bf16"], args.steps, args.warmup)
         elif args.only == "window":
             r = bench_window(srt, torch, w, 4096, 4, args.steps, args.warmup, float("nan"))
+        elif args.only == "gqa_8k":
+            w8 = synth.WORKLOADS["gqa_8k_bf16"]
+            r = prefill_leg(bench_prefill(srt, torch, w8, args.steps, args.warmup, True), w8)
         else:
             r = bench_backward(srt, torch, w, args.steps, args.warmup)
-        print(json.dumps({args.only: r}), flush=True)
+        print(json.dumps({args.only: r, "library": library}), flush=True)
         return
     p = bench_prefill(srt, torch, w, args.steps, args.warmup, not args.rotate_k_on_load)
-    traffic, mfma_util, traffic_note = traffic_from_counters()
-    roof = {"bound": "mfma", "achieved": round(p["tflops_kernel"], 2), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(p["tflops_kernel"] / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic, "traffic_note": traffic_note,
-            "mfma_busy_from_counters": None if mfma_util is None else round(mfma_util, 4),
-            "kernel": "prefill_bf16_kernel", "kernel_ms": round(p["kernel_ms"], 4),
-            "alg_flops_per_launch": p["flops"]}
+    flags = 3 if args.rotate_k_on_load else BENCH_ROPE_FLAGS
+    roof = prefill_leg(p, w, *traffic_from_counters(w.name, flags))
     line = {"metric": METRIC, "value": round(p["tflops_step"], 2), "unit": "TFLOP/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(p["ms_per_step"], 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
@@ -479,17 +614,31 @@ def main():
                                                                "cos/sin table + rope_apply(k) + prefill rotating q on load")},
             "roofline": roof}
     if not args.no_extras:
+        if args.workload != "gqa_8k_bf16":
+            torch.cuda.empty_cache()
+            w8 = synth.WORKLOADS["gqa_8k_bf16"]
+            p8 = bench_prefill(srt, torch, w8, 5 * args.steps, args.warmup, True)
+            line["gqa_8k"] = {"workload": w8.name, "unit": "TFLOP/s", "value": round(p8["tflops_kernel"], 2),
+                              "ms_per_step": round(p8["ms_per_step"], 4),
+                              "roofline": prefill_leg(p8, w8, *traffic_from_counters(w8.name, BENCH_ROPE_FLAGS))}
+            if "gqa_8k" in cpu:
+                line["gqa_8k"]["cpu_baseline"] = cpu["gqa_8k"]
         torch.cuda.empty_cache()
         line["decode"] = bench_decode(srt, torch, synth.WORKLOADS["decode_128k_bf16"], max(5, args.steps), args.warmup)
+        if "decode" in cpu:
+            line["decode"]["cpu_baseline"] = cpu["decode"]
         torch.cuda.empty_cache()
         line["ring"] = bench_ring(srt, torch, synth.WORKLOADS["ntk_128k_ring_bf16"], max(2, args.steps // 5), 1)
+        if "ring" in cpu:
+            line["ring"]["cpu_baseline"] = cpu["ring"]
         torch.cuda.empty_cache()
         line["window"] = bench_window(srt, torch, w, 4096, 4, args.steps, args.warmup, p["kernel_ms"])
         torch.cuda.empty_cache()
         line["backward"] = bench_backward(srt, torch, w, max(3, args.steps // 4), 1)
         torch.cuda.empty_cache()
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    if "headline" in cpu:
+        line["cpu_baseline"] = cpu["headline"]
+    line["library"] = library
     print(json.dumps(line), flush=True)
 
 

@@ -181,9 +181,15 @@ int srt_rope_apply(const void* x, void* y, int dtype, int B, int H, int N, int D
  * q: [B][Hq][Nq][D] with head stride q_hstride; k, v: [B][Hkv][Nk][D] with head
  * stride kv_hstride; dtype for q, k, v.  out: [B][Hq][Nq][D] in out_dtype with
  * head stride o_hstride (SRT_F32 keeps a partial state exact for merging).
- * lse: [B][Hq][Nq] fp32 with head stride lse_hstride, or NULL.
+ * lse: [B][Hq][Nq] fp32 with head stride lse_hstride, or NULL.  All device
+ * pointers (q, k, v, out, table_dev) must be 16-byte aligned and the head
+ * strides q_hstride, kv_hstride, o_hstride multiples of 8 elements (rows are
+ * moved in 16-byte vectors), else SRT_ERR_INVALID.  The table is
+ * [table_npos][D/2][2] fp32 for this D; a narrower table is read past its end.
  * Kernels: dtype BF16 with D = 128 (matrix cores), dtype F32 with D in {64, 128}.
- * table_dev may be NULL only when rope_flags == 0.
+ * table_dev may be NULL only when rope_flags == 0.  Without SRT_ROTATE_Q the
+ * bf16 kernel uses q exactly as given and scales the scores in fp32; with it,
+ * the rotated q carries one bf16 rounding (the MFMA operand).
  */
 int srt_attn_prefill(const void* q, const void* k, const void* v, int dtype,
                      int B, int Hq, int Hkv, int Nq, int Nk, int D,

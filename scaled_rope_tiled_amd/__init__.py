@@ -68,6 +68,33 @@ def _ptr(t):
     return None if t is None else C.c_void_p(t.data_ptr())
 
 
+def _on_device(dev: torch.device, **tensors) -> None:
+    """Every given tensor (None skipped) must live on the GPU `dev`: the kernels
+    take raw device pointers, so a host tensor or another device's memory would
+    be dereferenced as if it were this device's."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda or t.device != dev:
+            raise ValueError(f"{name} is on {t.device}; expected {dev}")
+
+
+def _table(table, D: int, dev: torch.device):
+    """(pointer, npos) of a cos/sin table for head size D, or (None, 0).
+
+    The kernels index entry (position, pair) at position * (D/2) + pair, so a
+    table built for another D, a strided view or another dtype would be read
+    out of bounds or misread."""
+    if table is None:
+        return None, 0
+    _on_device(dev, table=table)
+    if table.dtype != torch.float32 or not table.is_contiguous() or table.dim() != 3 \
+            or tuple(table.shape[1:]) != (D // 2, 2):
+        raise ValueError(f"table must be a contiguous float32 [npos, {D // 2}, 2] tensor for D={D} "
+                         f"(got {tuple(table.shape)} {table.dtype})")
+    return _ptr(table), int(table.shape[0])
+
+
 def _head_stride(t: torch.Tensor, name: str) -> int:
     """Head stride of a [B][H][N][D] tensor whose rows are contiguous.
 
@@ -143,8 +170,12 @@ def rope_apply(x: torch.Tensor, table: torch.Tensor, pos0: int = 0, out: torch.T
     if out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
         raise ValueError("out must match x")
     B, H, N, D = x.shape
-    _lib.check(lib().srt_rope_apply(_ptr(x), _ptr(out), _dt(x), B, H, N, D, int(pos0), _ptr(table),
-                                    table.shape[0], _pairing(pairing), _stream(x.device)), "rope_apply")
+    _on_device(x.device, x=x, out=out)
+    if table is None:
+        raise ValueError("rope_apply needs a table")
+    tp, npos = _table(table, D, x.device)
+    _lib.check(lib().srt_rope_apply(_ptr(x), _ptr(out), _dt(x), B, H, N, D, int(pos0), tp,
+                                    npos, _pairing(pairing), _stream(x.device)), "rope_apply")
     return out
 
 
@@ -183,10 +214,12 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, sm_scale:
         ls = lse.stride(1) if Hq > 1 else max(lse.stride(1), Nq)
     if rope_flags is None:
         rope_flags = (ROTATE_Q | ROTATE_K) if table is not None else 0
+    _on_device(q.device, q=q, k=k, v=v, out=out, lse=lse)
+    tp, npos = _table(table, D, q.device)
     sm = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
     _lib.check(lib().srt_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _dt(q), B, Hq, Hkv, Nq, Nk, D,
                                       qs, ks, int(q_pos0), int(k_pos0), int(bool(causal)), int(window), int(sink), sm,
-                                      _ptr(table), 0 if table is None else table.shape[0], int(rope_flags),
+                                      tp, npos, int(rope_flags),
                                       _ptr(out), _dt(out), os_, _ptr(lse), ls, _stream(q.device)),
                "attn_prefill")
     return out, lse
@@ -209,6 +242,7 @@ def attn_merge_states(o_a, lse_a, o_b, lse_b, *, out=None, lse_out=None, out_dty
     if lse_out is None:
         lse_out = torch.empty((B, H, N), dtype=torch.float32, device=o_a.device)
     ls = lse_out.stride(1) if H > 1 else max(lse_out.stride(1), N)
+    _on_device(o_a.device, o_a=o_a, lse_a=lse_a, o_b=o_b, lse_b=lse_b, out=out, lse_out=lse_out)
     _lib.check(lib().srt_attn_merge_states(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _dt(o_a), ia,
                                            _ptr(out), _dt(out), os_, _ptr(lse_out), ls, B, H, N, D,
                                            _stream(o_a.device)), "attn_merge_states")
@@ -244,10 +278,13 @@ def attn_decode_splitk(q, k_cache, v_cache, *, num_splits: int, sm_scale: float 
         lse = None
     if seq_lens is not None and (seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous()):
         raise ValueError("seq_lens must be contiguous int32 [B]")
+    _on_device(q.device, q=q, k_cache=k_cache, v_cache=v_cache, seq_lens=seq_lens, workspace=workspace, out=out,
+               lse=lse)
+    tp, npos = _table(table, D, q.device)
     sm = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
     _lib.check(lib().srt_attn_decode_splitk(_ptr(q), _ptr(k_cache), _ptr(v_cache), _dt(q), B, Hq, Hkv, Nk, D,
-                                            _ptr(seq_lens), int(num_splits), sm, _ptr(table),
-                                            0 if table is None else table.shape[0], _pairing(pairing),
+                                            _ptr(seq_lens), int(num_splits), sm, tp,
+                                            npos, _pairing(pairing),
                                             int(window), int(sink),
                                             _ptr(workspace),
                                             workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
@@ -302,10 +339,14 @@ def attn_ring_prefill(q, k, v, *, num_devices: int, partition="contiguous", devi
         lse = None
     if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
         raise ValueError("out must match q")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, N)):
+        raise ValueError("lse must be contiguous fp32 [B, Hq, N]")
+    _on_device(q.device, q=q, k=k, v=v, workspace=workspace, out=out, lse=lse)
+    tp, npos = _table(table, D, q.device)
     sm = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
     _lib.check(lib().srt_attn_ring_prefill(_ptr(q), _ptr(k), _ptr(v), _dt(q), B, Hq, Hkv, N, D,
                                            int(num_devices), _partition(partition), int(device), int(window),
-                                           int(sink), sm, _ptr(table), 0 if table is None else table.shape[0],
+                                           int(sink), sm, tp, npos,
                                            int(rope_flags), _ptr(workspace),
                                            workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
                                            _stream(q.device)), "attn_ring_prefill")
@@ -351,11 +392,13 @@ def attn_backward(q, k, v, out, dout, lse, *, sm_scale: float | None = None, cau
     for t, ref in ((dq, q), (dk, k), (dv, v)):
         if t.shape != ref.shape or t.dtype != torch.float32 or not t.is_contiguous():
             raise ValueError("gradient buffers must be contiguous fp32 of the input's shape")
+    _on_device(q.device, q=q, k=k, v=v, out=out, dout=dout, lse=lse, workspace=workspace, dq=dq, dk=dk, dv=dv)
+    tp, npos = _table(table, D, q.device)
     sm = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
     _lib.check(lib().srt_attn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _dt(q),
                                        B, Hq, Hkv, Nq, Nk, D, int(q_pos0), int(k_pos0), int(bool(causal)),
-                                       int(window), int(sink), sm, _ptr(table),
-                                       0 if table is None else table.shape[0], int(rope_flags), _ptr(workspace),
+                                       int(window), int(sink), sm, tp,
+                                       npos, int(rope_flags), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), _ptr(dq), _ptr(dk), _ptr(dv),
                                        _stream(q.device)), "attn_backward")
     return dq, dk, dv

@@ -9,8 +9,9 @@ import ctypes as C
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-# SRT_LIB may name another build of the same library (e.g. a tuning variant)
-LIB_PATH = os.environ.get("SRT_LIB", os.path.join(HERE, "libsrt.so"))
+# always the in-tree build next to this file: no environment override, so
+# what the tests and the benchmark load is what build.py produced
+LIB_PATH = os.path.join(HERE, "libsrt.so")
 
 c_int, c_ll, c_double, c_float, c_void_p, c_size_t = C.c_int, C.c_longlong, C.c_double, C.c_float, C.c_void_p, C.c_size_t
 c_char_p = C.c_char_p

@@ -195,6 +195,15 @@ int srt_attn_prefill(const void* q, const void* k, const void* v, int dtype, int
   if (window < 0 || sink < 0) return fail(SRT_ERR_INVALID, "attn_prefill: window and sink must be >= 0");
   if (window > 0 && !causal) return fail(SRT_ERR_INVALID, "attn_prefill: a sliding window needs causal = 1");
   if (Nq > (1 << 30) || Nk > (1 << 30)) return fail(SRT_ERR_UNSUPPORTED, "attn_prefill: N above 2^30");
+  // the kernels move rows in 16-byte vectors (q, k, v rows and table entries
+  // in, 8- or 16-byte groups of out rows out): every row must start on a
+  // 16-byte boundary, so the base pointers are 16-byte aligned and the head
+  // strides whole multiples of 8 elements
+  if (misaligned16(q) || misaligned16(out) || (Nk > 0 && (misaligned16(k) || misaligned16(v))) ||
+      misaligned16(table_dev))
+    return fail(SRT_ERR_INVALID, "attn_prefill: q, k, v, out and the table must be 16-byte aligned");
+  if ((q_hstride % 8) || (kv_hstride % 8) || (o_hstride % 8))
+    return fail(SRT_ERR_INVALID, "attn_prefill: head strides must be multiples of 8 elements");
   srt::PrefillArgs a{};
   a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse; a.table = table_dev;
   a.q_hstride = q_hstride; a.kv_hstride = kv_hstride; a.o_hstride = o_hstride; a.lse_hstride = lse_hstride;

@@ -21,6 +21,9 @@
 // rescales when a score exceeds its running max by more than 2^8 (the result is
 // exact for any choice of m; the bound only keeps e^(s-m) <= 2^8).  Partial
 // states are merged across lanes and waves once at the end.
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+
 #include "srt_internal.h"
 
 namespace srt {

@@ -8,6 +8,9 @@
 // One thread handles 8 consecutive elements of one row (32-byte fp32 or
 // 16-byte bf16 vectors); the two weights are recomputed per thread from the
 // row's lse pair (cached in L1/L2), which is cheaper than a second pass.
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+
 #include "srt_internal.h"
 
 namespace srt {

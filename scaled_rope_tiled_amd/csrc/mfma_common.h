@@ -3,6 +3,9 @@
 // operand reads and lane-pair reductions for v_mfma_f32_32x32x16_bf16 tiles.
 #pragma once
 
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+
 #include "srt_internal.h"
 
 namespace srt {

@@ -34,9 +34,11 @@
 //   ds_read_b64_tr_b16, four consecutive keys of one d column per read.
 //   The O^T accumulator again holds one query per lane, so the online-softmax
 //   rescale is a per-lane multiply.  The reference m of the exponentials is
-//   folded into the QK product: q~ is stored pre-scaled by sm_scale log2(e)
-//   and the accumulator starts at -m, so the scores arrive as
-//   s sm_scale log2(e) - m and each probability is one exp2.  A half's
+//   folded into the QK product: rotated q~ is stored pre-scaled by sm_scale
+//   log2(e) and the accumulator starts at -m, so the scores arrive as
+//   s sm_scale log2(e) - m and each probability is one exp2 (q that is not
+//   rotated stays exact: its accumulator starts at -m / (sm_scale log2(e))
+//   and one fp32 multiply per score gives the same value).  A half's
 //   exponentials are taken against the current m at once (no row maximum on
 //   the common path); m moves, in a rare branch, to the half's maximum only
 //   when a lane's sum over the half exceeds a bound or the lane has no
@@ -85,8 +87,10 @@ struct Smem {
 };
 
 // ROT_K: rotate K on its way into LDS; HALF: half-split pairs; WIN: sliding
-// window and sinks (without it, the window tests fold away).
-template <bool ROT_K, bool HALF, bool WIN>
+// window and sinks (without it, the window tests fold away); SCALE_S: q is
+// not rotated, so it is kept exact (no rounding of q * sm_scale log2(e)) and
+// the scores are multiplied by sm_scale log2(e) in fp32 instead.
+template <bool ROT_K, bool HALF, bool WIN, bool SCALE_S>
 __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a) {
   __shared__ Smem sm;
 
@@ -117,17 +121,15 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   // ---- Q^T operand: query wrow0 + l32, d = ks*16 + hl*8 + 0..7, rotated on load
   // With half-split pairs, dims d and d + 64 pair up; chunks ks and ks + 4
   // of the same lane hold exactly those, so the rotation stays in-lane.
-  // q~ is stored pre-multiplied by cscale = sm_scale * log2(e) (one rounding),
-  // so S^T comes out in log2 units and the softmax needs no multiply.
+  // Rotated q~ is stored pre-multiplied by cscale = sm_scale * log2(e), folded
+  // into the rotation's one rounding, so S^T comes out in log2 units and the
+  // softmax needs no multiply.  Unrotated q (SCALE_S) stays exact: a separate
+  // rounding of q * cscale would shift a score by up to 2^-9 of its size,
+  // which at |s| ~ 40 already exceeds the bf16 output bar; the scores are
+  // scaled in fp32 instead.
   const float cscale = a.sm_scale * kLog2e;
+  const float inv_cscale = cscale != 0.f ? 1.0f / cscale : 0.f;
   auto scale4 = [&](float4 t) { return make_float4(t.x * cscale, t.y * cscale, t.z * cscale, t.w * cscale); };
-  auto scale_chunk = [&](uint4 w) {
-    const uint32_t in[4] = {w.x, w.y, w.z, w.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = pack2(bf_lo(in[i]) * cscale, bf_hi(in[i]) * cscale);
-    return make_uint4(o[0], o[1], o[2], o[3]);
-  };
   bf16x8 qreg[8];
   {
     const int row = wrow0 + l32;
@@ -139,7 +141,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
       for (int ks = 0; ks < 8; ++ks)
         w[ks] = ok ? *reinterpret_cast<const uint4*>(qg + (long long)row * kD + ks * 16 + hl * 8)
                    : make_uint4(0, 0, 0, 0);
-      if (ok && (a.rope_flags & 1)) {
+      if (!SCALE_S && ok) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           const int d0 = ks * 16 + hl * 8;                  // first-half dims d0..d0+7 = pairs d0..d0+7
@@ -147,9 +149,6 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
           const float4 tt[4] = {scale4(t[0]), scale4(t[1]), scale4(t[2]), scale4(t[3])};
           rotate_chunk_pair(w[ks], w[ks + 4], tt);
         }
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) w[ks] = scale_chunk(w[ks]);
       }
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) qreg[ks] = as_bf16x8(w[ks]);
@@ -160,11 +159,9 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
         uint4 w = make_uint4(0, 0, 0, 0);
         if (ok) {
           w = *reinterpret_cast<const uint4*>(qg + (long long)row * kD + d0);
-          if (a.rope_flags & 1) {
+          if (!SCALE_S) {
             const float4* t = tab4 + (qpos * (kD / 2) + d0 / 2) / 2;
             w = rotate_chunk(w, scale4(t[0]), scale4(t[1]));
-          } else {
-            w = scale_chunk(w);
           }
         }
         qreg[ks] = as_bf16x8(w);
@@ -393,6 +390,11 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   auto step = [&](auto has_pv, auto qbuf, auto qkb, int pbuf, auto pkb, int key0h, f32x16& s_in, f32x16& s_out,
                   const bf16x8 (&p_in)[2], bf16x8 (&p_out)[2]) {
     constexpr bool HAS_PV = decltype(has_pv)::value;
+    if constexpr (SCALE_S) {
+      // the accumulator held q.k - m_run / cscale: one multiply gives s cscale - m_run
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s_in[j] *= cscale;
+    }
     if (need_prev) {
       if (HAS_PV) {
 #pragma unroll
@@ -439,10 +441,11 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
       // reference far below 0 would overflow exp2(-d), so that move scales by 1
       alpha_prev = first ? 1.f : __builtin_amdgcn_exp2f(-d);
       l_run *= alpha_prev;
+      const float nm = SCALE_S ? -m_run * inv_cscale : -m_run;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         s_in[j] -= d;
-        negm[j] = -m_run;
+        negm[j] = nm;
       }
       lsum = exps(s_in, p_out);
     }
@@ -564,18 +567,29 @@ hipError_t launch_prefill_bf16_d128(const PrefillArgs& a, hipStream_t stream) {
   const int quads = G > 4 ? G / 4 : 1;
   const dim3 grid(a.Hkv * quads, (a.Nq + rows_per_wg - 1) / rows_per_wg, a.B), block(kThreads);
   const bool rot_k = (a.rope_flags & 2) != 0, half = (a.rope_flags & 4) != 0;
-  const bool win = a.window > 0;
+  const bool win = a.window > 0, scale_s = (a.rope_flags & 1) == 0;
   auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, block, 0, stream, a); };
+  // half-split pairing changes only what is rotated: without a rotation it is
+  // the same kernel
+  auto pick = [&](auto wc, auto sc) {
+    constexpr bool W = decltype(wc)::value, S = decltype(sc)::value;
+    if (rot_k && half) go(prefill_bf16_kernel<true, true, W, S>);
+    else if (rot_k) go(prefill_bf16_kernel<true, false, W, S>);
+    else if constexpr (!S) {
+      if (half) go(prefill_bf16_kernel<false, true, W, S>);
+      else go(prefill_bf16_kernel<false, false, W, S>);
+    } else {
+      go(prefill_bf16_kernel<false, false, W, S>);
+    }
+  };
+  using T = std::true_type;
+  using F = std::false_type;
   if (win) {
-    if (rot_k && half) go(prefill_bf16_kernel<true, true, true>);
-    else if (rot_k) go(prefill_bf16_kernel<true, false, true>);
-    else if (half) go(prefill_bf16_kernel<false, true, true>);
-    else go(prefill_bf16_kernel<false, false, true>);
+    if (scale_s) pick(T{}, T{});
+    else pick(T{}, F{});
   } else {
-    if (rot_k && half) go(prefill_bf16_kernel<true, true, false>);
-    else if (rot_k) go(prefill_bf16_kernel<true, false, false>);
-    else if (half) go(prefill_bf16_kernel<false, true, false>);
-    else go(prefill_bf16_kernel<false, false, false>);
+    if (scale_s) pick(F{}, T{});
+    else pick(F{}, F{});
   }
   return hipGetLastError();
 }

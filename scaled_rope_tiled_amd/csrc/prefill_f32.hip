@@ -10,6 +10,9 @@
 // (1)-(2)); the N x N score matrix never exists.  Key tiles wholly above the
 // causal diagonal of the wave's rows, or wholly before its sliding window
 // (sinks aside, "Long Context..." §10.1-10.2), are never visited.
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+
 #include "srt_internal.h"
 
 namespace srt {

@@ -11,6 +11,9 @@
 // pairs (x_i, x_{i+D/2}) ("Long Context..." §2.4 code).  HBM-bound:
 // each thread moves 8 elements (one 16-byte bf16 vector or two fp32 vectors)
 // and reads the matching 4 table entries (32 bytes, L2-resident across heads).
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+
 #include "srt_internal.h"
 
 namespace srt {

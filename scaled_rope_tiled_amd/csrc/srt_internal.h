@@ -1,9 +1,11 @@
-// Internal declarations shared by the C-ABI layer (abi.cpp) and the kernel
-// translation units.  Nothing here is part of the public ABI.
+// Internal declarations shared by the C-ABI layer (abi.cpp), the ring schedule
+// (ring.cpp) and the kernel translation units.  Nothing here is part of the
+// public ABI.  Only the runtime API is included, so the host sources also
+// build with a plain C++ compiler (the kernel sources include the device
+// headers themselves).
 #pragma once
 
-#include <hip/hip_runtime.h>
-#include <hip/hip_bf16.h>
+#include <hip/hip_runtime_api.h>
 #include <cstdint>
 
 namespace srt {

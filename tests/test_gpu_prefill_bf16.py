@@ -14,6 +14,7 @@ import torch
 import synth
 from gpu_helpers import device_table, f64, max_abs, need_gpu, oracle_freq, qkv
 from oracle import attention as A
+from oracle import rope as orope
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -92,45 +93,145 @@ def test_repeat_is_bitwise_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-# sm_scale * log2(e) = 1/8 exactly: the kernel's scaling of q is then a power
-# of two (no rounding), so large scores stay comparable at the bf16 bar.
+# sm_scale * log2(e) = 1/8 exactly: scaling by it is a power of two (no
+# rounding anywhere).  SM_REAL is the method's own 1/sqrt(D).  With q and k
+# given as they are (no table) the kernel keeps q exact and scales the scores
+# in fp32, so both scales give the oracle's result up to the final roundings.
 SM_POW2 = 0.125 * math.log(2.0)
+SM_REAL = 1.0 / math.sqrt(128)
+SCALES = pytest.mark.parametrize("sm", [SM_POW2, SM_REAL], ids=["sm_pow2", "sm_real"])
 
 
-def _plain(srt, q, k, v, causal):
-    """q, k taken as already rotated (no table) against the oracle with no rotation."""
-    o, l = srt.attn_prefill(q, k, v, causal=causal, sm_scale=SM_POW2)
-    ro, rl = A.attention(f64(q), f64(k), f64(v), sm_scale=SM_POW2, causal=causal)
+def _plain(srt, q, k, v, causal, sm):
+    """q, k taken as already rotated (no table) against the oracle with no rotation.
+
+    The output is taken in fp32 (the ring's partial-state format): these rows
+    are dominated by one key, so |O| reaches ~4.3, where a bf16 output ulp is
+    2^-5 and its rounding alone reaches 0.0156; with the bf16 rounding of P
+    (the PV operand, relative 2^-9) that can pass 2e-2 without any error in
+    the softmax bookkeeping these tests are about (measured: 0.0276 in bf16,
+    0.0135 in fp32, lse within 1e-5)."""
+    o, l = srt.attn_prefill(q, k, v, causal=causal, sm_scale=sm, out_dtype=torch.float32)
+    ro, rl = A.attention(f64(q), f64(k), f64(v), sm_scale=sm, causal=causal)
     return f64(o), f64(l), ro, rl
 
 
-@pytest.mark.parametrize("causal", [True, False])
-def test_reference_moves_as_scores_grow(causal):
-    """Key c is scaled by 1 + 5c/N, so the row maxima keep rising along the key
-    walk (from ~7 to ~40 in log2 units) and the exponentials' reference must
-    move several times; each move rescales O and the partial sums."""
-    srt = need_gpu()
-    N, D = 640, 128
-    g = torch.Generator().manual_seed(11)
+def _grow_inputs(seed=11, N=640, D=128):
+    g = torch.Generator().manual_seed(seed)
     q = (2.0 * torch.randn(1, 4, N, D, generator=g)).to(torch.bfloat16).cuda()
     ramp = 1.0 + 5.0 * torch.arange(N, dtype=torch.float32) / N
     k = (torch.randn(1, 1, N, D, generator=g) * ramp[None, None, :, None]).to(torch.bfloat16).cuda()
     v = torch.randn(1, 1, N, D, generator=g).to(torch.bfloat16).cuda()
-    o, l, ro, rl = _plain(srt, q, k, v, causal)
+    return q, k, v
+
+
+def _far_inputs(seed=12, N=300, D=128):
+    g = torch.Generator().manual_seed(seed)
+    q = (-4.0 * (1.0 + 0.1 * torch.randn(1, 4, N, D, generator=g))).to(torch.bfloat16).cuda()
+    k = (4.0 * (1.0 + 0.1 * torch.randn(1, 2, N, D, generator=g))).to(torch.bfloat16).cuda()
+    v = torch.randn(1, 2, N, D, generator=g).to(torch.bfloat16).cuda()
+    return q, k, v
+
+
+@SCALES
+@pytest.mark.parametrize("causal", [True, False])
+def test_reference_moves_as_scores_grow(causal, sm):
+    """Key c is scaled by 1 + 5c/N, so the row maxima keep rising along the key
+    walk (from ~7 to ~40 in log2 units) and the exponentials' reference must
+    move several times; each move rescales O and the partial sums."""
+    srt = need_gpu()
+    q, k, v = _grow_inputs()
+    o, l, ro, rl = _plain(srt, q, k, v, causal, sm)
+    print(f"grow causal={causal} sm={sm:.4f}: max|dO|={max_abs(o, ro):.3g} max|dlse|={max_abs(l, rl):.3g}")
     assert max_abs(o, ro) <= TOL and max_abs(l, rl) <= TOL
 
 
+@SCALES
 @pytest.mark.parametrize("causal", [True, False])
-def test_reference_far_below_zero(causal):
+def test_reference_far_below_zero(causal, sm):
     """Every score is near -256 in log2 units: taken against the starting
     reference 0 the exponentials underflow to 0, so the first visible half of
     each row must set the reference from its maximum."""
     srt = need_gpu()
+    q, k, v = _far_inputs()
+    o, l, ro, rl = _plain(srt, q, k, v, causal, sm)
+    print(f"far causal={causal} sm={sm:.4f}: max|dO|={max_abs(o, ro):.3g} max|dlse|={max_abs(l, rl):.3g}")
+    assert np.all(rl < -150)
+    assert max_abs(o, ro) <= TOL and max_abs(l, rl) <= TOL
+
+
+YARN64 = synth.Rope(synth.YARN, 10000.0, 64.0, 64.0, 1.0, 32.0)   # s = 64: mscale 0.1 ln 64 + 1 = 1.416
+
+
+def _rising_inputs(rp, seed, N=640, D=128, S=14.0, G=4, ramp=200):
+    """Raw q, k whose rotated forms are b_c u (key c) and a_r u plus noise
+    (query r): the scores sm_scale q~.k~ climb from about -0.8 S to about S
+    (log2 units) over the first `ramp` keys and stay there, so every row past
+    the ramp moves its reference about twice.  The direction u has entries of
+    random sign and magnitude in [0.5, 1.5], so the bf16 roundings of the
+    rotated operands (relative 2^-9 per entry) do not add up coherently: a
+    score of size |s| then carries an error of about 3e-4 |s|, which keeps
+    |s| <= 20 inside the bf16 bar."""
+    th, ms, _ = oracle_freq(rp, D)
+    rng = np.random.default_rng(seed)
+    u = rng.choice([-1.0, 1.0], D) * rng.uniform(0.5, 1.5, D)
+    c = SM_REAL * math.log2(math.e) * float(u @ u)
+    pos = np.arange(N)
+    b = math.sqrt(S / c) * (-0.8 + 1.8 * np.minimum(1.0, pos / ramp))
+    a = math.sqrt(S / c) * (1.0 + 0.1 * rng.standard_normal((G, N)))
+    # rotation by -p undoes the rotation by p (R_p^T = R_-p); dividing by mscale undoes the temperature
+    k = orope.rotate(b[:, None] * u[None, :], -pos, th) / ms
+    q = np.stack([orope.rotate(a[g][:, None] * u[None, :], -pos, th) / ms for g in range(G)])
+    q = q + 0.3 * rng.standard_normal(q.shape)
+    v = rng.standard_normal((N, D))
+    to = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).cuda()
+    return to(q[None]), to(k[None, None]), to(v[None, None])
+
+
+@pytest.mark.parametrize("mode", ["rotate_qk", "prerotated_k"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_reference_moves_rotated(mode, causal):
+    """The moving reference at the method's own scale 1/sqrt(D) with RoPE on
+    (YaRN s = 64, so the temperature doubles every score): q and k rotated on
+    load, or K rotated once by rope_apply and q on load (the benchmark's
+    launch).  Scores climb from about -11 to +19 in log2 units along the keys."""
+    srt = need_gpu()
+    N, D = 640, 128
+    q, k, v = _rising_inputs(YARN64, 13, N, D)
+    table, _ = device_table(srt, YARN64, D, N)
+    if mode == "rotate_qk":
+        o, l = srt.attn_prefill(q, k, v, causal=causal, table=table)
+    else:
+        kr = srt.rope_apply(k, table)
+        o, l = srt.attn_prefill(q, kr, v, causal=causal, table=table, rope_flags=srt.ROTATE_Q)
+    th, ms, _ = oracle_freq(YARN64, D)
+    ro, rl = A.attention(f64(q), f64(k), f64(v), sm_scale=SM_REAL, causal=causal, theta=th, mscale=ms)
+    o, l = f64(o), f64(l)
+    print(f"rotated {mode} causal={causal}: max|dO|={max_abs(o, ro):.3g} max|dlse|={max_abs(l, rl):.3g} "
+          f"lse in [{rl.min():.1f}, {rl.max():.1f}]")
+    assert rl.max() > 10.0            # the large scores are really there
+    assert max_abs(o, ro) <= TOL and max_abs(l, rl) <= TOL
+
+
+@pytest.mark.parametrize("mode", ["rotate_qk", "prerotated_k"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_reference_far_below_zero_rotating_path(mode, causal):
+    """Scores near -256 (log2 units) through the kernel instances that rotate
+    on load.  The table has zero frequencies and mscale 1 (every rotation is
+    cos 0 = 1, sin 0 = 0) and sm_scale log2(e) = 1/8, so the rotated operands
+    are formed without rounding: at |s| ~ 256 a rounding of the rotated
+    operands alone would move lse by more than the bf16 bar."""
+    srt = need_gpu()
     N, D = 300, 128
-    g = torch.Generator().manual_seed(12)
-    q = (-4.0 * (1.0 + 0.1 * torch.randn(1, 4, N, D, generator=g))).to(torch.bfloat16).cuda()
-    k = (4.0 * (1.0 + 0.1 * torch.randn(1, 2, N, D, generator=g))).to(torch.bfloat16).cuda()
-    v = torch.randn(1, 2, N, D, generator=g).to(torch.bfloat16).cuda()
-    o, l, ro, rl = _plain(srt, q, k, v, causal)
+    q, k, v = _far_inputs(seed=14, N=N, D=D)
+    table = srt.rope_cos_sin(np.zeros(D // 2), D, 1.0, N, "cuda")
+    if mode == "rotate_qk":
+        o, l = srt.attn_prefill(q, k, v, causal=causal, table=table, sm_scale=SM_POW2)
+    else:
+        kr = srt.rope_apply(k, table)
+        assert torch.equal(kr, k)
+        o, l = srt.attn_prefill(q, kr, v, causal=causal, table=table, rope_flags=srt.ROTATE_Q, sm_scale=SM_POW2)
+    ro, rl = A.attention(f64(q), f64(k), f64(v), sm_scale=SM_POW2, causal=causal, theta=np.zeros(D // 2))
+    o, l = f64(o), f64(l)
     assert np.all(rl < -150)
     assert max_abs(o, ro) <= TOL and max_abs(l, rl) <= TOL

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 @pytest.fixture(scope="module")
 def srt():
-    if not os.path.exists(os.environ.get("SRT_LIB", os.path.join(ROOT, "scaled_rope_tiled_amd", "libsrt.so"))):
+    if not os.path.exists(os.path.join(ROOT, "scaled_rope_tiled_amd", "libsrt.so")):
         import __graft_entry__
         __graft_entry__.build()
     import scaled_rope_tiled_amd as m
@@ -218,3 +218,63 @@ def test_empty_problems_return_ok_without_pointers(srt):
     assert lib.srt_attn_prefill(None, None, None, 1, 1, 4, 2, -1, 64, 128, 0, 0, 0, 0, 1, 0, 0, 0.1,
                                 None, 0, 0, None, 1, 0, None, 0, None) == 1
     assert lib.srt_attn_merge_states(None, None, None, None, 0, 0, None, 1, 0, None, 0, 1, -4, 0, 128, None) == 1
+
+
+def test_prefill_rejects_misaligned_pointers_and_strides(srt):
+    """The kernels move q/k/v/out rows and table entries in 16-byte vectors:
+    a base pointer off a 16-byte boundary or a head stride that is not a
+    multiple of 8 elements is SRT_ERR_INVALID before anything is enqueued."""
+    lib = srt.lib()
+    good = C.c_void_p(0x100000)
+    odd = C.c_void_p(0x100008)         # 8-byte aligned only
+    call = lambda q, k, v, out, tab, flags, qs, ks, os_: lib.srt_attn_prefill(
+        q, k, v, 1, 1, 4, 2, 8, 8, 128, qs, ks, 0, 0, 1, 0, 0, 0.1, tab, 64 if tab else 0, flags, out, 1, os_,
+        None, 0, None)
+    for args in ((odd, good, good, good, None, 0), (good, odd, good, good, None, 0),
+                 (good, good, odd, good, None, 0), (good, good, good, odd, None, 0),
+                 (good, good, good, good, odd, 1)):
+        assert call(*args, 1024, 1024, 1024) == 1 and b"aligned" in lib.srt_last_error(), args
+    for qs, ks, os_ in ((1028, 1024, 1024), (1024, 1028, 1024), (1024, 1024, 1028)):
+        assert call(good, good, good, good, None, 0, qs, ks, os_) == 1
+        assert b"multiples of 8" in lib.srt_last_error()
+
+
+def test_binding_rejects_host_tensors_and_wrong_tables(srt):
+    """The binding hands raw pointers to the library: every tensor must be on
+    q's GPU and the table must be a contiguous fp32 [npos, D/2, 2] for this D.
+    Host (CPU) tensors fail before any call, with no GPU in this process."""
+    import torch
+    q = torch.zeros(1, 4, 8, 128, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="cpu"):
+        srt.attn_prefill(q, k, k)
+    with pytest.raises(ValueError, match="cpu"):
+        srt.rope_apply(k, torch.zeros(8, 64, 2))
+    with pytest.raises(ValueError, match="cpu"):
+        srt.attn_decode_splitk(q[:, :, 0].contiguous(), k, k, num_splits=2)
+
+    class FakeCuda:
+        """Stands in for a device tensor so the table-shape checks run without a GPU."""
+        def __init__(self, shape, dtype=torch.float32, contiguous=True):
+            self.shape, self.dtype, self._c = torch.Size(shape), dtype, contiguous
+            self.is_cuda, self.device = True, torch.device("cuda:0")
+
+        def is_contiguous(self):
+            return self._c
+
+        def dim(self):
+            return len(self.shape)
+
+        def data_ptr(self):
+            return 0x100000
+
+    dev = torch.device("cuda:0")
+    assert srt._table(FakeCuda((64, 64, 2)), 128, dev)[1] == 64
+    for bad in (FakeCuda((64, 32, 2)), FakeCuda((64, 64, 2), torch.float16), FakeCuda((64, 64, 2), contiguous=False),
+                FakeCuda((64, 128))):
+        with pytest.raises(ValueError, match="table"):
+            srt._table(bad, 128, dev)
+    with pytest.raises(ValueError, match="cuda:1"):
+        other = FakeCuda((64, 64, 2))
+        other.device = torch.device("cuda:1")
+        srt._table(other, 128, dev)
