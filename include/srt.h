@@ -252,6 +252,28 @@ int srt_attn_decode_splitk(const void* q, const void* k_cache, const void* v_cac
                            void* out, float* lse, void* stream);
 
 /*
+ * srt_attn_decode_splitk_noalloc - srt_attn_decode_splitk for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, meaning, layouts
+ * and results as srt_attn_decode_splitk, without the workspace: the split
+ * partials go to a static device array of the library (one per GPU, kept until
+ * the process ends) of srt_attn_decode_noalloc_max_workspace() bytes
+ * (32 MiB).  Calls whose partials need more,
+ * B * Hq * num_splits * (D + 1) * 4 bytes, return SRT_ERR_WORKSPACE with no
+ * side effects.  The call makes no allocation (no hipMalloc, hipFree or
+ * allocating library routine).  All calls on one GPU share that GPU's array:
+ * calls that overlap on one GPU (e.g. on two streams) race and must be
+ * ordered by the caller.
+ */
+int srt_attn_decode_splitk_noalloc(const void* q, const void* k_cache, const void* v_cache, int dtype,
+                                   int B, int Hq, int Hkv, int Nk, int D, const int* seq_lens_dev,
+                                   int num_splits, float sm_scale, const float* table_dev, long long table_npos,
+                                   int pairing, int window, int sink, void* out, float* lse, void* stream);
+
+/* Bytes of the static scratch of srt_attn_decode_splitk_noalloc (its size limit). */
+size_t srt_attn_decode_noalloc_max_workspace(void);
+
+/*
  * srt_attn_backward_workspace_size - bytes of workspace srt_attn_backward
  * needs for these arguments: delta = rowsum(dO * O), fp32 [B][Hq][Nq], and
  * for BF16 a copy of q ([B][Hq][Nq][D], rotated with SRT_ROTATE_Q, always

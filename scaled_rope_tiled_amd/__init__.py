@@ -13,6 +13,7 @@ HIP stream; every step of the computation runs in the library's kernels.
     attn_prefill(q, k, v, ...)                        -> (out, lse)
     attn_merge_states(o_a, lse_a, o_b, lse_b, ...)    -> (out, lse)
     attn_decode_splitk(q, k_cache, v_cache, ...)      -> (out, lse)
+    attn_decode_splitk_noalloc(q, k_cache, v_cache, ...) -> (out, lse), no workspace
     attn_ring_prefill(q, k, v, num_devices=, partition=, ...) -> (out, lse)
     attn_backward(q, k, v, out, dout, lse, ...)      -> (dq, dk, dv) fp32
     attn_backward_workspace_size(dtype, B, Hq, Hkv, Nq, Nk, D, rope_flags) -> bytes
@@ -35,7 +36,8 @@ PARTITIONS = {"contiguous": 0, "striped": 1, "zigzag": 2}
 BAND_LOW, BAND_MID, BAND_HIGH = 0, 1, 2
 
 __all__ = ["rope_inv_freq", "rope_inv_freq_dynamic_ntk", "rope_inv_freq_factors", "rope_cos_sin", "rope_apply", "attn_prefill", "attn_merge_states",
-           "attn_decode_splitk", "attn_decode_workspace_size", "attn_ring_prefill", "attn_ring_workspace_size",
+           "attn_decode_splitk", "attn_decode_workspace_size", "attn_decode_splitk_noalloc",
+           "attn_decode_noalloc_max_workspace", "attn_ring_prefill", "attn_ring_workspace_size",
            "attn_backward", "attn_backward_workspace_size", "NONE", "PI", "NTK", "YARN",
            "ROTATE_Q", "ROTATE_K", "PAIR_HALF", "PAIRING_INTERLEAVED", "PAIRING_HALF", "lib"]
 
@@ -290,6 +292,42 @@ def attn_decode_splitk(q, k_cache, v_cache, *, num_splits: int, sm_scale: float 
                                             workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
                                             _stream(q.device)), "attn_decode_splitk")
     return out, lse
+
+
+def attn_decode_splitk_noalloc(q, k_cache, v_cache, *, num_splits: int, sm_scale: float | None = None,
+                               table: torch.Tensor | None = None, seq_lens: torch.Tensor | None = None,
+                               out=None, lse=True, pairing="interleaved", window: int = 0, sink: int = 0):
+    """attn_decode_splitk without a workspace: the split partials go to the
+    library's static per-GPU scratch (no device allocation in the call, at most
+    srt_attn_decode_noalloc_max_workspace() bytes of partials).  Calls that
+    overlap on one GPU share that scratch and must be ordered by the caller.
+    Pass `out` (and `lse`, or lse=False) to make the whole call allocation-free."""
+    B, Hq, D = q.shape
+    _, Hkv, Nk, _ = k_cache.shape
+    for t in (q, k_cache, v_cache):
+        if not t.is_contiguous():
+            raise ValueError("decode tensors must be contiguous")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=q.dtype, device=q.device)
+    if lse is True:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    elif lse is False:
+        lse = None
+    if seq_lens is not None and (seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous()):
+        raise ValueError("seq_lens must be contiguous int32 [B]")
+    _on_device(q.device, q=q, k_cache=k_cache, v_cache=v_cache, seq_lens=seq_lens, out=out, lse=lse)
+    tp, npos = _table(table, D, q.device)
+    sm = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
+    _lib.check(lib().srt_attn_decode_splitk_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _dt(q), B, Hq, Hkv, Nk,
+                                                    D, _ptr(seq_lens), int(num_splits), sm, tp, npos,
+                                                    _pairing(pairing), int(window), int(sink), _ptr(out), _ptr(lse),
+                                                    _stream(q.device)), "attn_decode_splitk_noalloc")
+    return out, lse
+
+
+def attn_decode_noalloc_max_workspace() -> int:
+    """Bytes of split partials attn_decode_splitk_noalloc can hold."""
+    return int(lib().srt_attn_decode_noalloc_max_workspace())
 
 
 def _partition(p) -> int:

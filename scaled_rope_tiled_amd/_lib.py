@@ -41,6 +41,11 @@ SIGNATURES = {
                                c_int, c_int, c_int, c_int, c_int, c_void_p,
                                c_int, c_float, c_void_p, c_ll, c_int, c_int, c_int,
                                c_void_p, c_size_t, c_void_p, c_void_p, c_void_p],
+    "srt_attn_decode_splitk_noalloc": [c_void_p, c_void_p, c_void_p, c_int,
+                                       c_int, c_int, c_int, c_int, c_int, c_void_p,
+                                       c_int, c_float, c_void_p, c_ll, c_int, c_int, c_int,
+                                       c_void_p, c_void_p, c_void_p],
+    "srt_attn_decode_noalloc_max_workspace": [],
     "srt_attn_backward_workspace_size": [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                          C.POINTER(c_size_t)],
     "srt_attn_backward": [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int,
@@ -71,7 +76,8 @@ def load(path: str = LIB_PATH):
     for name, args in SIGNATURES.items():
         fn = getattr(lib, name)
         fn.argtypes = args
-        fn.restype = c_char_p if name in ("srt_status_string", "srt_last_error") else c_int
+        fn.restype = (c_char_p if name in ("srt_status_string", "srt_last_error")
+                      else c_size_t if name == "srt_attn_decode_noalloc_max_workspace" else c_int)
     _lib = lib
     return lib
 

@@ -257,14 +257,18 @@ int srt_attn_decode_workspace_size(int B, int Hq, int D, int num_splits, size_t*
   return ok();
 }
 
-int srt_attn_decode_splitk(const void* q, const void* k_cache, const void* v_cache, int dtype, int B, int Hq,
-                           int Hkv, int Nk, int D, const int* seq_lens_dev, int num_splits, float sm_scale,
-                           const float* table_dev, long long table_npos, int pairing, int window, int sink,
-                           void* workspace,
-                           size_t workspace_bytes, void* out, float* lse, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the two decode entry points; fills everything of `a` but
+// the workspace pointers.
+int decode_args(const void* q, const void* k_cache, const void* v_cache, int dtype, int B, int Hq, int Hkv, int Nk,
+                int D, const int* seq_lens_dev, int num_splits, float sm_scale, const float* table_dev,
+                long long table_npos, int pairing, int window, int sink, void* out, float* lse, srt::DecodeArgs& a) {
   if (!valid_dtype(dtype)) return fail(SRT_ERR_INVALID, "attn_decode_splitk: bad dtype");
   if (B < 0 || Hq < 1 || Hkv < 1 || Nk < 0) return fail(SRT_ERR_INVALID, "attn_decode_splitk: bad sizes");
-  if (B == 0) return ok();                     // no sequence: pointers may be NULL
+  if (B == 0) return SRT_OK;                   // no sequence: pointers may be NULL
   if (!q || !out) return fail(SRT_ERR_INVALID, "attn_decode_splitk: NULL q or out");
   if (Nk > 0 && (!k_cache || !v_cache)) return fail(SRT_ERR_INVALID, "attn_decode_splitk: NULL cache pointer");
   if (Hq % Hkv) return fail(SRT_ERR_INVALID, "attn_decode_splitk: Hq not a multiple of Hkv");
@@ -285,16 +289,9 @@ int srt_attn_decode_splitk(const void* q, const void* k_cache, const void* v_cac
   }
   if (misaligned16(q) || misaligned16(k_cache) || misaligned16(v_cache) || misaligned16(table_dev))
     return fail(SRT_ERR_INVALID, "attn_decode_splitk: tensors must be 16-byte aligned");
-  const size_t need = srt::decode_workspace_bytes(B, Hq, D, num_splits);
-  if (B > 0 && (!workspace || workspace_bytes < need))
-    return fail(SRT_ERR_WORKSPACE, "attn_decode_splitk: workspace %zu bytes, need %zu", workspace_bytes, need);
-  if (((uintptr_t)workspace) & 15) return fail(SRT_ERR_INVALID, "attn_decode_splitk: workspace not 16-byte aligned");
-  if (B == 0) return ok();
-  srt::DecodeArgs a{};
+  a = srt::DecodeArgs{};
   a.q = q; a.k = k_cache; a.v = v_cache; a.seq_lens = seq_lens_dev; a.table = table_dev;
   a.half_pairs = pairing == SRT_PAIRING_HALF;
-  a.ws_o = (float*)workspace;
-  a.ws_lse = (float*)((char*)workspace + (size_t)B * Hq * num_splits * D * sizeof(float));
   a.out = out; a.lse = lse;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nk = Nk; a.D = D; a.splits = num_splits;
   a.window = window; a.sink = window > 0 ? sink : 0;
@@ -304,7 +301,55 @@ int srt_attn_decode_splitk(const void* q, const void* k_cache, const void* v_cac
     a.split_len = (int)((span + num_splits - 1) / num_splits);
   }
   a.sm_scale = sm_scale;
+  return SRT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int srt_attn_decode_splitk(const void* q, const void* k_cache, const void* v_cache, int dtype, int B, int Hq,
+                           int Hkv, int Nk, int D, const int* seq_lens_dev, int num_splits, float sm_scale,
+                           const float* table_dev, long long table_npos, int pairing, int window, int sink,
+                           void* workspace,
+                           size_t workspace_bytes, void* out, float* lse, void* stream) {
+  srt::DecodeArgs a;
+  const int st = decode_args(q, k_cache, v_cache, dtype, B, Hq, Hkv, Nk, D, seq_lens_dev, num_splits, sm_scale,
+                             table_dev, table_npos, pairing, window, sink, out, lse, a);
+  if (st != SRT_OK) return st;
+  if (B == 0) return ok();
+  const size_t need = srt::decode_workspace_bytes(B, Hq, D, num_splits);
+  if (!workspace || workspace_bytes < need)
+    return fail(SRT_ERR_WORKSPACE, "attn_decode_splitk: workspace %zu bytes, need %zu", workspace_bytes, need);
+  if (((uintptr_t)workspace) & 15) return fail(SRT_ERR_INVALID, "attn_decode_splitk: workspace not 16-byte aligned");
+  a.ws_o = (float*)workspace;
+  a.ws_lse = (float*)((char*)workspace + (size_t)B * Hq * num_splits * D * sizeof(float));
   return hip_status(srt::launch_decode(a, (hipStream_t)stream), "attn_decode_splitk launch");
+}
+
+size_t srt_attn_decode_noalloc_max_workspace(void) { return srt::kDecodeScratchBytes; }
+
+int srt_attn_decode_splitk_noalloc(const void* q, const void* k_cache, const void* v_cache, int dtype, int B, int Hq,
+                                   int Hkv, int Nk, int D, const int* seq_lens_dev, int num_splits, float sm_scale,
+                                   const float* table_dev, long long table_npos, int pairing, int window, int sink,
+                                   void* out, float* lse, void* stream) {
+  srt::DecodeArgs a;
+  const int st = decode_args(q, k_cache, v_cache, dtype, B, Hq, Hkv, Nk, D, seq_lens_dev, num_splits, sm_scale,
+                             table_dev, table_npos, pairing, window, sink, out, lse, a);
+  if (st != SRT_OK) return st;
+  if (B == 0) return ok();
+  const size_t need = srt::decode_workspace_bytes(B, Hq, D, num_splits);
+  if (need > srt::kDecodeScratchBytes)
+    return fail(SRT_ERR_WORKSPACE,
+                "attn_decode_splitk_noalloc: the split partials need %zu bytes, above the %zu-byte static scratch "
+                "(B * Hq * num_splits * (D + 1) * 4 bytes); use fewer splits or srt_attn_decode_splitk", need,
+                srt::kDecodeScratchBytes);
+  void* scratch = nullptr;
+  const hipError_t e = srt::decode_scratch(&scratch);
+  if (e != hipSuccess) return hip_status(e, "attn_decode_splitk_noalloc: scratch address");
+  a.ws_o = (float*)scratch;
+  a.ws_lse = (float*)((char*)scratch + (size_t)B * Hq * num_splits * D * sizeof(float));
+  return hip_status(srt::launch_decode(a, (hipStream_t)stream), "attn_decode_splitk_noalloc launch");
 }
 
 namespace {

@@ -26,6 +26,8 @@
 
 #include "srt_internal.h"
 
+#include <mutex>
+
 namespace srt {
 namespace {
 
@@ -282,6 +284,38 @@ __global__ void __launch_bounds__(128) decode_combine_kernel(DecodeArgs a) {
 }
 
 }  // namespace
+
+// Scratch of srt_attn_decode_splitk_noalloc: the split partials (fp32 O and
+// lse of every split) live in this file-scope device array instead of a
+// caller workspace, for callers that cannot allocate.  Each GPU holds its own
+// copy for the life of the process, at its own address; in host code the
+// array's name is only a stand-in, so its device address is looked up once
+// per device with hipGetSymbolAddress and the kernels receive that address.
+// Every call on a GPU shares that GPU's copy (calls that overlap on one GPU
+// race); nothing in it needs clearing, as the split kernel writes every slot
+// the combine kernel reads.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));     // with device `dev` current
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 size_t decode_workspace_bytes(int B, int Hq, int D, int splits) {
   return (size_t)B * Hq * splits * (size_t)(D + 1) * sizeof(float);

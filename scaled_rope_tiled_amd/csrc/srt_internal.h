@@ -97,6 +97,12 @@ struct DecodeArgs {
 size_t decode_workspace_bytes(int B, int Hq, int D, int splits);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
+// Static device scratch of the allocation-free decode entry point (one copy
+// per GPU, in decode.hip): its size, and its address on the current device
+// (looked up once per device, then cached).
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+hipError_t decode_scratch(void** ptr);
+
 // ---------------------------------------------------------------- backward
 struct BwdArgs {
   const void* q;          // [B][Hq][Nq][D] dtype, raw (rotated on load with ROTATE_Q)

@@ -278,3 +278,23 @@ def test_binding_rejects_host_tensors_and_wrong_tables(srt):
         other = FakeCuda((64, 64, 2))
         other.device = torch.device("cuda:1")
         srt._table(other, 128, dev)
+
+
+def test_noalloc_decode_rejects_oversize_before_any_gpu_call(srt):
+    """The allocation-free decode holds at most its static scratch of split
+    partials: a larger problem is SRT_ERR_WORKSPACE before anything runs (this
+    process has no GPU); an empty problem is a no-op."""
+    lib = srt.lib()
+    cap = lib.srt_attn_decode_noalloc_max_workspace()
+    assert cap == 32 << 20
+    fake = C.c_void_p(0x100000)
+    # 16 x 32 x 64 splits x 129 x 4 = 16.9 MB fits; 64 x 32 x 64 x 129 x 4 = 67.6 MB does not
+    st = lib.srt_attn_decode_splitk_noalloc(fake, fake, fake, 1, 64, 32, 8, 1024, 128, None, 64, 0.1, None, 0,
+                                            0, 0, 0, fake, None, None)
+    assert st == 4 and b"static scratch" in lib.srt_last_error()
+    st = lib.srt_attn_decode_splitk_noalloc(None, None, None, 1, 0, 32, 8, 1024, 128, None, 64, 0.1, None, 0,
+                                            0, 0, 0, None, None, None)
+    assert st == 0
+    st = lib.srt_attn_decode_splitk_noalloc(fake, fake, fake, 1, 16, 24, 8, 1024, 128, None, 64, 0.1, None, 0,
+                                            0, 0, 0, fake, None, None)
+    assert st == 2
