@@ -535,15 +535,39 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   const float lt = pair_sum(l_run);
   const int row = wrow0 + l32;
   if (row < a.Nq) {
-    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    float lse_row = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -INFINITY;
     const long long obase = ((long long)b * a.Hq + hq) * a.o_hstride + (long long)row * kD;
+    float wa = 0.f;                 // weight of the running state (ring step)
+    const float* accp = nullptr;
+    if (a.acc_o) {
+      // fold this launch's (O, lse) into the running state by the log-sum-exp
+      // rule: lse = log(e^la + e^lb), O = e^(la-lse) O_a + e^(lb-lse) O_b
+      // ("8.3 长上下文技术" §8.3.5: a ring step rescales the running result)
+      const float la = a.acc_lse[((long long)b * a.Hq + hq) * a.acc_lse_hstride + row];
+      const float mx = fmaxf(la, lse_row);
+      if (mx == -INFINITY) {
+        inv = 0.f;
+      } else {
+        const float ea = __expf(la - mx), eb = __expf(lse_row - mx);   // exp(-inf) = 0
+        const float rs = 1.0f / (ea + eb);
+        wa = ea * rs;
+        inv *= eb * rs;
+        lse_row = mx + __logf(ea + eb);
+      }
+      accp = a.acc_o + ((long long)b * a.Hq + hq) * a.acc_hstride + (long long)row * kD;
+    }
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d = db * 32 + g4 * 8 + hl * 4;
-        const float o0 = oacc[db][g4 * 4 + 0] * inv, o1 = oacc[db][g4 * 4 + 1] * inv;
-        const float o2 = oacc[db][g4 * 4 + 2] * inv, o3 = oacc[db][g4 * 4 + 3] * inv;
+        float o0 = oacc[db][g4 * 4 + 0] * inv, o1 = oacc[db][g4 * 4 + 1] * inv;
+        float o2 = oacc[db][g4 * 4 + 2] * inv, o3 = oacc[db][g4 * 4 + 3] * inv;
+        if (accp) {
+          const float4 p = *reinterpret_cast<const float4*>(accp + d);
+          o0 = fmaf(wa, p.x, o0); o1 = fmaf(wa, p.y, o1); o2 = fmaf(wa, p.z, o2); o3 = fmaf(wa, p.w, o3);
+        }
         if (a.out_bf16) {
           *reinterpret_cast<uint2*>(reinterpret_cast<__hip_bfloat16*>(a.out) + obase + d) =
               make_uint2(pack2(o0, o1), pack2(o2, o3));
@@ -552,8 +576,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
         }
       }
     }
-    if (a.lse && hl == 0)
-      a.lse[((long long)b * a.Hq + hq) * a.lse_hstride + row] = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -INFINITY;
+    if (a.lse && hl == 0) a.lse[((long long)b * a.Hq + hq) * a.lse_hstride + row] = lse_row;
   }
 }
 

@@ -150,7 +150,27 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillArgs a) {
     m = mnew;
   }
   if (!row_ok) return;
-  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  float inv = l > 0.f ? 1.0f / l : 0.f;
+  float lse_row = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+  if (a.acc_o) {
+    // one ring step: fold (O, lse) into the running state by the log-sum-exp
+    // rule ("8.3 长上下文技术" §8.3.5), in place when out is the state itself
+    const float la = a.acc_lse[((long long)b * a.Hq + h) * a.acc_lse_hstride + r];
+    const float mx = fmaxf(la, lse_row);
+    float wa = 0.f;
+    if (mx == -INFINITY) {
+      inv = 0.f;
+    } else {
+      const float ea = expf(la - mx), eb = expf(lse_row - mx);
+      wa = ea / (ea + eb);
+      inv *= eb / (ea + eb);
+      lse_row = mx + logf(ea + eb);
+    }
+    const float* ap = a.acc_o + ((long long)b * a.Hq + h) * a.acc_hstride + (long long)r * D;
+#pragma unroll
+    for (int d = 0; d < D; ++d) o[d] = fmaf(wa, ap[d], o[d] * inv);
+    inv = 1.0f;
+  }
   if (a.out_bf16) {
     __hip_bfloat16* og = reinterpret_cast<__hip_bfloat16*>(a.out) + ((long long)b * a.Hq + h) * a.o_hstride +
                          (long long)r * D;
@@ -161,8 +181,7 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillArgs a) {
 #pragma unroll
     for (int d = 0; d < D; ++d) og[d] = o[d] * inv;
   }
-  if (a.lse)
-    a.lse[((long long)b * a.Hq + h) * a.lse_hstride + r] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+  if (a.lse) a.lse[((long long)b * a.Hq + h) * a.lse_hstride + r] = lse_row;
 }
 
 }  // namespace

@@ -13,7 +13,11 @@
 // that GPU of a real ring would compute).  Each (query run, key run) pair is
 // one launch of the tiled prefill kernel at the runs' true positions, so the
 // causal mask, the window and the sinks come out exactly; pairs with no
-// visible key are not launched.  Striped shards have positions r + P t: the
+// visible key are not launched.  The first launch of a query run writes its
+// (O, lse) as the run's fp32 running state; every later launch folds its own
+// result into that state in its epilogue (log-sum-exp rule, in place), and
+// the last one writes the merged state to the output rows, so no partial is
+// written out and read back by a separate merge.  Striped shards have positions r + P t: the
 // mask of a pair is then the causal mask in row-index space, shifted by one
 // row when the key shard's device comes after the query shard's, and RoPE uses
 // the strided positions.  K is rotated once, into the workspace, at its
@@ -68,7 +72,7 @@ size_t ring_workspace_bytes(const RingArgs& a) {
   const size_t R = a.mode == kZigzag ? C / 2 : C;
   size_t n = 0;
   if (a.rope_flags & 2) n += up((size_t)a.B * a.Hkv * a.N * a.D * elt);
-  n += 2 * (up((size_t)a.B * a.Hq * R * a.D * 4) + up((size_t)a.B * a.Hq * R * 4));
+  n += up((size_t)a.B * a.Hq * R * a.D * 4) + up((size_t)a.B * a.Hq * R * 4);
   return n;
 }
 
@@ -88,13 +92,10 @@ hipError_t ring_prefill(const RingArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     kk = krot;
   }
+  // running state of the current query run: fp32 O and lse
   float* acc_o = reinterpret_cast<float*>(ws);
   ws += up((size_t)a.B * a.Hq * R * a.D * 4);
   float* acc_l = reinterpret_cast<float*>(ws);
-  ws += up((size_t)a.B * a.Hq * R * 4);
-  float* tmp_o = reinterpret_cast<float*>(ws);
-  ws += up((size_t)a.B * a.Hq * R * a.D * 4);
-  float* tmp_l = reinterpret_cast<float*>(ws);
 
   const char* qb = static_cast<const char*>(a.q);
   const char* kb = static_cast<const char*>(kk);
@@ -102,8 +103,9 @@ hipError_t ring_prefill(const RingArgs& a, hipStream_t stream) {
   char* ob = static_cast<char*>(a.out);
   const long long hs = (long long)a.N * a.D;    // head stride of q, k, v, out
 
+  // merge: fold the launch's result into the running state (acc_o, acc_l)
   auto prefill = [&](const Run& q, const Run& k, int r, int j, void* out, bool out_bf16, long long o_hstride,
-                     float* lse, long long lse_hstride) {
+                     float* lse, long long lse_hstride, bool merge) {
     PrefillArgs p{};
     p.q = qb + q.row0 * a.D * elt;
     p.k = kb + k.row0 * a.D * elt;
@@ -127,14 +129,11 @@ hipError_t ring_prefill(const RingArgs& a, hipStream_t stream) {
     p.out_bf16 = out_bf16 ? 1 : 0;
     p.window = a.window; p.sink = a.window > 0 ? a.sink : 0;
     p.sm_scale = a.sm_scale;
+    if (merge) {
+      p.acc_o = acc_o; p.acc_lse = acc_l;
+      p.acc_hstride = (long long)R * a.D; p.acc_lse_hstride = (long long)R;
+    }
     return a.bf16 ? launch_prefill_bf16_d128(p, stream) : launch_prefill_f32(p, stream);
-  };
-  auto merge = [&](void* out, bool out_bf16, long long out_hstride, float* lse_out, long long lse_hstride) {
-    MergeArgs m{};
-    m.oa = acc_o; m.la = acc_l; m.ob = tmp_o; m.lb = tmp_l; m.oo = out; m.lo = lse_out;
-    m.in_hstride = (long long)R * a.D; m.out_hstride = out_hstride; m.lse_out_hstride = lse_hstride;
-    m.BH = a.B * a.Hq; m.N = (int)R; m.D = a.D; m.in_bf16 = 0; m.out_bf16 = out_bf16 ? 1 : 0;
-    return launch_merge(m, stream);
   };
 
   const int r_lo = a.device >= 0 ? a.device : 0, r_hi = a.device >= 0 ? a.device + 1 : a.P;
@@ -156,24 +155,17 @@ hipError_t ring_prefill(const RingArgs& a, hipStream_t stream) {
       float* lse = a.lse ? a.lse + q.row0 : nullptr;
       hipError_t e = hipSuccess;
       if (todo.empty()) {              // no visible key (not reachable under a causal mask): O = 0, lse = -inf
-        e = prefill(q, Run{0, 0, 0, q.step}, r, r, out, a.bf16, hs, lse, a.N);
-        if (e != hipSuccess) return e;
-        continue;
-      }
-      if (todo.size() == 1) {          // one partial: it is the result
-        e = prefill(q, todo[0].first, r, todo[0].second, out, a.bf16, hs, lse, a.N);
+        e = prefill(q, Run{0, 0, 0, q.step}, r, r, out, a.bf16, hs, lse, a.N, false);
         if (e != hipSuccess) return e;
         continue;
       }
       for (size_t i = 0; i < todo.size() && e == hipSuccess; ++i) {
-        if (i == 0) {
-          e = prefill(q, todo[i].first, r, todo[i].second, acc_o, false, (long long)R * a.D, acc_l, (long long)R);
-          continue;
-        }
-        e = prefill(q, todo[i].first, r, todo[i].second, tmp_o, false, (long long)R * a.D, tmp_l, (long long)R);
-        if (e != hipSuccess) break;
-        e = (i + 1 < todo.size()) ? merge(acc_o, false, (long long)R * a.D, acc_l, (long long)R)
-                                  : merge(out, a.bf16, hs, lse, a.N);
+        const bool last = i + 1 == todo.size();
+        // the last launch writes the merged result to the output rows, the
+        // others keep the running state in the workspace
+        e = last ? prefill(q, todo[i].first, r, todo[i].second, out, a.bf16, hs, lse, a.N, i > 0)
+                 : prefill(q, todo[i].first, r, todo[i].second, acc_o, false, (long long)R * a.D, acc_l,
+                           (long long)R, i > 0);
       }
       if (e != hipSuccess) return e;
     }

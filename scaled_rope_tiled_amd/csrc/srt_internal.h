@@ -57,6 +57,16 @@ struct PrefillArgs {
   int window;           // > 0: key j visible to query i only if i - j < window or j < sink
   int sink;             // first positions kept visible (used only with a window)
   float sm_scale;
+  // One Ring Attention step: with acc_o set, the launch's own (O, lse) is
+  // folded into the running state (acc_o fp32 [B][Hq][Nq][D], acc_lse fp32
+  // [B][Hq][Nq], head strides acc_hstride / acc_lse_hstride) by the
+  // log-sum-exp rule and the merged state is what goes to out / lse, which
+  // may be acc_o / acc_lse themselves (in place: each lane reads the elements
+  // it then writes).  acc_lse must be set with acc_o; lse may be NULL (then
+  // only O is written).
+  const float* acc_o;
+  const float* acc_lse;
+  long long acc_hstride, acc_lse_hstride;
 };
 
 hipError_t launch_prefill_bf16_d128(const PrefillArgs& a, hipStream_t stream);

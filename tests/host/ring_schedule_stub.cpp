@@ -16,7 +16,7 @@ static int g_nbuf = 0;
 
 static void name_ptr(const void* p, const char** name, long long* off) {
   const char* c = static_cast<const char*>(p);
-  *name = "?";
+  *name = p ? "?" : "none";
   *off = -1;
   for (int i = 0; i < g_nbuf; ++i)
     if (c >= g_base[i] && c < g_base[i] + (1LL << 36)) { *name = g_name[i]; *off = c - g_base[i]; }
@@ -34,18 +34,21 @@ hipError_t launch_rope_apply(const void* x, void* y, bool bf16, bool half_pairs,
 }
 
 static hipError_t log_prefill(const PrefillArgs& a, const char* kind) {
-  const char *nq, *nk, *nv, *no, *nl;
-  long long oq, ok, ov, oo, ol;
+  const char *nq, *nk, *nv, *no, *nl, *na, *nal;
+  long long oq, ok, ov, oo, ol, oa, oal;
   name_ptr(a.q, &nq, &oq);
   name_ptr(a.k, &nk, &ok);
   name_ptr(a.v, &nv, &ov);
   name_ptr(a.out, &no, &oo);
   name_ptr(a.lse, &nl, &ol);
-  printf("prefill %s q=%s:%lld k=%s:%lld v=%s:%lld out=%s:%lld lse=%s:%lld Nq=%d Nk=%d qp=%lld kp=%lld qr=%lld kr=%lld "
-         "step=%lld qhs=%lld kvhs=%lld ohs=%lld lhs=%lld flags=%d obf16=%d window=%d sink=%d causal=%d\n",
-         kind, nq, oq, nk, ok, nv, ov, no, oo, nl, ol, a.Nq, a.Nk, a.q_pos0, a.k_pos0, a.q_rope0, a.k_rope0,
-         a.rope_step, a.q_hstride, a.kv_hstride, a.o_hstride, a.lse_hstride, a.rope_flags, a.out_bf16, a.window,
-         a.sink, a.causal);
+  name_ptr(a.acc_o, &na, &oa);
+  name_ptr(a.acc_lse, &nal, &oal);
+  printf("prefill %s q=%s:%lld k=%s:%lld v=%s:%lld out=%s:%lld lse=%s:%lld acc=%s:%lld acclse=%s:%lld Nq=%d Nk=%d "
+         "qp=%lld kp=%lld qr=%lld kr=%lld step=%lld qhs=%lld kvhs=%lld ohs=%lld lhs=%lld ahs=%lld alhs=%lld "
+         "flags=%d obf16=%d window=%d sink=%d causal=%d\n",
+         kind, nq, oq, nk, ok, nv, ov, no, oo, nl, ol, na, oa, nal, oal, a.Nq, a.Nk, a.q_pos0, a.k_pos0, a.q_rope0,
+         a.k_rope0, a.rope_step, a.q_hstride, a.kv_hstride, a.o_hstride, a.lse_hstride, a.acc_hstride,
+         a.acc_lse_hstride, a.rope_flags, a.out_bf16, a.window, a.sink, a.causal);
   return hipSuccess;
 }
 

@@ -5,9 +5,11 @@ launcher stubs print every launch instead of running it.  From the printed
 launches the test rebuilds which (query row, key row) pairs the schedule
 scores, each under its launch's own mask, and compares them with the oracle's
 visible pairs at the partition's true positions: every visible pair exactly
-once, nothing else.  It also checks the partial-state chain (first partial,
-then tmp + merge, the last merge into the output rows) and the RoPE
-positions each launch is given."""
+once, nothing else.  It also checks the running-state chain of every query
+run (the first launch writes the fp32 state, each later launch folds its
+result into that state in its epilogue, in place, and the last one writes the
+merged result to the run's output rows) and the RoPE positions each launch is
+given."""
 import os
 import re
 import subprocess
@@ -69,7 +71,6 @@ def test_schedule_scores_every_visible_pair_once(stub, mode, P, N, window, sink,
     want[~rows] = 0
     got = np.zeros((N, N), dtype=int)
     chains = {}
-    last_q0 = None
     for ln in lines[1:]:
         kv = _kv(ln)
         if ln.startswith("rope"):
@@ -89,27 +90,28 @@ def test_schedule_scores_every_visible_pair_once(stub, mode, P, N, window, sink,
             assert int(kv["qr"]) == pos[q0] and int(kv["kr"]) == pos[k0]
             assert all(pos[q0 + t] == pos[q0] + step * t for t in range(Nq))
             assert all(pos[k0 + u] == pos[k0] + step * u for u in range(Nk))
-            chains.setdefault(q0, []).append(("p", kv["out"], kv["obf16"], Nq))
-            last_q0 = q0
-            for key in ("out", "lse"):
+            chains.setdefault(q0, []).append((kv["out"], kv["obf16"], kv["acc"], kv["lse"], kv["acclse"],
+                                              int(kv["ohs"]), int(kv["ahs"])))
+            for key in ("out", "lse", "acc", "acclse"):
                 name, off = _loc(kv[key])
                 if name == "ws":
                     assert 0 <= off < ws_bytes
-        elif ln.startswith("merge"):
-            # a merge folds the partial the launch just before it produced
-            assert chains[last_q0][-1][0] == "p"
-            chains[last_q0].append(("m", kv["out"], kv["obf16"], int(kv["N"])))
+        assert not ln.startswith("merge")              # no separate merge launches
     np.testing.assert_array_equal(got, want)
     for q0, ch in chains.items():
-        prefills = [c for c in ch if c[0] == "p"]
-        merges = [c for c in ch if c[0] == "m"]
-        assert len(merges) == max(0, len(prefills) - 1)
-        assert [c[0] for c in ch] == ["p"] + ["p", "m"] * (len(prefills) - 1)
-        final = ch[-1]
-        name, off = _loc(final[1])
-        assert name == "out" and off == q0 * D * elt and final[2] == "1"
-        for c in ch[:-1]:
-            assert _loc(c[1])[0] == "ws" and c[2] == "0"
+        out, obf16, acc, lse, acclse, ohs, ahs = zip(*ch)
+        # the first launch starts the running state; every later one folds into it
+        assert acc[0] == "none:-1" and acclse[0] == "none:-1"
+        assert all(_loc(x)[0] == "ws" for x in acc[1:]) and all(_loc(x)[0] == "ws" for x in acclse[1:])
+        # all but the last keep the fp32 state in the workspace, in place
+        for i in range(len(ch) - 1):
+            assert _loc(out[i])[0] == "ws" and obf16[i] == "0" and _loc(lse[i])[0] == "ws"
+            if i > 0:
+                assert out[i] == acc[i] and lse[i] == acclse[i] and ohs[i] == ahs[i]
+        # the last writes the merged result to the run's own output rows
+        name, off = _loc(out[-1])
+        assert name == "out" and off == q0 * D * elt and obf16[-1] == "1"
+        assert _loc(lse[-1]) == ("lse", q0 * 4)
 
 
 def test_zigzag_and_striped_balance_launch_work(stub):
