@@ -130,8 +130,10 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   const float cscale = a.sm_scale * kLog2e;
   const float inv_cscale = cscale != 0.f ? 1.0f / cscale : 0.f;
   auto scale4 = [&](float4 t) { return make_float4(t.x * cscale, t.y * cscale, t.z * cscale, t.w * cscale); };
+  // (loaded once the first K/V tile's loads are in flight, so the two
+  // round trips to HBM overlap)
   bf16x8 qreg[8];
-  {
+  auto load_q = [&]() {
     const int row = wrow0 + l32;
     const bool ok = row < a.Nq;
     const long long qpos = a.q_rope0 + (long long)row * a.rope_step;   // RoPE position
@@ -167,7 +169,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
         qreg[ks] = as_bf16x8(w);
       }
     }
-  }
+  };
 
   // ---- key range of the workgroup (causal: up to its last query position)
   int kend = a.Nk;
@@ -474,6 +476,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
 
   if (ntiles > 0) {
     issue_loads(tile_key0(0));
+    load_q();
     store_lds(0);
     __syncthreads();
     issue_loads(tile_key0(1));
