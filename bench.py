@@ -21,6 +21,8 @@ same line carries:
   * ``ring``: the 128K NTK prefill as Ring Attention over 8 devices run on
     this GPU (contiguous, zig-zag and striped shards): TFLOP/s of the whole
     ring and each device's share timed alone;
+  * ``merge``: attn_merge_states on two fp32 states the size of one 128K
+    ring device's query run, against the 8 TB/s HBM peak;
   * ``window``: the same prefill with a 4096-key sliding window and 4 sink
     tokens (flops of the kept pairs only), and its time against full causal;
   * ``backward``: dq, dk, dv of the same prefill, TFLOP/s of the five
@@ -307,6 +309,39 @@ def bench_decode(srt, torch, w, steps, warmup):
             "cache_build_ms": round(cache_ms, 3)}
 
 
+# ----------------------------------------------------------------------------- merge
+
+def bench_merge(srt, torch, w, steps, warmup):
+    """attn_merge_states on two fp32 partial states of one 128K ring device's
+    query run (B=1, 32 heads, C = N / chunks rows, D=128), in place into the
+    first, as a separate ring step would merge them.  HBM-bound: per row it
+    reads two D-vectors and two lse values and writes one D-vector and one
+    lse (algorithmic bytes)."""
+    import synth
+    C = w.N // w.chunks
+    shape = (w.B, w.Hq, C, w.D)
+    oa = synth.randn(shape, torch.float32, w.seed, synth.Q_ID, "cuda")
+    ob = synth.randn(shape, torch.float32, w.seed, synth.K_ID, "cuda")
+    la = synth.randn(shape[:3], torch.float32, w.seed, synth.V_ID, "cuda")
+    lb = synth.randn(shape[:3], torch.float32, w.seed, synth.DO_ID, "cuda")
+    fn = lambda: srt.attn_merge_states(oa, la, ob, lb, out=oa, lse_out=la)
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    kt = Timer(torch)
+    for _ in range(steps):
+        kt.run(fn)
+    torch.cuda.synchronize()
+    ms_ = kt.mean_ms()
+    rows = w.B * w.Hq * C
+    alg = rows * (3 * w.D * 4 + 3 * 4)
+    gbs = alg / (ms_ * 1e-3) / 1e9
+    return {"workload": f"attn_merge_states, two fp32 states of {w.Hq} heads x {C} rows x {w.D}", "unit": "GB/s",
+            "value": round(gbs, 1), "kernel_ms": round(ms_, 4), "alg_bytes": alg,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+
+
 # ----------------------------------------------------------------------------- ring step on one GPU
 
 def bench_ring(srt, torch, w, steps, warmup):
@@ -552,7 +587,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=24.0,
                     help="seconds of oracle time over all legs (split among them)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
-    ap.add_argument("--only", choices=["decode", "ring", "window", "backward", "gqa_8k"], default=None,
+    ap.add_argument("--only", choices=["decode", "ring", "window", "backward", "gqa_8k", "merge"], default=None,
                     help="run one extra leg alone and print its JSON (for profiling that leg's kernels)")
     args = ap.parse_args()
 
@@ -594,6 +629,8 @@ def main():
             r = bench_ring(srt, torch, synth.WORKLOADS["ntk_128k_ring_bf16"], args.steps, args.warmup)
         elif args.only == "window":
             r = bench_window(srt, torch, w, 4096, 4, args.steps, args.warmup, float("nan"))
+        elif args.only == "merge":
+            r = bench_merge(srt, torch, synth.WORKLOADS["ntk_128k_ring_bf16"], args.steps, args.warmup)
         elif args.only == "gqa_8k":
             w8 = synth.WORKLOADS["gqa_8k_bf16"]
             r = prefill_leg(bench_prefill(srt, torch, w8, args.steps, args.warmup, True), w8)
@@ -631,6 +668,8 @@ def main():
         line["ring"] = bench_ring(srt, torch, synth.WORKLOADS["ntk_128k_ring_bf16"], max(2, args.steps // 5), 1)
         if "ring" in cpu:
             line["ring"]["cpu_baseline"] = cpu["ring"]
+        torch.cuda.empty_cache()
+        line["merge"] = bench_merge(srt, torch, synth.WORKLOADS["ntk_128k_ring_bf16"], args.steps, args.warmup)
         torch.cuda.empty_cache()
         line["window"] = bench_window(srt, torch, w, 4096, 4, args.steps, args.warmup, p["kernel_ms"])
         torch.cuda.empty_cache()
