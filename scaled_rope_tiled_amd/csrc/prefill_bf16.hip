@@ -75,6 +75,7 @@ constexpr int kBM = 32;           // query rows per wave
 constexpr int kBN = 64;           // keys per tile
 constexpr int kKStr = kD + 8;     // K tile row stride (bf16 elements) = 272 B
 constexpr int kVStr = kD + 32;    // V tile row stride (bf16 elements) = 320 B
+constexpr int kOStr = kD + 8;     // epilogue staging row stride (bf16 elements) = 272 B
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSumBound = 4096.0f;   // a lane's exponential sum over a half that moves the reference
@@ -85,6 +86,7 @@ struct Smem {
   __hip_bfloat16 k[3][kBN * kKStr];
   __hip_bfloat16 v[3][kBN * kVStr];
 };
+static_assert(kWaves * kBM * kOStr * 2 <= sizeof(Smem), "the epilogue staging fits in the tile buffers");
 
 // ROT_K: rotate K on its way into LDS; HALF: half-split pairs; WIN: sliding
 // window and sinks (without it, the window tests fold away); SCALE_S: q is
@@ -537,7 +539,37 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   // ---- epilogue: combine the two lane halves' sums, normalise, write O and lse
   const float lt = pair_sum(l_run);
   const int row = wrow0 + l32;
-  if (row < a.Nq) {
+  if (a.out_bf16 && !a.acc_o) {
+    // A lane holds four d values of one row per 32-wide d block, so storing
+    // straight from registers writes 32 scattered 16-byte pieces per
+    // instruction.  Instead the wave's 32 x 128 block goes through its own
+    // 8.5 KB of the (now idle) tile buffers and every 16 lanes then write one
+    // whole 256-byte row: each store instruction covers four full rows.
+    __syncthreads();                                 // every wave is done reading the last tiles
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    const uint32_t stg = lds_off(&sm) + wave * (kBM * kOStr * 2);
+    typedef __attribute__((address_space(3))) uint32_t lds_u32;
+    typedef __attribute__((address_space(3))) u32x4_t lds_u4w;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const uint32_t at = stg + (l32 * kOStr + db * 32 + g4 * 8 + hl * 4) * 2;
+        *(lds_u32*)(uintptr_t)at = pack2(oacc[db][g4 * 4 + 0] * inv, oacc[db][g4 * 4 + 1] * inv);
+        *(lds_u32*)(uintptr_t)(at + 4) = pack2(oacc[db][g4 * 4 + 2] * inv, oacc[db][g4 * 4 + 3] * inv);
+      }
+    asm volatile("" ::: "memory");                    // the reads below follow the writes (one wave: in order)
+    __hip_bfloat16* og = reinterpret_cast<__hip_bfloat16*>(a.out) + ((long long)b * a.Hq + hq) * a.o_hstride +
+                         (long long)wrow0 * kD;
+#pragma unroll
+    for (int i = 0; i < kBM / 4; ++i) {
+      const int r = i * 4 + (lane >> 4);
+      const u32x4_t w = *(const lds_u4*)(uintptr_t)(stg + (r * kOStr + (lane & 15) * 8) * 2);
+      if (wrow0 + r < a.Nq) *reinterpret_cast<uint4*>(og + (long long)r * kD + (lane & 15) * 8) = make_uint4(w.x, w.y, w.z, w.w);
+    }
+    if (a.lse && hl == 0 && row < a.Nq)
+      a.lse[((long long)b * a.Hq + hq) * a.lse_hstride + row] = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -INFINITY;
+  } else if (row < a.Nq) {
     float inv = lt > 0.f ? 1.0f / lt : 0.f;
     float lse_row = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -INFINITY;
     const long long obase = ((long long)b * a.Hq + hq) * a.o_hstride + (long long)row * kD;
