@@ -68,6 +68,9 @@ typedef enum { SRT_F32 = 0, SRT_BF16 = 1 } srt_dtype;
 #define SRT_ROTATE_K 2      /* rotate k rows on load with table rows k_pos0 + c */
 #define SRT_PAIR_HALF 4     /* half-split pairs (x[i], x[i + D/2]) instead of interleaved */
 
+/* Bytes of the scheduling block of srt_attn_prefill (see there). */
+#define SRT_PREFILL_SCHED_BYTES 128
+
 /* pairing argument of srt_rope_apply and srt_attn_decode_splitk */
 #define SRT_PAIRING_INTERLEAVED 0
 #define SRT_PAIRING_HALF 1
@@ -190,6 +193,19 @@ int srt_rope_apply(const void* x, void* y, int dtype, int B, int H, int N, int D
  * table_dev may be NULL only when rope_flags == 0.  Without SRT_ROTATE_Q the
  * bf16 kernel uses q exactly as given and scales the scores in fp32; with it,
  * the rotated q carries one bf16 rounding (the MFMA operand).
+ *
+ * sched: NULL, or a device block of SRT_PREFILL_SCHED_BYTES bytes, 8-byte
+ * aligned (else SRT_ERR_INVALID), owned by the caller and zero-filled before
+ * its first use.  With it the bf16 kernel hands its (head, query tile) work
+ * items to workgroups at run time: each XCD first takes the heavy query tiles
+ * of its own KV heads (its L2 keeps their K/V), then the light last quarter
+ * of the tiles from a pool shared by all XCDs, so XCDs that run faster take
+ * more of it.  The results are bit-identical either way; only the finishing
+ * times of the XCDs change.  The launch's last workgroup zero-fills the block
+ * again, so one block serves any number of calls issued one after another
+ * (one stream); calls that may run at the same time each need their own
+ * block.  Launches of at most two workgroups per compute unit, and the fp32
+ * kernel, ignore it.  NULL keeps a fixed assignment.
  */
 int srt_attn_prefill(const void* q, const void* k, const void* v, int dtype,
                      int B, int Hq, int Hkv, int Nq, int Nk, int D,
@@ -197,7 +213,7 @@ int srt_attn_prefill(const void* q, const void* k, const void* v, int dtype,
                      long long q_pos0, long long k_pos0, int causal, int window, int sink, float sm_scale,
                      const float* table_dev, long long table_npos, int rope_flags,
                      void* out, int out_dtype, long long o_hstride,
-                     float* lse, long long lse_hstride, void* stream);
+                     float* lse, long long lse_hstride, void* sched, void* stream);
 
 /*
  * srt_attn_merge_states - combine two partial attention states over disjoint keys.
@@ -324,9 +340,10 @@ int srt_attn_backward(const void* q, const void* k, const void* v, const void* o
 
 /*
  * srt_attn_ring_workspace_size - bytes of workspace srt_attn_ring_prefill needs:
- * two fp32 partial states of one query run ([B][Hq][R][D] + [B][Hq][R], R =
- * N/P, or N/(2P) for zigzag) and, when rope_flags has SRT_ROTATE_K, a rotated
- * copy of K ([B][Hkv][N][D] in dtype).
+ * the fp32 running state of one query run (O [B][Hq][R][D] and lse
+ * [B][Hq][R], R = N/P, or N/(2P) for zigzag), the scheduling block of its
+ * prefill launches (zero-filled by each call) and, when rope_flags has
+ * SRT_ROTATE_K, a rotated copy of K ([B][Hkv][N][D] in dtype).
  */
 int srt_attn_ring_workspace_size(int B, int Hq, int Hkv, int N, int D, int dtype, int num_devices, int partition,
                                  int rope_flags, size_t* bytes_out_host);

@@ -39,7 +39,7 @@ __all__ = ["rope_inv_freq", "rope_inv_freq_dynamic_ntk", "rope_inv_freq_factors"
            "attn_decode_splitk", "attn_decode_workspace_size", "attn_decode_splitk_noalloc",
            "attn_decode_noalloc_max_workspace", "attn_ring_prefill", "attn_ring_workspace_size",
            "attn_backward", "attn_backward_workspace_size", "NONE", "PI", "NTK", "YARN",
-           "ROTATE_Q", "ROTATE_K", "PAIR_HALF", "PAIRING_INTERLEAVED", "PAIRING_HALF", "lib"]
+           "ROTATE_Q", "ROTATE_K", "PAIR_HALF", "PAIRING_INTERLEAVED", "PAIRING_HALF", "PREFILL_SCHED_BYTES", "lib"]
 
 
 def lib():
@@ -185,13 +185,18 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, sm_scale:
                  causal: bool = True, q_pos0: int = 0, k_pos0: int = 0, table: torch.Tensor | None = None,
                  rope_flags: int | None = None, out: torch.Tensor | None = None,
                  out_dtype: torch.dtype | None = None, lse: torch.Tensor | bool = True,
-                 window: int = 0, sink: int = 0):
+                 window: int = 0, sink: int = 0, sched=True):
     """Tiled causal attention with rotate-on-load RoPE.
 
     q [B, Hq, Nq, D], k/v [B, Hkv, Nk, D] (views sliced along N allowed).
     rope_flags defaults to ROTATE_Q|ROTATE_K when a table is given; add
     PAIR_HALF for half-split pairs.  window > 0 (causal only) keeps key j for
     query i iff i - j < window or j < sink (absolute positions).
+    sched: the scheduling block of srt_attn_prefill: True (default) uses one
+    zero-filled block per (device, stream), kept for reuse (the kernel leaves
+    it zero-filled; calls on one stream never overlap); a tensor of at least
+    PREFILL_SCHED_BYTES zero-filled bytes on q's device is used as given;
+    False or None asks for the fixed assignment.
     Returns (out [B, Hq, Nq, D], lse [B, Hq, Nq] fp32 or None)."""
     B, Hq, Nq, D = q.shape
     _, Hkv, Nk, _ = k.shape
@@ -219,12 +224,34 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, sm_scale:
     _on_device(q.device, q=q, k=k, v=v, out=out, lse=lse)
     tp, npos = _table(table, D, q.device)
     sm = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
+    sp = _sched_block(sched, q.device)
     _lib.check(lib().srt_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _dt(q), B, Hq, Hkv, Nq, Nk, D,
                                       qs, ks, int(q_pos0), int(k_pos0), int(bool(causal)), int(window), int(sink), sm,
                                       tp, npos, int(rope_flags),
-                                      _ptr(out), _dt(out), os_, _ptr(lse), ls, _stream(q.device)),
+                                      _ptr(out), _dt(out), os_, _ptr(lse), ls, sp, _stream(q.device)),
                "attn_prefill")
     return out, lse
+
+
+PREFILL_SCHED_BYTES = 128     # SRT_PREFILL_SCHED_BYTES
+_sched_blocks = {}
+
+
+def _sched_block(sched, dev: torch.device):
+    """Pointer to the scheduling block for this call (see attn_prefill), or None."""
+    if sched is None or sched is False:
+        return None
+    if sched is True:
+        key = (dev.index, _stream(dev))
+        blk = _sched_blocks.get(key)
+        if blk is None:
+            blk = _sched_blocks[key] = torch.zeros(PREFILL_SCHED_BYTES, dtype=torch.uint8, device=dev)
+        return _ptr(blk)
+    _on_device(dev, sched=sched)
+    if not sched.is_contiguous() or sched.numel() * sched.element_size() < PREFILL_SCHED_BYTES \
+            or sched.data_ptr() % 8:
+        raise ValueError(f"sched must be a contiguous, 8-byte aligned block of >= {PREFILL_SCHED_BYTES} bytes")
+    return _ptr(sched)
 
 
 def attn_merge_states(o_a, lse_a, o_b, lse_b, *, out=None, lse_out=None, out_dtype=None):

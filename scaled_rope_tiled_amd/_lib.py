@@ -32,7 +32,7 @@ SIGNATURES = {
                          c_int, c_int, c_int, c_int, c_int, c_int,
                          c_ll, c_ll, c_ll, c_ll, c_int, c_int, c_int, c_float,
                          c_void_p, c_ll, c_int,
-                         c_void_p, c_int, c_ll, c_void_p, c_ll, c_void_p],
+                         c_void_p, c_int, c_ll, c_void_p, c_ll, c_void_p, c_void_p],
     "srt_attn_merge_states": [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_ll,
                               c_void_p, c_int, c_ll, c_void_p, c_ll,
                               c_int, c_int, c_int, c_int, c_void_p],
@@ -63,6 +63,7 @@ SIGNATURES = {
 }
 
 _lib = None
+ABI_VERSION = 2          # srt_abi_version() of the library these signatures describe
 
 
 def load(path: str = LIB_PATH):
@@ -73,6 +74,9 @@ def load(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(f"libsrt.so not built at {path}: run `python scaled_rope_tiled_amd/build.py`")
     lib = C.CDLL(path)
+    lib.srt_abi_version.restype = c_int
+    if lib.srt_abi_version() != ABI_VERSION:
+        raise ImportError(f"{path} implements ABI {lib.srt_abi_version()}, this binding ABI {ABI_VERSION}: rebuild it")
     for name, args in SIGNATURES.items():
         fn = getattr(lib, name)
         fn.argtypes = args

@@ -41,7 +41,7 @@ constexpr double kTwoPi = 6.283185307179586476925286766559;
 
 extern "C" {
 
-int srt_abi_version(void) { return 1; }
+int srt_abi_version(void) { return 2; }
 
 const char* srt_status_string(int status) {
   switch (status) {
@@ -169,7 +169,7 @@ int srt_attn_prefill(const void* q, const void* k, const void* v, int dtype, int
                      int Nk, int D, long long q_hstride, long long kv_hstride, long long q_pos0,
                      long long k_pos0, int causal, int window, int sink, float sm_scale, const float* table_dev,
                      long long table_npos, int rope_flags, void* out, int out_dtype, long long o_hstride,
-                     float* lse, long long lse_hstride, void* stream) {
+                     float* lse, long long lse_hstride, void* sched, void* stream) {
   if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return fail(SRT_ERR_INVALID, "attn_prefill: bad dtype");
   if (B < 0 || Hq < 1 || Hkv < 1 || Nq < 0 || Nk < 0) return fail(SRT_ERR_INVALID, "attn_prefill: bad sizes");
   if ((long long)B * Nq == 0) return ok();     // no query row: nothing to write, pointers may be NULL
@@ -213,6 +213,9 @@ int srt_attn_prefill(const void* q, const void* k, const void* v, int dtype, int
   a.causal = causal ? 1 : 0; a.rope_flags = rope_flags; a.out_bf16 = out_dtype == SRT_BF16;
   a.window = window; a.sink = window > 0 ? sink : 0;
   a.sm_scale = sm_scale;
+  if (sched && (reinterpret_cast<uintptr_t>(sched) & 7))
+    return fail(SRT_ERR_INVALID, "attn_prefill: sched must be 8-byte aligned");
+  a.sched = static_cast<unsigned long long*>(sched);
   if (dtype == SRT_BF16) {
     if (D != 128) return fail(SRT_ERR_UNSUPPORTED, "attn_prefill: bf16 kernel needs D = 128 (got %d)", D);
     const int g = Hq / Hkv;

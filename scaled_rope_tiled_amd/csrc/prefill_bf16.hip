@@ -12,10 +12,13 @@
 //     LDS serves all eight waves, i.e. up to four query heads.
 //   * Wave w owns 32 query rows of one head and keeps them in registers:
 //     rotated q as the B operand of S^T = K Q^T, the output as O^T (fp32).
-//   * The grid's x index is the KV head (fastest), so consecutive workgroups,
-//     which the dispatcher spreads round-robin over the 8 XCDs, keep one head
-//     per XCD L2; the y index walks query tiles from the last (most keys under
-//     the causal mask) to the first, so the long tiles start first.
+//   * Items (workgroup head, batch, query tile) are numbered with the head
+//     fastest and the query tiles from the last (most keys under the causal
+//     mask) to the first, so the long tiles start first; consecutive
+//     workgroups, which the dispatcher spreads round-robin over the 8 XCDs,
+//     keep one head per XCD L2.  With a scheduling block the items are handed
+//     out at run time instead (see sched_take), which evens out XCDs that run
+//     at different speeds.
 //   * Key tiles wholly above the causal diagonal, or wholly before the sliding
 //     window of the workgroup's rows (sinks aside: "Long Context..." §10.1-10.2),
 //     are never visited; only the 32-key halves that cross the diagonal, the
@@ -88,6 +91,62 @@ struct Smem {
 };
 static_assert(kWaves * kBM * kOStr * 2 <= sizeof(Smem), "the epilogue staging fits in the tile buffers");
 
+// ---- run-time assignment of (head, query tile) items to workgroups
+//
+// Items are numbered heavy first: item = (y * B + b) * HX + x, with x the
+// workgroup head (KV head and quad, HX of them), b the batch and y the
+// query-tile rank (y = 0 is the tile with the most keys under the causal
+// mask).  The hardware hands workgroups to the eight XCDs in turn, so every
+// XCD runs the same number of them, and with a fixed assignment (item =
+// workgroup index) XCD k runs heads x = k mod 8: its L2 keeps their K/V, but
+// XCDs that run slower (measured: up to 3 % on one chip) finish last.  With a
+// scheduling block each workgroup instead takes the next item from
+//   1. its own XCD's queue: the heads x = k mod 8, row tiles y < ysplit;
+//   2. once that is empty, one shared pool: every head, the light tail
+//      y >= ysplit (the last quarter of the row tiles), heavy first;
+//   3. then any other XCD's queue (there are as many items as workgroups, so
+//      a workgroup always finds one, whatever the hardware's distribution).
+// A faster XCD reaches the pool sooner and takes its heavier items, which
+// evens out the finishing times while the heavy items keep their locality.
+// Each queue is a counter in the block: atomicAdd hands out index old and the
+// item exists while old < the queue's length.
+__device__ inline int sched_take(unsigned long long* blk, int HX, int B, int ntq) {
+  const int ysplit = ntq - (ntq >= 4 ? ntq / 4 : 0);
+  const int own = (int)(__builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11)) & 7);   // this XCD
+  for (int t = 0; t < 9; ++t) {
+    if (t == 1) {
+      const long long n = (long long)(ntq - ysplit) * B * HX;
+      if (n == 0) continue;
+      const long long idx = (long long)atomicAdd(&blk[8], 1ull);
+      if (idx < n) {
+        const int per_y = B * HX;
+        const int yy = ysplit + (int)(idx / per_y), r = (int)(idx % per_y);
+        return (yy * B + r / HX) * HX + r % HX;
+      }
+      continue;
+    }
+    const int k = t == 0 ? own : (own + t - 1) & 7;   // t = 2..8: the other seven queues
+    const int nh = k < HX ? (HX - 1 - k) / 8 + 1 : 0;   // heads k, k + 8, ... below HX
+    const long long n = (long long)nh * B * ysplit;
+    if (n == 0) continue;
+    const long long idx = (long long)atomicAdd(&blk[k], 1ull);
+    if (idx < n) {
+      const int per_y = nh * B;
+      const int yy = (int)(idx / per_y), r = (int)(idx % per_y);
+      const int bb = r / nh;
+      return (yy * B + bb) * HX + k + 8 * (r - bb * nh);
+    }
+  }
+  return 0;   // not reached from a zero-filled block
+}
+
+// The launch's last workgroup zero-fills the block again for the next call.
+__device__ inline void sched_release(unsigned long long* blk, unsigned nwg) {
+  if (atomicAdd(&blk[9], 1ull) == (unsigned long long)nwg - 1) {
+    for (int k = 0; k < kSchedWords; ++k) atomicExch(&blk[k], 0ull);
+  }
+}
+
 // ROT_K: rotate K on its way into LDS; HALF: half-split pairs; WIN: sliding
 // window and sinks (without it, the window tests fold away); SCALE_S: q is
 // not rotated, so it is kept exact (no rounding of q * sm_scale log2(e)) and
@@ -95,6 +154,7 @@ static_assert(kWaves * kBM * kOStr * 2 <= sizeof(Smem), "the epilogue staging fi
 template <bool ROT_K, bool HALF, bool WIN, bool SCALE_S>
 __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a) {
   __shared__ Smem sm;
+  __shared__ int s_item;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -103,11 +163,21 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   const int HPW = G < 4 ? G : 4;                 // query heads per workgroup
   const int RB = kWaves / HPW;                   // 32-row blocks per workgroup
   const int quads = G > 4 ? G / 4 : 1;
-  const int hk = blockIdx.x / quads;
-  const int quad = blockIdx.x - hk * quads;
-  const int b = blockIdx.z;
-  const int ntiles_q = gridDim.y;
-  const int qt = a.causal ? (ntiles_q - 1 - (int)blockIdx.y) : (int)blockIdx.y;
+  const int HX = a.Hkv * quads;                  // workgroup heads
+  const int ntiles_q = (a.Nq + kBM * RB - 1) / (kBM * RB);
+  int item = (int)blockIdx.x;
+  if (a.sched) {
+    if (tid == 0) s_item = sched_take(a.sched, HX, a.B, ntiles_q);
+    __syncthreads();
+    item = __builtin_amdgcn_readfirstlane(s_item);
+  }
+  const int xh = item % HX;
+  const int yb = item / HX;
+  const int yq = yb / a.B;                       // query-tile rank, 0 = most keys
+  const int b = yb - yq * a.B;
+  const int hk = xh / quads;
+  const int quad = xh - hk * quads;
+  const int qt = a.causal ? (ntiles_q - 1 - yq) : yq;
   const int hq = hk * G + quad * 4 + (wave % HPW);
   const int wrow0 = qt * (kBM * RB) + (wave / HPW) * kBM;     // first query row of this wave
   const int wg_row_last = min(a.Nq, (qt + 1) * kBM * RB) - 1;  // last valid row of the workgroup
@@ -134,44 +204,90 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   auto scale4 = [&](float4 t) { return make_float4(t.x * cscale, t.y * cscale, t.z * cscale, t.w * cscale); };
   // (loaded once the first K/V tile's loads are in flight, so the two
   // round trips to HBM overlap)
+  //
+  // The wave's 32 q rows and their table rows are read coalesced: load i of
+  // lane j takes 16-byte chunk j % 16 of row 4i + j / 16, so each load
+  // instruction covers four whole rows (the operand layout would spread one
+  // instruction over 32 rows, and those scattered reads of q and the table
+  // took about 4 us of a workgroup's start).  A chunk holds 8 dims = 4
+  // interleaved pairs, whose 4 table entries are 32 contiguous bytes; with
+  // half-split pairs chunk c < 8 pairs with chunk c + 8 of the same row, one
+  // lane over (a lane exchange), and both take the 8 entries of pairs 8(c % 8)...
+  // The rotated chunks then go through LDS (tile buffers 1 and 2, untouched
+  // until the first barrier) into the MFMA operand layout.  Rows past the
+  // last one read the last row (in bounds) and are zeroed.
   bf16x8 qreg[8];
   auto load_q = [&]() {
-    const int row = wrow0 + l32;
-    const bool ok = row < a.Nq;
-    const long long qpos = a.q_rope0 + (long long)row * a.rope_step;   // RoPE position
-    if constexpr (HALF) {
-      uint4 w[8];
+    const int cr = lane >> 4, cc = lane & 15;
+    uint4 w[8];
+    bool ok[8];
+    long long qp[8];
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        w[ks] = ok ? *reinterpret_cast<const uint4*>(qg + (long long)row * kD + ks * 16 + hl * 8)
-                   : make_uint4(0, 0, 0, 0);
-      if (!SCALE_S && ok) {
+    for (int i = 0; i < 8; ++i) {
+      const int row = wrow0 + 4 * i + cr;
+      ok[i] = row < a.Nq;
+      const int rowc = ok[i] ? row : a.Nq - 1;
+      qp[i] = a.q_rope0 + (long long)rowc * a.rope_step;   // RoPE position
+      w[i] = *reinterpret_cast<const uint4*>(qg + (long long)rowc * kD + cc * 8);
+    }
+    if constexpr (!SCALE_S) {
+      if constexpr (HALF) {
+        // (rows in two groups of four: eight rows of 64-byte table entries
+        // at once would hold 128 registers)
+        const bool first = cc < 8;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int d0 = ks * 16 + hl * 8;                  // first-half dims d0..d0+7 = pairs d0..d0+7
-          const float4* t = tab4 + (qpos * (kD / 2) + d0) / 2;
-          const float4 tt[4] = {scale4(t[0]), scale4(t[1]), scale4(t[2]), scale4(t[3])};
-          rotate_chunk_pair(w[ks], w[ks + 4], tt);
+        for (int g = 0; g < 2; ++g) {
+        float4 t[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4* tp = tab4 + (qp[g * 4 + i] * (kD / 2) + (cc & 7) * 8) / 2;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) t[i * 4 + e] = tp[e];
         }
-      }
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) qreg[ks] = as_bf16x8(w[ks]);
-    } else {
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int i = g * 4 + i4;
+          // partner chunk (the other half of the same pairs) from lane j ^ 8
+          const uint4 o = make_uint4(__shfl_xor(w[i].x, 8), __shfl_xor(w[i].y, 8), __shfl_xor(w[i].z, 8),
+                                     __shfl_xor(w[i].w, 8));
+          const uint32_t m4[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+          const uint32_t p4[4] = {o.x, o.y, o.z, o.w};
+          uint32_t r4[4];
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const int d0 = ks * 16 + hl * 8;
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (ok) {
-          w = *reinterpret_cast<const uint4*>(qg + (long long)row * kD + d0);
-          if (!SCALE_S) {
-            const float4* t = tab4 + (qpos * (kD / 2) + d0 / 2) / 2;
-            w = rotate_chunk(w, scale4(t[0]), scale4(t[1]));
+          for (int q = 0; q < 4; ++q) {
+            const float4 tt = scale4(t[i4 * 4 + q]);   // pairs 2q, 2q + 1 of the chunk: (c, s, c, s)
+            const float m0 = bf_lo(m4[q]), m1 = bf_hi(m4[q]), p0 = bf_lo(p4[q]), p1 = bf_hi(p4[q]);
+            // first half: x c - y s; second half: x s + y c (x from the first half, y from the second)
+            r4[q] = first ? pack2(m0 * tt.x - p0 * tt.y, m1 * tt.z - p1 * tt.w)
+                          : pack2(p0 * tt.y + m0 * tt.x, p1 * tt.w + m1 * tt.z);
           }
+          w[i] = make_uint4(r4[0], r4[1], r4[2], r4[3]);
         }
-        qreg[ks] = as_bf16x8(w);
+        }
+      } else {
+        float4 t[16];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float4* tp = tab4 + (qp[i] * (kD / 2) + cc * 4) / 2;
+          t[i * 2] = tp[0];
+          t[i * 2 + 1] = tp[1];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[i] = rotate_chunk(w[i], scale4(t[i * 2]), scale4(t[i * 2 + 1]));
       }
     }
+    typedef __attribute__((address_space(3))) u32x4_t lds_u4q;
+    const uint32_t stg = (wave < 4 ? lds_off(&sm.k[1][0]) : lds_off(&sm.v[1][0])) + (wave & 3) * (kBM * kKStr * 2);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint4 x = ok[i] ? w[i] : make_uint4(0, 0, 0, 0);
+      *(lds_u4q*)(uintptr_t)(stg + ((4 * i + cr) * kKStr + cc * 8) * 2) = (u32x4_t){x.x, x.y, x.z, x.w};
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qreg[ks] = lds_read16(stg + (l32 * kKStr + ks * 16 + hl * 8) * 2);
   };
+  static_assert(4 * kBM * kKStr * 2 <= 2 * kBN * kKStr * 2 && 4 * kBM * kKStr * 2 <= 2 * kBN * kVStr * 2,
+                "the q staging of four waves fits in tile buffers 1 and 2 of K, and of V");
 
   // ---- key range of the workgroup (causal: up to its last query position)
   int kend = a.Nk;
@@ -613,9 +729,33 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
     }
     if (a.lse && hl == 0) a.lse[((long long)b * a.Hq + hq) * a.lse_hstride + row] = lse_row;
   }
+  if (a.sched && tid == 0) sched_release(a.sched, gridDim.x);
 }
 
 }  // namespace
+
+// Compute units of the current device (cached per device).
+static int compute_units() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cache[dev]) {
+    int n = 0;
+    cache[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return cache[dev];
+}
+
+__global__ void __launch_bounds__(64) zero_words_kernel(unsigned long long* p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0ull;
+}
+
+hipError_t launch_zero_words(unsigned long long* p, int n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  if (n > 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(64), 0, stream, p, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill_bf16_d128(const PrefillArgs& a, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
@@ -623,10 +763,16 @@ hipError_t launch_prefill_bf16_d128(const PrefillArgs& a, hipStream_t stream) {
   const int HPW = G < 4 ? G : 4;
   const int rows_per_wg = kBM * (kWaves / HPW);
   const int quads = G > 4 ? G / 4 : 1;
-  const dim3 grid(a.Hkv * quads, (a.Nq + rows_per_wg - 1) / rows_per_wg, a.B), block(kThreads);
+  const long long items = (long long)a.Hkv * quads * ((a.Nq + rows_per_wg - 1) / rows_per_wg) * a.B;
+  if (items > 0x7fffffffLL) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)items), block(kThreads);
+  // the run-time assignment pays one atomic round trip per workgroup and
+  // helps only when the XCDs run several workgroups each
+  PrefillArgs la = a;
+  if (la.sched && items <= 2LL * compute_units()) la.sched = nullptr;
   const bool rot_k = (a.rope_flags & 2) != 0, half = (a.rope_flags & 4) != 0;
   const bool win = a.window > 0, scale_s = (a.rope_flags & 1) == 0;
-  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, block, 0, stream, a); };
+  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, block, 0, stream, la); };
   // half-split pairing changes only what is rotated: without a rotation it is
   // the same kernel
   auto pick = [&](auto wc, auto sc) {

@@ -73,6 +73,7 @@ size_t ring_workspace_bytes(const RingArgs& a) {
   size_t n = 0;
   if (a.rope_flags & 2) n += up((size_t)a.B * a.Hkv * a.N * a.D * elt);
   n += up((size_t)a.B * a.Hq * R * a.D * 4) + up((size_t)a.B * a.Hq * R * 4);
+  n += up(kSchedWords * 8);            // the prefill launches' scheduling block
   return n;
 }
 
@@ -96,6 +97,11 @@ hipError_t ring_prefill(const RingArgs& a, hipStream_t stream) {
   float* acc_o = reinterpret_cast<float*>(ws);
   ws += up((size_t)a.B * a.Hq * R * a.D * 4);
   float* acc_l = reinterpret_cast<float*>(ws);
+  ws += up((size_t)a.B * a.Hq * R * 4);
+  // one scheduling block serves every launch of the call (they run one after
+  // another on the stream, and each leaves it zero-filled)
+  unsigned long long* sched = reinterpret_cast<unsigned long long*>(ws);
+  if (hipError_t e = launch_zero_words(sched, kSchedWords, stream); e != hipSuccess) return e;
 
   const char* qb = static_cast<const char*>(a.q);
   const char* kb = static_cast<const char*>(kk);
@@ -113,6 +119,7 @@ hipError_t ring_prefill(const RingArgs& a, hipStream_t stream) {
     p.out = out;
     p.lse = lse;
     p.table = a.table;
+    p.sched = sched;
     p.q_hstride = hs; p.kv_hstride = hs; p.o_hstride = o_hstride; p.lse_hstride = lse_hstride;
     if (a.mode == kStriped) {
       // key u at j + P u is visible to query t at r + P t iff u <= t (j <= r) or u <= t - 1 (j > r)

@@ -67,7 +67,15 @@ struct PrefillArgs {
   const float* acc_o;
   const float* acc_lse;
   long long acc_hstride, acc_lse_hstride;
+  // Run-time assignment of the bf16 kernel's (head, query tile) items to
+  // workgroups: kSchedWords zero-filled 64-bit counters, left zeroed by the
+  // launch's last workgroup; nullptr keeps the fixed assignment by grid index.
+  unsigned long long* sched;
 };
+constexpr int kSchedWords = 10;   // 8 per-XCD queues, the shared pool, the count of finished workgroups
+
+// Zero-fill n 64-bit words on the stream (a kernel, so that it may be captured).
+hipError_t launch_zero_words(unsigned long long* p, int n, hipStream_t stream);
 
 hipError_t launch_prefill_bf16_d128(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);

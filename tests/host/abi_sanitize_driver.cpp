@@ -45,7 +45,13 @@ hipError_t launch_rope_apply(const void* x, void* y, bool, bool, long long group
   ++g_launches;
   return hipSuccess;
 }
+hipError_t launch_zero_words(unsigned long long* p, int n, hipStream_t) {
+  EXPECT(p && n >= 1 && n <= 64 && (reinterpret_cast<uintptr_t>(p) & 7) == 0);
+  ++g_launches;
+  return hipSuccess;
+}
 static hipError_t check_prefill(const PrefillArgs& a) {
+  EXPECT(!a.sched || (reinterpret_cast<uintptr_t>(a.sched) & 7) == 0);
   EXPECT(a.B >= 1 && a.Nq >= 1 && a.Nk >= 0 && a.Hq % a.Hkv == 0);
   EXPECT(a.q && a.out && aligned16(a.q) && aligned16(a.out));
   EXPECT(a.q_hstride >= (long long)a.Nq * a.D && a.o_hstride >= (long long)a.Nq * a.D);
@@ -130,21 +136,25 @@ int main() {
       const int st = srt_attn_prefill(fake(1), fake(2), fake(3), dtype, 2, 8, 2, 300, 500, D, 300LL * D, 500LL * D,
                                       200, 0, 1, flags == 5 ? 64 : 0, 4, 0.1f, tab ? (float*)fake(0) : nullptr,
                                       tab ? 1000 : 0, flags, fake(4), SRT_F32, 300LL * D, (float*)fake(5), 300,
-                                      nullptr);
+                                      flags == 3 ? fake(6) : nullptr, nullptr);
       EXPECT(st == SRT_OK);
     }
   }
   EXPECT(srt_attn_prefill(fake(1), fake(2), fake(3), SRT_BF16, 1, 8, 2, 64, 64, 128, 64 * 128 + 4, 64 * 128, 0, 0, 1,
-                          0, 0, 0.1f, nullptr, 0, 0, fake(4), SRT_BF16, 64 * 128, nullptr, 0, nullptr) ==
+                          0, 0, 0.1f, nullptr, 0, 0, fake(4), SRT_BF16, 64 * 128, nullptr, 0, nullptr, nullptr) ==
          SRT_ERR_INVALID);
   EXPECT(srt_attn_prefill(fake(1), fake(2), fake(3), SRT_BF16, 1, 8, 2, 64, 64, 128, 64 * 128, 64 * 128, 0, 0, 1, 0,
                           0, 0.1f, (float*)fake(0), 32, SRT_ROTATE_Q, fake(4), SRT_BF16, 64 * 128, nullptr, 0,
-                          nullptr) == SRT_ERR_INVALID);
+                          nullptr, nullptr) == SRT_ERR_INVALID);
+  // a scheduling block off an 8-byte boundary
+  EXPECT(srt_attn_prefill(fake(1), fake(2), fake(3), SRT_BF16, 1, 8, 2, 64, 64, 128, 64 * 128, 64 * 128, 0, 0, 1, 0,
+                          0, 0.1f, nullptr, 0, 0, fake(4), SRT_BF16, 64 * 128, nullptr, 0,
+                          static_cast<char*>(fake(6)) + 4, nullptr) == SRT_ERR_INVALID);
   EXPECT(srt_attn_prefill(fake(1), fake(2), fake(3), SRT_BF16, 1, 6, 4, 64, 64, 128, 64 * 128, 64 * 128, 0, 0, 1, 0,
-                          0, 0.1f, nullptr, 0, 0, fake(4), SRT_BF16, 64 * 128, nullptr, 0, nullptr) ==
+                          0, 0.1f, nullptr, 0, 0, fake(4), SRT_BF16, 64 * 128, nullptr, 0, nullptr, nullptr) ==
          SRT_ERR_INVALID);
   EXPECT(srt_attn_prefill(fake(1), fake(2), fake(3), SRT_BF16, 1, 24, 8, 64, 64, 128, 64 * 128, 64 * 128, 0, 0, 1, 0,
-                          0, 0.1f, nullptr, 0, 0, fake(4), SRT_BF16, 64 * 128, nullptr, 0, nullptr) ==
+                          0, 0.1f, nullptr, 0, 0, fake(4), SRT_BF16, 64 * 128, nullptr, 0, nullptr, nullptr) ==
          SRT_ERR_UNSUPPORTED);
   // ---- merge
   EXPECT(srt_attn_merge_states(fake(1), (float*)fake(2), fake(3), (float*)fake(4), SRT_F32, 1024, fake(1), SRT_F32,

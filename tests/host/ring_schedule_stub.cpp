@@ -33,9 +33,18 @@ hipError_t launch_rope_apply(const void* x, void* y, bool bf16, bool half_pairs,
   return hipSuccess;
 }
 
+hipError_t launch_zero_words(unsigned long long* p, int n, hipStream_t) {
+  const char* np;
+  long long op;
+  name_ptr(p, &np, &op);
+  printf("zero at=%s:%lld n=%d\n", np, op, n);
+  return hipSuccess;
+}
+
 static hipError_t log_prefill(const PrefillArgs& a, const char* kind) {
-  const char *nq, *nk, *nv, *no, *nl, *na, *nal;
-  long long oq, ok, ov, oo, ol, oa, oal;
+  const char *nq, *nk, *nv, *no, *nl, *na, *nal, *ns;
+  long long oq, ok, ov, oo, ol, oa, oal, os;
+  name_ptr(a.sched, &ns, &os);
   name_ptr(a.q, &nq, &oq);
   name_ptr(a.k, &nk, &ok);
   name_ptr(a.v, &nv, &ov);
@@ -45,10 +54,10 @@ static hipError_t log_prefill(const PrefillArgs& a, const char* kind) {
   name_ptr(a.acc_lse, &nal, &oal);
   printf("prefill %s q=%s:%lld k=%s:%lld v=%s:%lld out=%s:%lld lse=%s:%lld acc=%s:%lld acclse=%s:%lld Nq=%d Nk=%d "
          "qp=%lld kp=%lld qr=%lld kr=%lld step=%lld qhs=%lld kvhs=%lld ohs=%lld lhs=%lld ahs=%lld alhs=%lld "
-         "flags=%d obf16=%d window=%d sink=%d causal=%d\n",
+         "flags=%d obf16=%d window=%d sink=%d causal=%d sched=%s:%lld\n",
          kind, nq, oq, nk, ok, nv, ov, no, oo, nl, ol, na, oa, nal, oal, a.Nq, a.Nk, a.q_pos0, a.k_pos0, a.q_rope0,
          a.k_rope0, a.rope_step, a.q_hstride, a.kv_hstride, a.o_hstride, a.lse_hstride, a.acc_hstride,
-         a.acc_lse_hstride, a.rope_flags, a.out_bf16, a.window, a.sink, a.causal);
+         a.acc_lse_hstride, a.rope_flags, a.out_bf16, a.window, a.sink, a.causal, ns, os);
   return hipSuccess;
 }
 

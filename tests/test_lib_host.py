@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(srt):
 
 def test_status_strings(srt):
     lib = srt.lib()
-    assert lib.srt_abi_version() == 1
+    assert lib.srt_abi_version() == 2
     for s in range(5):
         assert lib.srt_status_string(s)
     assert lib.srt_status_string(99) == b"unknown status"
@@ -95,28 +95,28 @@ def test_abi_rejects_before_launch(srt):
     lib = srt.lib()
     fake = C.c_void_p(0x100000)      # never dereferenced: every call below fails validation first
     st = lib.srt_attn_prefill(None, fake, fake, 1, 1, 4, 2, 8, 8, 128, 1024, 1024, 0, 0, 1, 0, 0, 0.1,
-                              None, 0, 0, fake, 1, 1024, None, 0, None)
+                              None, 0, 0, fake, 1, 1024, None, 0, None, None)
     assert st == 1 and b"NULL" in lib.srt_last_error()
     st = lib.srt_attn_prefill(fake, fake, fake, 1, 1, 4, 3, 8, 8, 128, 1024, 1024, 0, 0, 1, 0, 0, 0.1,
-                              None, 0, 0, fake, 1, 1024, None, 0, None)
+                              None, 0, 0, fake, 1, 1024, None, 0, None, None)
     assert st == 1 and b"multiple" in lib.srt_last_error()
     st = lib.srt_attn_prefill(fake, fake, fake, 1, 1, 4, 2, 8, 8, 96, 768, 768, 0, 0, 1, 0, 0, 0.1,
-                              None, 0, 0, fake, 1, 768, None, 0, None)
+                              None, 0, 0, fake, 1, 768, None, 0, None, None)
     assert st == 2
     st = lib.srt_attn_prefill(fake, fake, fake, 1, 1, 4, 2, 8, 8, 128, 1024, 1024, 0, 0, 1, 0, 0, 0.1,
-                              None, 0, 3, fake, 1, 1024, None, 0, None)
+                              None, 0, 3, fake, 1, 1024, None, 0, None, None)
     assert st == 1 and b"table" in lib.srt_last_error()
     st = lib.srt_attn_prefill(fake, fake, fake, 1, 1, 4, 2, 8, 8, 128, 1024, 1024, 0, 0, 1, 0, 0, 0.1,
-                              fake, 4, 3, fake, 1, 1024, None, 0, None)
+                              fake, 4, 3, fake, 1, 1024, None, 0, None, None)
     assert st == 1 and b"outside table" in lib.srt_last_error()
     st = lib.srt_attn_prefill(fake, fake, fake, 1, 1, 4, 2, 8, 8, 128, 1024, 1024, 0, 0, 0, 16, 0, 0.1,
-                              None, 0, 0, fake, 1, 1024, None, 0, None)
+                              None, 0, 0, fake, 1, 1024, None, 0, None, None)
     assert st == 1 and b"causal" in lib.srt_last_error()
     st = lib.srt_attn_prefill(fake, fake, fake, 1, 1, 4, 2, 8, 8, 128, 1024, 1024, 0, 0, 1, -1, 0, 0.1,
-                              None, 0, 0, fake, 1, 1024, None, 0, None)
+                              None, 0, 0, fake, 1, 1024, None, 0, None, None)
     assert st == 1 and b"window" in lib.srt_last_error()
     st = lib.srt_attn_prefill(fake, fake, fake, 1, 1, 4, 2, 8, 8, 128, 1024, 1024, 0, 0, 1, 16, -4, 0.1,
-                              None, 0, 0, fake, 1, 1024, None, 0, None)
+                              None, 0, 0, fake, 1, 1024, None, 0, None, None)
     assert st == 1 and b"sink" in lib.srt_last_error()
     st = lib.srt_rope_apply(fake, fake, 1, 1, 1, 8, 128, 5, fake, 10, 0, None)
     assert st == 1 and b"outside table" in lib.srt_last_error()
@@ -204,9 +204,9 @@ def test_empty_problems_return_ok_without_pointers(srt):
     assert lib.srt_rope_apply(None, None, 0, 0, 4, 16, 128, 0, None, 0, 0, None) == 0
     # prefill: no query row (Nq = 0), then no batch
     assert lib.srt_attn_prefill(None, None, None, 1, 1, 4, 2, 0, 64, 128, 0, 0, 0, 0, 1, 0, 0, 0.1,
-                                None, 0, 0, None, 1, 0, None, 0, None) == 0
+                                None, 0, 0, None, 1, 0, None, 0, None, None) == 0
     assert lib.srt_attn_prefill(None, None, None, 1, 0, 4, 2, 64, 64, 128, 0, 0, 0, 0, 1, 0, 0, 0.1,
-                                None, 0, 0, None, 1, 0, None, 0, None) == 0
+                                None, 0, 0, None, 1, 0, None, 0, None, None) == 0
     assert lib.srt_attn_merge_states(None, None, None, None, 0, 0, None, 1, 0, None, 0, 1, 4, 0, 128, None) == 0
     assert lib.srt_attn_decode_splitk(None, None, None, 1, 0, 32, 8, 1024, 128, None, 64, 0.1, None, 0, 0, 0, 0,
                                       None, 0, None, None, None) == 0
@@ -216,7 +216,7 @@ def test_empty_problems_return_ok_without_pointers(srt):
                                  None, 0, 0, None, 0, None, None, None, None) == 0
     # sizes are still validated first: a negative size is an error even when the problem is empty
     assert lib.srt_attn_prefill(None, None, None, 1, 1, 4, 2, -1, 64, 128, 0, 0, 0, 0, 1, 0, 0, 0.1,
-                                None, 0, 0, None, 1, 0, None, 0, None) == 1
+                                None, 0, 0, None, 1, 0, None, 0, None, None) == 1
     assert lib.srt_attn_merge_states(None, None, None, None, 0, 0, None, 1, 0, None, 0, 1, -4, 0, 128, None) == 1
 
 
@@ -229,7 +229,7 @@ def test_prefill_rejects_misaligned_pointers_and_strides(srt):
     odd = C.c_void_p(0x100008)         # 8-byte aligned only
     call = lambda q, k, v, out, tab, flags, qs, ks, os_: lib.srt_attn_prefill(
         q, k, v, 1, 1, 4, 2, 8, 8, 128, qs, ks, 0, 0, 1, 0, 0, 0.1, tab, 64 if tab else 0, flags, out, 1, os_,
-        None, 0, None)
+        None, 0, None, None)
     for args in ((odd, good, good, good, None, 0), (good, odd, good, good, None, 0),
                  (good, good, odd, good, None, 0), (good, good, good, odd, None, 0),
                  (good, good, good, good, odd, 1)):
@@ -237,6 +237,10 @@ def test_prefill_rejects_misaligned_pointers_and_strides(srt):
     for qs, ks, os_ in ((1028, 1024, 1024), (1024, 1028, 1024), (1024, 1024, 1028)):
         assert call(good, good, good, good, None, 0, qs, ks, os_) == 1
         assert b"multiples of 8" in lib.srt_last_error()
+    # the scheduling block: 8-byte alignment
+    assert lib.srt_attn_prefill(good, good, good, 1, 1, 4, 2, 8, 8, 128, 1024, 1024, 0, 0, 1, 0, 0, 0.1, None, 0, 0,
+                                good, 1, 1024, None, 0, C.c_void_p(0x100004), None) == 1
+    assert b"sched" in lib.srt_last_error()
 
 
 def test_binding_rejects_host_tensors_and_wrong_tables(srt):

@@ -71,8 +71,16 @@ def test_schedule_scores_every_visible_pair_once(stub, mode, P, N, window, sink,
     want[~rows] = 0
     got = np.zeros((N, N), dtype=int)
     chains = {}
+    sched = None
     for ln in lines[1:]:
         kv = _kv(ln)
+        if ln.startswith("zero"):
+            # the prefill launches' scheduling block: zero-filled once, before any launch
+            assert sched is None and not chains and kv["n"] == "10"
+            sched = kv["at"]
+            name, off = _loc(sched)
+            assert name == "ws" and off % 8 == 0 and off + 80 <= ws_bytes
+            continue
         if ln.startswith("rope"):
             assert "mode=%d" % MODES[mode] in ln and "P=%d" % P in ln and "C=%d" % C in ln
             continue
@@ -92,10 +100,11 @@ def test_schedule_scores_every_visible_pair_once(stub, mode, P, N, window, sink,
             assert all(pos[k0 + u] == pos[k0] + step * u for u in range(Nk))
             chains.setdefault(q0, []).append((kv["out"], kv["obf16"], kv["acc"], kv["lse"], kv["acclse"],
                                               int(kv["ohs"]), int(kv["ahs"])))
+            assert kv["sched"] == sched                  # every launch shares the one block
             for key in ("out", "lse", "acc", "acclse"):
                 name, off = _loc(kv[key])
                 if name == "ws":
-                    assert 0 <= off < ws_bytes
+                    assert 0 <= off < ws_bytes and off + 80 <= _loc(sched)[1]   # state before the block
         assert not ln.startswith("merge")              # no separate merge launches
     np.testing.assert_array_equal(got, want)
     for q0, ch in chains.items():
