@@ -295,9 +295,11 @@ size_t srt_attn_decode_noalloc_max_workspace(void);
  * for BF16 a copy of q ([B][Hq][Nq][D], rotated with SRT_ROTATE_Q, always
  * multiplied by sm_scale log2(e) and rounded once exactly as the forward
  * kernel forms its q, so the recomputed scores equal the forward's) and a
- * rotated copy of k ([B][Hkv][Nk][D], with SRT_ROTATE_K), each region 256-byte
- * aligned.  The copies are made once per call, so the kernels stage tiles that
- * need no rotation.  Returns SRT_ERR_INVALID for a bad dtype, negative sizes or
+ * rotated copy of k ([B][Hkv][Nk][D], with SRT_ROTATE_K) and two scheduling
+ * blocks (the run-time work assignment of srt_attn_prefill, for the dk/dv and
+ * the dq kernel, zero-filled by each call), each region 256-byte aligned.  The
+ * copies are made once per call, so the kernels stage tiles that need no
+ * rotation.  Returns SRT_ERR_INVALID for a bad dtype, negative sizes or
  * unknown flags.
  */
 int srt_attn_backward_workspace_size(int dtype, int B, int Hq, int Hkv, int Nq, int Nk, int D, int rope_flags,

@@ -356,14 +356,14 @@ int srt_attn_decode_splitk_noalloc(const void* q, const void* k_cache, const voi
 }
 
 namespace {
-// Backward workspace: delta, then (bf16 only) the scaled, rotated q copy and the rotated k copy, each 256-byte
-// aligned.
+// Backward workspace: delta, then (bf16 only) the scaled, rotated q copy, the rotated k copy and the two
+// scheduling blocks of the dk/dv and dq kernels, each 256-byte aligned.
 struct BwdWorkspace {
-  size_t delta, q_rot, k_rot, total;   // offsets of the regions (q_rot / k_rot: 0 when absent) and the size
+  size_t delta, q_rot, k_rot, sched, total;   // offsets of the regions (0 when absent) and the size
 };
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 BwdWorkspace bwd_workspace(int dtype, int B, int Hq, int Hkv, int Nq, int Nk, int D, int rope_flags) {
-  BwdWorkspace w{0, 0, 0, 0};
+  BwdWorkspace w{0, 0, 0, 0, 0};
   size_t off = round256((size_t)B * Hq * Nq * sizeof(float));
   if (dtype == SRT_BF16 && (size_t)B * Nq > 0) {
     w.q_rot = off;
@@ -372,6 +372,10 @@ BwdWorkspace bwd_workspace(int dtype, int B, int Hq, int Hkv, int Nq, int Nk, in
   if (dtype == SRT_BF16 && (rope_flags & SRT_ROTATE_K) && (size_t)B * Nk > 0) {
     w.k_rot = off;
     off += round256((size_t)B * Hkv * Nk * D * 2);
+  }
+  if (dtype == SRT_BF16 && (size_t)B * Nq > 0) {
+    w.sched = off;
+    off += round256(2 * srt::kSchedBlockWords * sizeof(unsigned long long));
   }
   w.total = off;
   return w;
@@ -453,6 +457,7 @@ int srt_attn_backward(const void* q, const void* k, const void* v, const void* o
     if (e != hipSuccess) return hip_status(e, "attn_backward: rotating k");
     a.k_rot = kr;
   }
+  if (ws.sched) a.sched = reinterpret_cast<unsigned long long*>((char*)workspace + ws.sched);
   a.table = table_dev; a.dq = dq; a.dk = dk; a.dv = dv;
   a.q_pos0 = q_pos0; a.k_pos0 = k_pos0;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.D = D;

@@ -22,6 +22,7 @@
 // keep every product in fp32 on the vector ALUs.  Gradients are written in
 // fp32.
 #include "mfma_common.h"
+#include "item_queue.h"
 
 namespace srt {
 namespace {
@@ -469,11 +470,21 @@ struct Dkdv2Smem {
 template <bool HALF, bool WIN>
 __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) {
   __shared__ Dkdv2Smem sm;
+  __shared__ int s_item;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave & 3, role = wave >> 2;
   const int l32 = lane & 31, hl = lane >> 5;
-  const int hk = blockIdx.x, kblk = blockIdx.y, b = blockIdx.z;
+  // item (key block y, batch b, KV head x), x fastest, key blocks from the first (heavy first)
+  int item = (int)blockIdx.x;
+  if (a.sched) {
+    if (tid == 0) s_item = sched_take(a.sched, a.Hkv, a.B, (a.Nk + kKVKeys - 1) / kKVKeys);
+    __syncthreads();
+    item = __builtin_amdgcn_readfirstlane(s_item);
+  }
+  const int hk = item % a.Hkv;
+  const int kblk = item / a.Hkv / a.B;
+  const int b = item / a.Hkv - kblk * a.B;
   const int G = a.Hq / a.Hkv;
   const int wk0 = kblk * kKVKeys + grp * 32;
   const int key = wk0 + l32;
@@ -666,6 +677,7 @@ __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) 
       if (i <= nit) dstep(C0{}, dp_b, dp_a, i < nit), ++i;
     }
   }
+  if (a.sched && tid == 0) sched_release(a.sched, gridDim.x);
   if (!key_ok) return;
   const long long krow = ((long long)b * a.Hkv + hk) * a.Nk + key;
   if (role == 0) store_grad<HALF>(a.dv + krow * kD, acc, 1.f, false, tab2, kpos, hl);
@@ -689,6 +701,7 @@ struct DqSmem {
 template <bool HALF, bool WIN>
 __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_bf16_kernel(BwdArgs a) {
   __shared__ DqSmem sm;
+  __shared__ int s_item;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
@@ -696,9 +709,19 @@ __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_bf16_kernel(BwdArgs a) {
   const int HPW = G < 4 ? G : 4;
   const int RB = kQWaves / HPW;
   const int quads = G > 4 ? G / 4 : 1;
-  const int hk = blockIdx.x / quads, quad = blockIdx.x - hk * quads;
-  const int b = blockIdx.z;
-  const int qt = a.causal ? ((int)gridDim.y - 1 - (int)blockIdx.y) : (int)blockIdx.y;
+  const int HX = a.Hkv * quads;
+  const int ntq = (a.Nq + 32 * RB - 1) / (32 * RB);
+  // item (query-tile rank y, batch b, workgroup head x), x fastest, y = 0 the last query tile
+  int item = (int)blockIdx.x;
+  if (a.sched) {
+    if (tid == 0) s_item = sched_take(a.sched, HX, a.B, ntq);
+    __syncthreads();
+    item = __builtin_amdgcn_readfirstlane(s_item);
+  }
+  const int xh = item % HX, yq = item / HX / a.B;
+  const int b = item / HX - yq * a.B;
+  const int hk = xh / quads, quad = xh - hk * quads;
+  const int qt = a.causal ? (ntq - 1 - yq) : yq;
   const int hq = hk * G + quad * 4 + (wave % HPW);
   const int wrow0 = qt * (32 * RB) + (wave / HPW) * 32;
   const int wg_row_last = min(a.Nq, (qt + 1) * 32 * RB) - 1;
@@ -840,6 +863,7 @@ __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_bf16_kernel(BwdArgs a) {
     }
     if (t < ntiles) tile(B0{}, t);
   }
+  if (a.sched && tid == 0) sched_release(a.sched, gridDim.x);
   if (!row_ok) return;
   store_grad<HALF>(a.dq + qrow * kD, dqacc, a.sm_scale, (a.rope_flags & 1) != 0, tab2, qpos, hl);
 }
@@ -888,15 +912,25 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
     if (a.D != kD) return hipErrorInvalidValue;
     const int G = a.Hq / a.Hkv;
     if (!(G == 1 || G == 2 || G % 4 == 0)) return hipErrorInvalidValue;
-    const dim3 gkv(a.Hkv, (a.Nk + kKVKeys - 1) / kKVKeys, a.B);
+    // run-time assignment (two scheduling blocks: dk/dv, then dq) when a
+    // kernel runs more than two rounds of workgroups
+    BwdArgs akv = a, aq = a;
+    akv.sched = aq.sched = nullptr;
+    const long long nkv = (long long)a.Hkv * ((a.Nk + kKVKeys - 1) / kKVKeys) * a.B;
+    const dim3 gkv((unsigned)nkv);
     const bool win = a.causal && a.window > 0;
+    if (a.sched) {
+      e = launch_zero_words(a.sched, 2 * kSchedBlockWords, stream);
+      if (e != hipSuccess) return e;
+      if (nkv > 2LL * compute_units()) akv.sched = a.sched;
+    }
     if (a.Nk > 0) {
       if (win) {
-        if (half) hipLaunchKernelGGL((bwd_dkdv2_bf16_kernel<true, true>), gkv, dim3(kKV2Threads), 0, stream, a);
-        else hipLaunchKernelGGL((bwd_dkdv2_bf16_kernel<false, true>), gkv, dim3(kKV2Threads), 0, stream, a);
+        if (half) hipLaunchKernelGGL((bwd_dkdv2_bf16_kernel<true, true>), gkv, dim3(kKV2Threads), 0, stream, akv);
+        else hipLaunchKernelGGL((bwd_dkdv2_bf16_kernel<false, true>), gkv, dim3(kKV2Threads), 0, stream, akv);
       } else {
-        if (half) hipLaunchKernelGGL((bwd_dkdv2_bf16_kernel<true, false>), gkv, dim3(kKV2Threads), 0, stream, a);
-        else hipLaunchKernelGGL((bwd_dkdv2_bf16_kernel<false, false>), gkv, dim3(kKV2Threads), 0, stream, a);
+        if (half) hipLaunchKernelGGL((bwd_dkdv2_bf16_kernel<true, false>), gkv, dim3(kKV2Threads), 0, stream, akv);
+        else hipLaunchKernelGGL((bwd_dkdv2_bf16_kernel<false, false>), gkv, dim3(kKV2Threads), 0, stream, akv);
       }
       e = hipGetLastError();
       if (e != hipSuccess) return e;
@@ -904,13 +938,15 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
     const int HPW = G < 4 ? G : 4;
     const int rows_per_wg = 32 * (kQWaves / HPW);
     const int quads = G > 4 ? G / 4 : 1;
-    const dim3 gq(a.Hkv * quads, (a.Nq + rows_per_wg - 1) / rows_per_wg, a.B);
+    const long long nq = (long long)a.Hkv * quads * ((a.Nq + rows_per_wg - 1) / rows_per_wg) * a.B;
+    const dim3 gq((unsigned)nq);
+    if (a.sched && nq > 4LL * compute_units()) aq.sched = a.sched + kSchedBlockWords;   // two workgroups per CU
     if (win) {
-      if (half) hipLaunchKernelGGL((bwd_dq_bf16_kernel<true, true>), gq, dim3(kQThreads), 0, stream, a);
-      else hipLaunchKernelGGL((bwd_dq_bf16_kernel<false, true>), gq, dim3(kQThreads), 0, stream, a);
+      if (half) hipLaunchKernelGGL((bwd_dq_bf16_kernel<true, true>), gq, dim3(kQThreads), 0, stream, aq);
+      else hipLaunchKernelGGL((bwd_dq_bf16_kernel<false, true>), gq, dim3(kQThreads), 0, stream, aq);
     } else {
-      if (half) hipLaunchKernelGGL((bwd_dq_bf16_kernel<true, false>), gq, dim3(kQThreads), 0, stream, a);
-      else hipLaunchKernelGGL((bwd_dq_bf16_kernel<false, false>), gq, dim3(kQThreads), 0, stream, a);
+      if (half) hipLaunchKernelGGL((bwd_dq_bf16_kernel<true, false>), gq, dim3(kQThreads), 0, stream, aq);
+      else hipLaunchKernelGGL((bwd_dq_bf16_kernel<false, false>), gq, dim3(kQThreads), 0, stream, aq);
     }
     return hipGetLastError();
   }

@@ -73,9 +73,12 @@ struct PrefillArgs {
   unsigned long long* sched;
 };
 constexpr int kSchedWords = 10;   // 8 per-XCD queues, the shared pool, the count of finished workgroups
+constexpr int kSchedBlockWords = 16;   // one block: SRT_PREFILL_SCHED_BYTES = 128 bytes
 
-// Zero-fill n 64-bit words on the stream (a kernel, so that it may be captured).
+// Zero-fill n <= 64 64-bit words on the stream (a kernel, so that it may be captured).
 hipError_t launch_zero_words(unsigned long long* p, int n, hipStream_t stream);
+// Compute units of the current device.
+int compute_units();
 
 hipError_t launch_prefill_bf16_d128(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
@@ -143,6 +146,9 @@ struct BwdArgs {
   int rope_flags;         // bit0: q rotated on load, bit1: k, bit2: half-split pairs
   int bf16;
   float sm_scale;
+  // bf16: two scheduling blocks of kSchedBlockWords words in the workspace
+  // (dk/dv, then dq), zero-filled by the launcher; see PrefillArgs::sched
+  unsigned long long* sched;
 };
 
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);

@@ -146,15 +146,17 @@ def test_abi_rejects_before_launch(srt):
     st = lib.srt_attn_merge_states(fake, fake, fake, fake, 0, 96, fake, 0, 96, None, 0, 1, 1, 1, 96, None)
     assert st == 2
     # backward: workspace size, bad D, window without causal, missing workspace
-    # delta (fp32 [B][Hq][Nq]), then for bf16 the rotated q and k copies, each region 256-byte aligned
+    # delta (fp32 [B][Hq][Nq]), then for bf16 the rotated q and k copies and two 128-byte scheduling
+    # blocks, each region 256-byte aligned
     ws = lambda *args: (lib.srt_attn_backward_workspace_size(*args, C.byref(n)), n.value)
     assert ws(0, 2, 8, 2, 100, 50, 64, 3) == (0, 6400)
     qcopy = 2 * 8 * 100 * 128 * 2               # bf16 always keeps a scaled copy of q
-    assert ws(1, 2, 8, 2, 100, 50, 128, 0) == (0, 6400 + qcopy)
-    assert ws(1, 2, 8, 2, 100, 50, 128, 1) == (0, 6400 + qcopy)
-    assert ws(1, 2, 8, 2, 100, 50, 128, 2) == (0, 6400 + qcopy + 2 * 2 * 50 * 128 * 2)
+    sched = 256
+    assert ws(1, 2, 8, 2, 100, 50, 128, 0) == (0, 6400 + qcopy + sched)
+    assert ws(1, 2, 8, 2, 100, 50, 128, 1) == (0, 6400 + qcopy + sched)
+    assert ws(1, 2, 8, 2, 100, 50, 128, 2) == (0, 6400 + qcopy + 2 * 2 * 50 * 128 * 2 + sched)
     assert ws(1, 2, 8, 2, 0, 50, 128, 3) == (0, 2 * 2 * 50 * 128 * 2)
-    assert ws(1, 1, 1, 1, 3, 5, 128, 7) == (0, 256 + 768 + 1280)
+    assert ws(1, 1, 1, 1, 3, 5, 128, 7) == (0, 256 + 768 + 1280 + sched)
     assert ws(1, 2, 8, 2, 100, 50, 128, 8)[0] == 1 and b"rope_flags" in lib.srt_last_error()
     assert ws(2, 2, 8, 2, 100, 50, 128, 0)[0] == 1
     bw = lambda dt, D, causal, window, ws, wsb: lib.srt_attn_backward(
