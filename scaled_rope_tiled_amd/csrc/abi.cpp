@@ -437,7 +437,11 @@ int srt_attn_backward(const void* q, const void* k, const void* v, const void* o
   a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse; a.delta = (float*)workspace;
   // rotate q and k once into the workspace ([LC] §2.4: each row by its own position)
   const bool half_pairs = (rope_flags & SRT_PAIR_HALF) != 0;
-  if (ws.q_rot) {
+  if (ws.q_rot && !(rope_flags & SRT_ROTATE_Q) && sm_scale != 0.f) {
+    // q not rotated: the kernels use it exactly as the forward kernel does (unscaled; the scores are scaled
+    // in fp32), so no copy is made
+    a.q_rot = q;
+  } else if (ws.q_rot) {
     // q~ = bf16(rotated q * sm_scale log2(e)), rounded once exactly as the forward kernel forms it, so the
     // backward's scores (and P = exp2(S - lse)) are those the forward normalised
     void* qr = (char*)workspace + ws.q_rot;

@@ -24,6 +24,8 @@
 #include "mfma_common.h"
 #include "item_queue.h"
 
+#include <type_traits>
+
 namespace srt {
 namespace {
 
@@ -467,7 +469,11 @@ struct Dkdv2Smem {
 };
 
 
-template <bool HALF, bool WIN>
+// EXACT_Q: q enters unrotated and unscaled (no SRT_ROTATE_Q), exactly as the
+// forward kernel then uses it; the S accumulator starts at -lse / sm_scale
+// and its product times sm_scale log2(e) is the forward's S - lse in log2
+// units (one multiply per score instead of a rounding of q * sm_scale log2(e)).
+template <bool HALF, bool WIN, bool EXACT_Q>
 __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) {
   __shared__ Dkdv2Smem sm;
   __shared__ int s_item;
@@ -476,7 +482,7 @@ __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) 
   const int grp = wave & 3, role = wave >> 2;
   const int l32 = lane & 31, hl = lane >> 5;
   // item (key block y, batch b, KV head x), x fastest, key blocks from the first (heavy first)
-  int item = (int)blockIdx.x;
+  int item = a.item0 + (int)blockIdx.x;
   if (a.sched) {
     if (tid == 0) s_item = sched_take(a.sched, a.Hkv, a.B, (a.Nk + kKVKeys - 1) / kKVKeys);
     __syncthreads();
@@ -492,6 +498,7 @@ __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) 
   const long long kpos = a.k_pos0 + key;
   const float4* tab4 = reinterpret_cast<const float4*>(a.table);
   const float2* tab2 = reinterpret_cast<const float2*>(a.table);
+  const float cq = a.sm_scale * kLog2e;   // (EXACT_Q)
 
   // query rows [r_lo, r_hi) that can see some key of this workgroup
   const int wg_k0 = kblk * kKVKeys;
@@ -523,7 +530,7 @@ __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) 
     if (wave == 0) {
       const float* src = lane < 32 ? a.lse + hrow : a.delta + hrow;
       const float x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(raw_buffer(src, rows * 4), l32 * 4, 0, 0));
-      ldv = lane < 32 ? x * -kLog2e : -x;
+      ldv = lane < 32 ? x * (EXACT_Q ? -1.0f / a.sm_scale : -kLog2e) : -x;
     }
     hrow += 32;
     if (++itq == t0 + ntq) {
@@ -599,7 +606,7 @@ __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) 
         mma_rows1c(lds_off(&sm.q[nb][l32 * kTStr + hl * 8]), breg, s_out, init_rows(&sm.ld[nb][0]));   // stale past the end
         float p[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) p[j] = __builtin_amdgcn_exp2f(s_in[j]);
+        for (int j = 0; j < 16; ++j) p[j] = __builtin_amdgcn_exp2f(EXACT_Q ? s_in[j] * cq : s_in[j]);
         if (ct < tm_lo || ct > tm_hi) {
           const int qt0 = ct * 32;
           const long long relb = a.q_pos0 + qt0 - kpos;
@@ -680,8 +687,9 @@ __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) 
   if (a.sched && tid == 0) sched_release(a.sched, gridDim.x);
   if (!key_ok) return;
   const long long krow = ((long long)b * a.Hkv + hk) * a.Nk + key;
+  // dK~ = sm_scale dS^T q: with q~ carrying sm_scale log2(e) the factor is ln 2
   if (role == 0) store_grad<HALF>(a.dv + krow * kD, acc, 1.f, false, tab2, kpos, hl);
-  else store_grad<HALF>(a.dk + krow * kD, acc, kLn2, (a.rope_flags & 2) != 0, tab2, kpos, hl);
+  else store_grad<HALF>(a.dk + krow * kD, acc, EXACT_Q ? a.sm_scale : kLn2, (a.rope_flags & 2) != 0, tab2, kpos, hl);
 }
 
 // ---- dq: a workgroup of 4 waves owns one KV head and 32 * (4 / HPW) query
@@ -698,7 +706,7 @@ struct DqSmem {
   alignas(16) __hip_bfloat16 v[2][32 * kRStr];
 };
 
-template <bool HALF, bool WIN>
+template <bool HALF, bool WIN, bool EXACT_Q>
 __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_bf16_kernel(BwdArgs a) {
   __shared__ DqSmem sm;
   __shared__ int s_item;
@@ -712,7 +720,7 @@ __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_bf16_kernel(BwdArgs a) {
   const int HX = a.Hkv * quads;
   const int ntq = (a.Nq + 32 * RB - 1) / (32 * RB);
   // item (query-tile rank y, batch b, workgroup head x), x fastest, y = 0 the last query tile
-  int item = (int)blockIdx.x;
+  int item = a.item0 + (int)blockIdx.x;
   if (a.sched) {
     if (tid == 0) s_item = sched_take(a.sched, HX, a.B, ntq);
     __syncthreads();
@@ -737,7 +745,7 @@ __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_bf16_kernel(BwdArgs a) {
   const float c2 = a.sm_scale * kLog2e;
   bf16x8 qreg[8], doreg[8];
   load_row_rotated<HALF>(reinterpret_cast<const __hip_bfloat16*>(a.q) + qrow * kD, row_ok, (a.rope_flags & 1) != 0,
-                         tab4, qpos, hl, qreg, c2);
+                         tab4, qpos, hl, qreg, EXACT_Q ? 1.f : c2);
   load_row_rotated<HALF>(reinterpret_cast<const __hip_bfloat16*>(a.dout) + qrow * kD, row_ok, false, tab4, 0, hl,
                          doreg);
   // Rows past Nq have q = dO = 0, so S^T = dP^T = 0 and dS = 0.  A row with no
@@ -747,7 +755,7 @@ __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_bf16_kernel(BwdArgs a) {
   f32x16 negl, negd, dqacc[4];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    negl[j] = -lse2;
+    negl[j] = EXACT_Q ? -lse2 / c2 : -lse2;   // (EXACT_Q: the scores are multiplied by c2 after the product)
     negd[j] = -dl;
   }
 #pragma unroll
@@ -830,6 +838,10 @@ __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_bf16_kernel(BwdArgs a) {
     // S^T = k~ q~^T - lse and dP^T = V dO^T - delta: lane = query, rows = 16 of the tile's keys
     f32x16 s, dp;
     mma_rows2c(k_row + BUF * kKBuf, qreg, s, negl, v_row + BUF * kVBuf, doreg, dp, negd);
+    if constexpr (EXACT_Q) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s[j] *= c2;
+    }
     if (key0 > mask_hi || (WIN && key0 < mask_lo && key0 + 32 > csink)) {
       const int base = key0 + hl * 4;
       const int rel = klim - base, rlo = klo - base, rsk = csink - base;
@@ -916,38 +928,56 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
     // kernel runs more than two rounds of workgroups
     BwdArgs akv = a, aq = a;
     akv.sched = aq.sched = nullptr;
+    akv.item0 = aq.item0 = 0;
     const long long nkv = (long long)a.Hkv * ((a.Nk + kKVKeys - 1) / kKVKeys) * a.B;
-    const dim3 gkv((unsigned)nkv);
-    const bool win = a.causal && a.window > 0;
-    if (a.sched) {
-      e = launch_zero_words(a.sched, 2 * kSchedBlockWords, stream);
-      if (e != hipSuccess) return e;
-      if (nkv > 2LL * compute_units()) akv.sched = a.sched;
-    }
-    if (a.Nk > 0) {
-      if (win) {
-        if (half) hipLaunchKernelGGL((bwd_dkdv2_bf16_kernel<true, true>), gkv, dim3(kKV2Threads), 0, stream, akv);
-        else hipLaunchKernelGGL((bwd_dkdv2_bf16_kernel<false, true>), gkv, dim3(kKV2Threads), 0, stream, akv);
-      } else {
-        if (half) hipLaunchKernelGGL((bwd_dkdv2_bf16_kernel<true, false>), gkv, dim3(kKV2Threads), 0, stream, akv);
-        else hipLaunchKernelGGL((bwd_dkdv2_bf16_kernel<false, false>), gkv, dim3(kKV2Threads), 0, stream, akv);
-      }
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
     const int HPW = G < 4 ? G : 4;
     const int rows_per_wg = 32 * (kQWaves / HPW);
     const int quads = G > 4 ? G / 4 : 1;
     const long long nq = (long long)a.Hkv * quads * ((a.Nq + rows_per_wg - 1) / rows_per_wg) * a.B;
-    const dim3 gq((unsigned)nq);
-    if (a.sched && nq > 4LL * compute_units()) aq.sched = a.sched + kSchedBlockWords;   // two workgroups per CU
-    if (win) {
-      if (half) hipLaunchKernelGGL((bwd_dq_bf16_kernel<true, true>), gq, dim3(kQThreads), 0, stream, aq);
-      else hipLaunchKernelGGL((bwd_dq_bf16_kernel<false, true>), gq, dim3(kQThreads), 0, stream, aq);
-    } else {
-      if (half) hipLaunchKernelGGL((bwd_dq_bf16_kernel<true, false>), gq, dim3(kQThreads), 0, stream, aq);
-      else hipLaunchKernelGGL((bwd_dq_bf16_kernel<false, false>), gq, dim3(kQThreads), 0, stream, aq);
+    if (nkv > 0x7fffffffLL || nq > 0x7fffffffLL) return hipErrorInvalidValue;
+    const bool win = a.causal && a.window > 0;
+    if (a.sched) {
+      e = launch_zero_words(a.sched, 2 * kSchedBlockWords, stream);
+      if (e != hipSuccess) return e;
+      if (nkv > 2LL * compute_units() && nkv <= kMaxLaunchItems) akv.sched = a.sched;
     }
+    // a grid too large for one launch goes in launches of kMaxLaunchItems items (fixed assignment)
+    auto launch_items = [&](auto kernel, BwdArgs& args, long long n_items, int threads) {
+      for (long long base = 0; base < n_items; base += kMaxLaunchItems) {
+        args.item0 = (int)base;
+        const long long n = n_items - base < kMaxLaunchItems ? n_items - base : kMaxLaunchItems;
+        hipLaunchKernelGGL(kernel, dim3((unsigned)n), dim3(threads), 0, stream, args);
+      }
+    };
+    // q used exactly as given (no rotation of q, a non-zero scale): see EXACT_Q
+    const bool exact = !(a.rope_flags & 1) && a.sm_scale != 0.f;
+    auto kv_kernel = [&](auto h, auto w, auto x) {
+      launch_items(bwd_dkdv2_bf16_kernel<decltype(h)::value, decltype(w)::value, decltype(x)::value>, akv, nkv,
+                   kKV2Threads);
+    };
+    auto q_kernel = [&](auto h, auto w, auto x) {
+      launch_items(bwd_dq_bf16_kernel<decltype(h)::value, decltype(w)::value, decltype(x)::value>, aq, nq,
+                   kQThreads);
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+    auto pick = [&](auto launch) {
+      if (win) {
+        if (half) { if (exact) launch(T{}, T{}, T{}); else launch(T{}, T{}, F{}); }
+        else { if (exact) launch(F{}, T{}, T{}); else launch(F{}, T{}, F{}); }
+      } else {
+        if (half) { if (exact) launch(T{}, F{}, T{}); else launch(T{}, F{}, F{}); }
+        else { if (exact) launch(F{}, F{}, T{}); else launch(F{}, F{}, F{}); }
+      }
+    };
+    if (a.Nk > 0) {
+      pick(kv_kernel);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (a.sched && nq > 4LL * compute_units() && nq <= kMaxLaunchItems)
+      aq.sched = a.sched + kSchedBlockWords;   // (two workgroups per CU)
+    pick(q_kernel);
     return hipGetLastError();
   }
   if (a.D != 64) return hipErrorInvalidValue;

@@ -110,7 +110,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   const int quads = G > 4 ? G / 4 : 1;
   const int HX = a.Hkv * quads;                  // workgroup heads
   const int ntiles_q = (a.Nq + kBM * RB - 1) / (kBM * RB);
-  int item = (int)blockIdx.x;
+  int item = a.item0 + (int)blockIdx.x;
   if (a.sched) {
     if (tid == 0) s_item = sched_take(a.sched, HX, a.B, ntiles_q);
     __syncthreads();
@@ -710,14 +710,22 @@ hipError_t launch_prefill_bf16_d128(const PrefillArgs& a, hipStream_t stream) {
   const int quads = G > 4 ? G / 4 : 1;
   const long long items = (long long)a.Hkv * quads * ((a.Nq + rows_per_wg - 1) / rows_per_wg) * a.B;
   if (items > 0x7fffffffLL) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)items), block(kThreads);
   // the run-time assignment pays one atomic round trip per workgroup and
-  // helps only when the XCDs run several workgroups each
+  // helps only when the XCDs run several workgroups each; a grid too large
+  // for one launch goes in launches of kMaxLaunchItems with the fixed one
   PrefillArgs la = a;
-  if (la.sched && items <= 2LL * compute_units()) la.sched = nullptr;
+  la.item0 = 0;
+  if (la.sched && (items <= 2LL * compute_units() || items > kMaxLaunchItems)) la.sched = nullptr;
   const bool rot_k = (a.rope_flags & 2) != 0, half = (a.rope_flags & 4) != 0;
   const bool win = a.window > 0, scale_s = (a.rope_flags & 1) == 0;
-  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, block, 0, stream, la); };
+  const dim3 block(kThreads);
+  auto go = [&](auto kernel) {
+    for (long long base = 0; base < items; base += kMaxLaunchItems) {
+      la.item0 = (int)base;
+      const long long n = items - base < kMaxLaunchItems ? items - base : kMaxLaunchItems;
+      hipLaunchKernelGGL(kernel, dim3((unsigned)n), block, 0, stream, la);
+    }
+  };
   // half-split pairing changes only what is rotated: without a rotation it is
   // the same kernel
   auto pick = [&](auto wc, auto sc) {

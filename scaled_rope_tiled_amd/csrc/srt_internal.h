@@ -71,7 +71,9 @@ struct PrefillArgs {
   // workgroups: kSchedWords zero-filled 64-bit counters, left zeroed by the
   // launch's last workgroup; nullptr keeps the fixed assignment by grid index.
   unsigned long long* sched;
+  int item0;            // first item of this launch (launches of more than kMaxLaunchItems items are split)
 };
+constexpr int kMaxLaunchItems = 1 << 22;   // workgroups per launch: x-dimension work-items stay below 2^32
 constexpr int kSchedWords = 10;   // 8 per-XCD queues, the shared pool, the count of finished workgroups
 constexpr int kSchedBlockWords = 16;   // one block: SRT_PREFILL_SCHED_BYTES = 128 bytes
 
@@ -149,6 +151,7 @@ struct BwdArgs {
   // bf16: two scheduling blocks of kSchedBlockWords words in the workspace
   // (dk/dv, then dq), zero-filled by the launcher; see PrefillArgs::sched
   unsigned long long* sched;
+  int item0;            // first item of this launch (see PrefillArgs::item0)
 };
 
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);

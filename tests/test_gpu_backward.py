@@ -170,3 +170,31 @@ def test_backward_yarn_32k_full_size_sampled():
         print(f"32K kv head {hk}: sum dv vs sum dO rel err {rel:.3g}", flush=True)
         assert rel <= 1e-2
     assert worst <= 2e-2
+
+
+@pytest.mark.parametrize("rotate", [False, True], ids=["given", "rotated"])
+def test_backward_recomputes_the_forward_softmax(rotate):
+    """With a one-key window every query sees only its own position, so the
+    forward's weight is exactly 1: dv of a key is the sum of its group's dO
+    and dq = dk = 0.  At sm_scale = 0.5 the scores reach about 30 in log2
+    units, where a backward that rounded q * sm_scale log2(e) differently from
+    the forward would be off by about 2^-9 of that (4 %).  The backward must
+    recompute the forward's own P (given q: kept exact on both sides; rotated
+    q: the same one bf16 rounding on both sides)."""
+    srt = need_gpu()
+    B, Hq, Hkv, N, D = 1, 8, 2, 256, 128
+    q, k, v = qkv(B, Hq, Hkv, N, N, D, torch.bfloat16, 61)
+    do = synth.randn((B, Hq, N, D), torch.bfloat16, 61, synth.DO_ID, "cuda")
+    table, _ = device_table(srt, YARN_SMALL, D, N)
+    flags = (srt.ROTATE_Q | srt.ROTATE_K) if rotate else 0
+    kw = dict(table=table, rope_flags=flags, sm_scale=0.5, window=1)
+    o, l = srt.attn_prefill(q, k, v, **kw)
+    dq, dk, dv = srt.attn_backward(q, k, v, o, do, l, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o, v.repeat_interleave(Hq // Hkv, dim=1))
+    want = do.float().reshape(B, Hkv, Hq // Hkv, N, D).sum(dim=2)
+    err = float((dv - want).abs().max())
+    print(f"rotate={rotate}: |dv - sum dO| {err:.3g}, |dq| {float(dq.abs().max()):.3g}, |dk| {float(dk.abs().max()):.3g}",
+          flush=True)
+    assert err <= 1e-4 * float(want.abs().max())
+    assert float(dq.abs().max()) <= 1e-3 and float(dk.abs().max()) <= 1e-3
