@@ -292,9 +292,11 @@ size_t srt_attn_decode_noalloc_max_workspace(void);
 /*
  * srt_attn_backward_workspace_size - bytes of workspace srt_attn_backward
  * needs for these arguments: delta = rowsum(dO * O), fp32 [B][Hq][Nq], and
- * for BF16 a copy of q ([B][Hq][Nq][D], rotated with SRT_ROTATE_Q, always
- * multiplied by sm_scale log2(e) and rounded once exactly as the forward
- * kernel forms its q, so the recomputed scores equal the forward's) and a
+ * for BF16 room for a copy of q ([B][Hq][Nq][D]: with SRT_ROTATE_Q, or a zero
+ * sm_scale, q rotated, multiplied by sm_scale log2(e) and rounded once exactly
+ * as the forward kernel forms its q; otherwise q is used as given, as the
+ * forward uses it, and the room stays unused), so the recomputed scores equal
+ * the forward's, and a
  * rotated copy of k ([B][Hkv][Nk][D], with SRT_ROTATE_K) and two scheduling
  * blocks (the run-time work assignment of srt_attn_prefill, for the dk/dv and
  * the dq kernel, zero-filled by each call), each region 256-byte aligned.  The
