@@ -109,9 +109,13 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
     return;
   }
 
-  // ---- q of the G heads: rotate at position seq-1, fold sm_scale*log2(e), pack to bf16 pairs
+  // ---- q of the G heads: rotate at position seq-1, fold sm_scale*log2(e), pack to bf16 pairs.
+  // A q that is not rotated stays exact (as the prefill kernel keeps it): it is
+  // packed as given and the dot products are scaled in fp32 instead, since a
+  // rounding of q * sm_scale*log2(e) would move each score by up to 2^-9 of it.
   const long long qpos = seq - 1;
-  const float qs = a.sm_scale * kLog2e;
+  const float qs_pre = a.table ? a.sm_scale * kLog2e : 1.f;
+  const float qs_post = a.table ? 1.f : a.sm_scale * kLog2e;
   uint32_t qp[G][8];       // [head][chunk c (0: dims 8sub.., 1: dims 64+8sub..) * 4 + pair-in-chunk]
   const uint4* qg = reinterpret_cast<const uint4*>(a.q);
 #pragma unroll
@@ -150,7 +154,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int p = 0; p < 4; ++p) qp[j][c * 4 + p] = pack2(x[c][2 * p] * qs, x[c][2 * p + 1] * qs);
+      for (int p = 0; p < 4; ++p) qp[j][c * 4 + p] = pack2(x[c][2 * p] * qs_pre, x[c][2 * p + 1] * qs_pre);
   }
 
   float m[G], l[G], acc[G][16];
@@ -190,7 +194,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
         float t = 0.f;
 #pragma unroll
         for (int p = 0; p < 8; ++p) t = dot2(qp[j][p], kk[p], t);
-        t = sum8_dpp(t);
+        t = sum8_dpp(t) * qs_post;
         s[j] = valid[u] ? t : -INFINITY;
       }
       const uint32_t vv[8] = {vw[u][0].x, vw[u][0].y, vw[u][0].z, vw[u][0].w,

@@ -49,3 +49,21 @@ def test_decode_one_split_and_many_splits():
     for splits in (1, 64, 200):
         o, l, ro, rl = _case(srt, 2, 4, 1, 2000, splits, seed=7)
         assert max_abs(o, ro) <= TOL and max_abs(l, rl) <= 1e-2
+
+
+def test_decode_given_q_is_exact_at_large_scores():
+    """Without a table q is used as given, exactly (the dot products are
+    scaled in fp32, as the prefill kernel does), so at sm_scale = 0.5 (scores
+    near 30 in log2 units) lse stays within fp32 accuracy of the oracle; a
+    bf16 rounding of q * sm_scale log2(e) would move it by about 2^-9 of the
+    score (~0.04)."""
+    srt = need_gpu()
+    B, Hq, Hkv, Nk, D = 2, 8, 2, 1500, 128
+    q = synth.randn((B, Hq, D), torch.bfloat16, 71, synth.Q_ID, "cuda")
+    k = synth.randn((B, Hkv, Nk, D), torch.bfloat16, 71, synth.K_ID, "cuda")
+    v = synth.randn((B, Hkv, Nk, D), torch.bfloat16, 71, synth.V_ID, "cuda")
+    o, l = srt.attn_decode_splitk(q, k, v, num_splits=16, sm_scale=0.5)
+    ro, rl = A.decode(f64(q), f64(k), f64(v), sm_scale=0.5)
+    print(f"max|err| O {max_abs(f64(o), ro):.3g} lse {max_abs(f64(l), rl):.3g}", flush=True)
+    assert max_abs(f64(l), rl) <= 1e-3
+    assert max_abs(f64(o), ro) <= TOL
