@@ -440,6 +440,10 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
         w[i] = pack2(p0, p1);
         part[half] += p0 + p1;
       }
+      // (an empty asm that reads the packed words keeps the conversions in
+      // the step's main block, among its MFMAs: otherwise they sink below the
+      // reference-move branch and run after the last MFMA of the step)
+      asm volatile("" :: "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]));
       pout[half] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
     }
     return part[0] + part[1];
