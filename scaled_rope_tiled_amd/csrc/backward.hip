@@ -519,7 +519,9 @@ __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) 
   const int sc = tid & 15, sr = tid >> 4;
   const uint32_t soff = sr * (kD * 2) + sc * 16;
   uint4 qb, ob;
-  float ldv = 0.f;           // wave 0: lane r < 32 -lse log2(e) of row r, lane 32 + r -delta of row r
+  // wave 0: lse (lanes r < 32) and delta (lanes 32 + r) of row r, raw; store()
+  // writes -lse log2(e) and -delta a step later, when the loads have landed
+  float lse_raw = 0.f, delta_raw = 0.f;
   // next tile to load: head ig of the group, row tile itq, first row hrow (all wave-uniform)
   int ig = 0, itq = t0;
   long long hrow = ((long long)b * a.Hq + hk * G) * a.Nq + (long long)t0 * 32;
@@ -528,9 +530,10 @@ __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) 
     qb = buffer_ld16(raw_buffer(qsrc + hrow * kD, rows * (kD * 2)), soff);
     ob = buffer_ld16(raw_buffer(dog + hrow * kD, rows * (kD * 2)), soff);
     if (wave == 0) {
-      const float* src = lane < 32 ? a.lse + hrow : a.delta + hrow;
-      const float x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(raw_buffer(src, rows * 4), l32 * 4, 0, 0));
-      ldv = lane < 32 ? x * (EXACT_Q ? -1.0f / a.sm_scale : -kLog2e) : -x;
+      // one descriptor per array (a per-lane choice of base would make the
+      // descriptor divergent: a waterfall loop and a wait for the data here)
+      lse_raw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(raw_buffer(a.lse + hrow, rows * 4), l32 * 4, 0, 0));
+      delta_raw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(raw_buffer(a.delta + hrow, rows * 4), l32 * 4, 0, 0));
     }
     hrow += 32;
     if (++itq == t0 + ntq) {
@@ -542,7 +545,7 @@ __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) 
   auto store = [&](int buf) {
     *reinterpret_cast<uint4*>(&sm.q[buf][sr * kTStr + sc * 8]) = qb;
     *reinterpret_cast<uint4*>(&sm.o[buf][sr * kTStr + sc * 8]) = ob;
-    if (wave == 0) sm.ld[buf][lane] = ldv;
+    if (wave == 0) sm.ld[buf][lane] = lane < 32 ? lse_raw * (EXACT_Q ? -1.0f / a.sm_scale : -kLog2e) : -delta_raw;
   };
   auto init_rows = [&](const float* src) {     // the 16 accumulator rows (queries) of this lane
     f32x16 c;
@@ -649,6 +652,9 @@ __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) 
         constexpr int R = decltype(rc)::value;
         store((R + 2) & 3);
         issue();
+        // (the loads stay here, a step ahead of the store that consumes them:
+        // left alone the scheduler sinks them to the end of the step)
+        __builtin_amdgcn_sched_barrier(0);
         if (dp_active) mma_rows1c(lds_off(&sm.o[R][l32 * kTStr + hl * 8]), breg, dp_out, init_rows(&sm.ld[R][32]));
         float ds[16];
 #pragma unroll
