@@ -639,8 +639,18 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
     float lse_row = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -INFINITY;
     const long long obase = ((long long)b * a.Hq + hq) * a.o_hstride + (long long)row * kD;
     float wa = 0.f;                 // weight of the running state (ring step)
-    const float* accp = nullptr;
+    f32x16 accv[4];                 // the running state's O, in the oacc layout
     if (a.acc_o) {
+      // every load of the running state is issued before any is used, so the
+      // epilogue waits for one round trip to memory instead of one per load
+      const float* accp = a.acc_o + ((long long)b * a.Hq + hq) * a.acc_hstride + (long long)row * kD;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 x = *reinterpret_cast<const float4*>(accp + db * 32 + g4 * 8 + hl * 4);
+          accv[db][g4 * 4 + 0] = x.x; accv[db][g4 * 4 + 1] = x.y; accv[db][g4 * 4 + 2] = x.z; accv[db][g4 * 4 + 3] = x.w;
+        }
       // fold this launch's (O, lse) into the running state by the log-sum-exp
       // rule: lse = log(e^la + e^lb), O = e^(la-lse) O_a + e^(lb-lse) O_b
       // ("8.3 长上下文技术" §8.3.5: a ring step rescales the running result)
@@ -655,7 +665,6 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
         inv *= eb * rs;
         lse_row = mx + __logf(ea + eb);
       }
-      accp = a.acc_o + ((long long)b * a.Hq + hq) * a.acc_hstride + (long long)row * kD;
     }
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -664,9 +673,9 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
         const int d = db * 32 + g4 * 8 + hl * 4;
         float o0 = oacc[db][g4 * 4 + 0] * inv, o1 = oacc[db][g4 * 4 + 1] * inv;
         float o2 = oacc[db][g4 * 4 + 2] * inv, o3 = oacc[db][g4 * 4 + 3] * inv;
-        if (accp) {
-          const float4 p = *reinterpret_cast<const float4*>(accp + d);
-          o0 = fmaf(wa, p.x, o0); o1 = fmaf(wa, p.y, o1); o2 = fmaf(wa, p.z, o2); o3 = fmaf(wa, p.w, o3);
+        if (a.acc_o) {
+          o0 = fmaf(wa, accv[db][g4 * 4 + 0], o0); o1 = fmaf(wa, accv[db][g4 * 4 + 1], o1);
+          o2 = fmaf(wa, accv[db][g4 * 4 + 2], o2); o3 = fmaf(wa, accv[db][g4 * 4 + 3], o3);
         }
         if (a.out_bf16) {
           *reinterpret_cast<uint2*>(reinterpret_cast<__hip_bfloat16*>(a.out) + obase + d) =
