@@ -117,7 +117,7 @@ def attention(q, k, v, *, sm_scale: float, causal: bool = True, q_pos0: int = 0,
                     qt = q[b, h, rr] if theta is None else rot(q[b, h, rr], qpos, theta, mscale)
                     s = sm_scale * (qt @ kt.T)                              # [r, Nk]
                     s = np.where(visible(qpos, kpos, causal=causal, window=window, sink=sink), s, -np.inf)
-                    M = s.max(axis=1)
+                    M = s.max(axis=1, initial=-np.inf)   # no key at all: every row sees none
                     ok = np.isfinite(M)
                     Ms = np.where(ok, M, 0.0)
                     p = np.exp(s - Ms[:, None])                            # exp(-inf) = 0

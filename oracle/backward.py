@@ -56,7 +56,7 @@ def attention_backward(q, k, v, dout, *, sm_scale: float, causal: bool = True, q
             for h in range(hk * g, (hk + 1) * g):
                 qt = q[b, h] if theta is None else rot(q[b, h], qpos, theta, mscale)
                 s = np.where(vis, sm_scale * (qt @ kt.T), -np.inf)
-                M = s.max(axis=1)
+                M = s.max(axis=1, initial=-np.inf)   # no key at all: every row sees none
                 ok = np.isfinite(M)
                 p = np.zeros_like(s)
                 p[ok] = np.exp(s[ok] - M[ok, None])

@@ -99,7 +99,7 @@ def _masked_attention(q, k, v, qpos, kpos, sm_scale, window, sink):
     for b in range(B):
         for h in range(Hq):
             s = np.where(vis, sm_scale * (q[b, h] @ k[b, h // g].T), -np.inf)
-            M = s.max(axis=1)
+            M = s.max(axis=1, initial=-np.inf)   # no key at all: every row sees none
             ok = np.isfinite(M)
             Ms = np.where(ok, M, 0.0)
             p = np.exp(s - Ms[:, None])

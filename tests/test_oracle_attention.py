@@ -304,3 +304,23 @@ def test_decode_window_equals_last_row():
         o, l = A.decode(q[:, :, -1], kc, v, sm_scale=0.25, theta=th, mscale=msc, window=W, sink=S)
         np.testing.assert_allclose(o, full_o[:, :, -1], atol=1e-12)
         np.testing.assert_allclose(l, full_l[:, :, -1], atol=1e-12)
+
+
+@pytest.mark.parametrize("window,sink", [(0, 0), (5, 2)])
+def test_empty_key_set_equals_invisible_keys(window, sink):
+    """Nk = 0 is the limit of a key set no row can see: every row has O = 0 and
+    lse = -inf (the convention for a row without a visible key), exactly what
+    keys placed after every query position give under the causal mask; the
+    backward of such rows is zero."""
+    from oracle import backward as BW
+    D = 8
+    q, k, v = _qkv(2, 4, 2, 9, 6, D)
+    th = rope.base_inv_freq(D, 1e4)
+    kw = dict(sm_scale=0.3, causal=True, theta=th, window=window, sink=sink, q_pos0=40)
+    o0, l0 = A.attention(q, k[:, :, :0], v[:, :, :0], **kw)
+    o1, l1 = A.attention(q, k, v, k_pos0=50, **kw)        # keys at 50.., queries at 40..48
+    assert o0.shape == q.shape and (o0 == 0).all() and np.isneginf(l0).all()
+    np.testing.assert_array_equal(o0, o1)
+    np.testing.assert_array_equal(l0, l1)
+    dq, dk, dv, _ = BW.attention_backward(q, k[:, :, :0], v[:, :, :0], np.ones_like(q), **kw)
+    assert (dq == 0).all() and dk.shape[2] == 0 and dv.shape[2] == 0
