@@ -235,3 +235,25 @@ def test_reference_far_below_zero_rotating_path(mode, causal):
     o, l = f64(o), f64(l)
     assert np.all(rl < -150)
     assert max_abs(o, ro) <= TOL and max_abs(l, rl) <= TOL
+
+
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float32, 64)], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("window,sink", [(0, 0), (8, 2)])
+@pytest.mark.parametrize("rotate", [True, False])
+def test_empty_key_set(dtype, D, window, sink, rotate):
+    """Nk = 0 with query rows: every row sees no key, so O = 0 and lse = -inf (the
+    oracle's convention), and the backward's dq is zero."""
+    srt = need_gpu()
+    q, k, v = qkv(2, 8, 2, 70, 0, D, dtype, 11)
+    table = device_table(srt, YARN_SMALL, D, 200)[0] if rotate else None
+    o, l = srt.attn_prefill(q, k, v, q_pos0=100, table=table, window=window, sink=sink)
+    th, ms, _ = oracle_freq(YARN_SMALL, D) if rotate else (None, 1.0, None)
+    ro, rl = A.attention(f64(q), f64(k), f64(v), sm_scale=1 / math.sqrt(D), q_pos0=100, theta=th, mscale=ms,
+                         window=window, sink=sink)
+    assert (f64(o) == 0).all() and np.isneginf(f64(l)).all()
+    np.testing.assert_array_equal(f64(o), ro)
+    np.testing.assert_array_equal(f64(l), rl)
+    do = synth.randn(q.shape, dtype, 11, synth.DO_ID, "cuda")
+    dq, dk, dv = srt.attn_backward(q, k, v, o, do, l, q_pos0=100, table=table, window=window, sink=sink)
+    torch.cuda.synchronize()
+    assert (dq == 0).all() and dk.numel() == 0 and dv.numel() == 0
