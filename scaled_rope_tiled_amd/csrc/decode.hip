@@ -268,19 +268,58 @@ __global__ void __launch_bounds__(kThreads, 2) decode_split_kernel(DecodeArgs a)
 }
 
 // Merge the `splits` partial states of one (b, h): lse-weighted average.
-__global__ void __launch_bounds__(128) decode_combine_kernel(DecodeArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+// Thread (d, part) folds the splits s = part, part + kCombineParts, ... of
+// dimension d into a running (m, l, o) state, with eight splits' loads in
+// flight at a time, and the kCombineParts states of each d are merged through
+// LDS: the splits are read in a few round trips instead of one loop
+// iteration after another.
+constexpr int kCombineParts = 4;
+__global__ void __launch_bounds__(kD * kCombineParts) decode_combine_kernel(DecodeArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int d = tid % kD, part = tid / kD;
   const long long bh = (long long)b * a.Hq + h;
   const float* pl = a.ws_lse + bh * a.splits;
   const float* po = a.ws_o + bh * a.splits * kD;
+  float m = -INFINITY, l = 0.f, o = 0.f;
+  for (int s0 = part; s0 < a.splits; s0 += 8 * kCombineParts) {
+    float ls[8], os[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = s0 + u * kCombineParts;
+      ls[u] = s < a.splits ? pl[s] : -INFINITY;
+      os[u] = s < a.splits ? po[(long long)s * kD + d] : 0.f;
+    }
+    float mn = m;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) mn = fmaxf(mn, ls[u]);
+    if (mn != -INFINITY) {
+      const float sc = __expf(m - mn);                  // m = -inf: exp(-inf) = 0, and l = o = 0 anyway
+      l *= sc;
+      o *= sc;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float w = __expf(ls[u] - mn);             // an empty split (lse = -inf) weighs 0
+        l += w;
+        o = fmaf(w, os[u], o);
+      }
+      m = mn;
+    }
+  }
+  __shared__ float sm_m[kCombineParts], sm_l[kCombineParts], sm_o[kCombineParts][kD];
+  if (d == 0) { sm_m[part] = m; sm_l[part] = l; }
+  sm_o[part][d] = o;
+  __syncthreads();
+  if (part != 0) return;
   float M = -INFINITY;
-  for (int s = 0; s < a.splits; ++s) M = fmaxf(M, pl[s]);
+#pragma unroll
+  for (int p = 0; p < kCombineParts; ++p) M = fmaxf(M, sm_m[p]);
   float L = 0.f, O = 0.f;
   if (M != -INFINITY) {
-    for (int s = 0; s < a.splits; ++s) {
-      const float w = __expf(pl[s] - M);
-      L += w;
-      O = fmaf(w, po[(long long)s * kD + d], O);
+#pragma unroll
+    for (int p = 0; p < kCombineParts; ++p) {
+      const float w = __expf(sm_m[p] - M);
+      L += w * sm_l[p];
+      O = fmaf(w, sm_o[p][d], O);
     }
   }
   reinterpret_cast<__hip_bfloat16*>(a.out)[bh * kD + d] = __float2bfloat16(L > 0.f ? O / L : 0.f);
@@ -338,7 +377,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(a.Hq, a.B), dim3(kD), 0, stream, a);
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(a.Hq, a.B), dim3(kD * kCombineParts), 0, stream, a);
   return hipGetLastError();
 }
 
