@@ -292,7 +292,13 @@ constexpr int kD = 128;
 // and 320 B the transposing reads; no stride does both.  Tiles read both ways
 // use 304 B (row reads conflict-free, transposing reads two-way in part):
 // storing such a tile twice, once per stride, measured slower.
-constexpr int kTStr = kD + 24;    // 304 B: tiles read as rows and transposed
+// Tiles read both as 16-byte row chunks and with the transposing read: 272-byte
+// rows, the 32 rows of a tile permuted, row r in slot prow(r) = (r & 16) +
+// 4 (r & 3) + ((r >> 2) & 3).  The 16 rows of one row read then fall on 16
+// distinct 16-byte bank groups and the 4 rows of one transposing read on the 4
+// disjoint 64-byte quarters of the banks.
+constexpr int kTStr = kD + 8;
+__device__ constexpr int prow(int r) { return (r & 16) + 4 * (r & 3) + ((r >> 2) & 3); }
 constexpr int kRStr = kD + 8;     // 272 B: tiles read only as 16-byte row chunks
 
 // Load 8 d-chunks of one row (d = ks * 16 + hl * 8 + 0..7) and rotate them
@@ -345,7 +351,7 @@ __device__ inline void mma_tr(f32x16 (&acc)[4], uint32_t x_lane, const bf16x8 (&
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const i16x4 lo = lds_read_tr(x_lane + ((half * 16) * kTStr + db * 32) * 2);
-      const i16x4 hi = lds_read_tr(x_lane + ((half * 16 + 8) * kTStr + db * 32) * 2);
+      const i16x4 hi = lds_read_tr(x_lane + ((half * 16 + 2) * kTStr + db * 32) * 2);   // rows + 8: slots + 2
       const bf16x8 xa = __builtin_bit_cast(
           bf16x8, (__attribute__((__vector_size__(8 * sizeof(short)))) short){lo[0], lo[1], lo[2], lo[3], hi[0],
                                                                              hi[1], hi[2], hi[3]});
@@ -543,8 +549,8 @@ __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) 
     }
   };
   auto store = [&](int buf) {
-    *reinterpret_cast<uint4*>(&sm.q[buf][sr * kTStr + sc * 8]) = qb;
-    *reinterpret_cast<uint4*>(&sm.o[buf][sr * kTStr + sc * 8]) = ob;
+    *reinterpret_cast<uint4*>(&sm.q[buf][prow(sr) * kTStr + sc * 8]) = qb;
+    *reinterpret_cast<uint4*>(&sm.o[buf][prow(sr) * kTStr + sc * 8]) = ob;
     if (wave == 0) sm.ld[buf][lane] = lane < 32 ? lse_raw * (EXACT_Q ? -1.0f / a.sm_scale : -kLog2e) : -delta_raw;
   };
   auto init_rows = [&](const float* src) {     // the 16 accumulator rows (queries) of this lane
@@ -559,7 +565,7 @@ __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) 
 
   const int gj = lane & 15;
   const int gd = ((lane >> 4) & 1) * 16 + 4 * (gj & 3);
-  const int tr_off = (hl * 4 + (gj >> 2)) * kTStr + gd;
+  const int tr_off = prow(hl * 4 + (gj >> 2)) * kTStr + gd;
   bf16x8 breg[8];            // P waves: k~ (scaled); dS waves: v
   f32x16 acc[4];             // P waves: dV^T; dS waves: dK~^T
 #pragma unroll
@@ -598,7 +604,7 @@ __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) 
       const int tm_lo = (int)max((long long)INT_MIN, min((long long)INT_MAX, tlo));
       const int tm_hi = (int)max((long long)INT_MIN, min((long long)INT_MAX, thi));
       f32x16 s_a, s_b;
-      mma_rows1c(lds_off(&sm.q[0][l32 * kTStr + hl * 8]), breg, s_a, init_rows(&sm.ld[0][0]));
+      mma_rows1c(lds_off(&sm.q[0][prow(l32) * kTStr + hl * 8]), breg, s_a, init_rows(&sm.ld[0][0]));
       int ct = t0;
       // step i = R (mod 4) on tile i: S(i+1) into s_out next to P(i) from s_in
       auto pstep = [&](auto rc, const f32x16& s_in, f32x16& s_out) {
@@ -606,7 +612,7 @@ __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) 
         constexpr int nb = (R + 1) & 3;
         store((R + 2) & 3);
         issue();
-        mma_rows1c(lds_off(&sm.q[nb][l32 * kTStr + hl * 8]), breg, s_out, init_rows(&sm.ld[nb][0]));   // stale past the end
+        mma_rows1c(lds_off(&sm.q[nb][prow(l32) * kTStr + hl * 8]), breg, s_out, init_rows(&sm.ld[nb][0]));   // stale past the end
         float p[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) p[j] = __builtin_amdgcn_exp2f(EXACT_Q ? s_in[j] * cq : s_in[j]);
@@ -655,7 +661,7 @@ __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) 
         // (the loads stay here, a step ahead of the store that consumes them:
         // left alone the scheduler sinks them to the end of the step)
         __builtin_amdgcn_sched_barrier(0);
-        if (dp_active) mma_rows1c(lds_off(&sm.o[R][l32 * kTStr + hl * 8]), breg, dp_out, init_rows(&sm.ld[R][32]));
+        if (dp_active) mma_rows1c(lds_off(&sm.o[R][prow(l32) * kTStr + hl * 8]), breg, dp_out, init_rows(&sm.ld[R][32]));
         float ds[16];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -674,7 +680,7 @@ __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) 
       // step 0: dP(0) only
       store(2);
       issue();
-      mma_rows1c(lds_off(&sm.o[0][l32 * kTStr + hl * 8]), breg, dp_a, init_rows(&sm.ld[0][32]));
+      mma_rows1c(lds_off(&sm.o[0][prow(l32) * kTStr + hl * 8]), breg, dp_a, init_rows(&sm.ld[0][32]));
       __syncthreads();
       int i = 1;
       for (; i + 3 < nit; i += 4) {
@@ -821,15 +827,15 @@ __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_bf16_kernel(BwdArgs a) {
   auto store = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      *reinterpret_cast<uint4*>(&sm.k[buf][(sr + 16 * i) * kTStr + sc * 8]) = kb[i];
+      *reinterpret_cast<uint4*>(&sm.k[buf][prow(sr + 16 * i) * kTStr + sc * 8]) = kb[i];
       *reinterpret_cast<uint4*>(&sm.v[buf][(sr + 16 * i) * kRStr + sc * 8]) = vb[i];
     }
   };
   const int gj = lane & 15;
   const int gd = ((lane >> 4) & 1) * 16 + 4 * (gj & 3);
-  const uint32_t k_row = lds_off(&sm.k[0][l32 * kTStr + hl * 8]);
+  const uint32_t k_row = lds_off(&sm.k[0][prow(l32) * kTStr + hl * 8]);
   const uint32_t v_row = lds_off(&sm.v[0][l32 * kRStr + hl * 8]);
-  const uint32_t k_tr = lds_off(&sm.k[0][(hl * 4 + (gj >> 2)) * kTStr + gd]);
+  const uint32_t k_tr = lds_off(&sm.k[0][prow(hl * 4 + (gj >> 2)) * kTStr + gd]);
   constexpr uint32_t kKBuf = 32 * kTStr * 2, kVBuf = 32 * kRStr * 2;
 
   // One 32-key tile in LDS buffer BUF (a compile-time constant: the loop takes
