@@ -13,8 +13,8 @@
 // of one KV head and walks the query tiles of every query head of its GQA
 // group that can see them; half its waves produce P and dV, the other half
 // dS and dK, exchanging P through LDS) and dq (a workgroup owns query rows,
-// like the forward kernel, and walks the visible key tiles; two workgroups
-// per CU).
+// like the forward kernel, and walks the visible key tiles; 8 waves, one
+// workgroup per CU, every staged k/v tile serving all of them).
 // The entry point rotates q and k once into its workspace, so the tiles the
 // kernels stage need no rotation (every key block would otherwise rotate each
 // q tile again, and every query block each k tile).  bf16 kernels (D = 128)
@@ -704,13 +704,13 @@ __global__ void __launch_bounds__(kKV2Threads) bwd_dkdv2_bf16_kernel(BwdArgs a) 
   else store_grad<HALF>(a.dk + krow * kD, acc, EXACT_Q ? a.sm_scale : kLn2, (a.rope_flags & 2) != 0, tab2, kpos, hl);
 }
 
-// ---- dq: a workgroup of 4 waves owns one KV head and 32 * (4 / HPW) query
+// ---- dq: a workgroup of 8 waves owns one KV head and 32 * (8 / HPW) query
 // rows of HPW = min(G, 4) query heads (as the forward kernel); wave w holds
 // rotated q (pre-multiplied by sm_scale log2(e), as in the forward) and dO of
 // its 32 rows in registers and walks 32-key tiles of rotated k and v staged in
 // LDS.  The S^T accumulator starts at -lse log2(e) and the dP^T accumulator at
 // -delta, so P = exp2(S^T) and dS = P (dP - delta) = P dP^T.
-constexpr int kQWaves = 4;
+constexpr int kQWaves = 8;
 constexpr int kQThreads = 64 * kQWaves;
 
 struct DqSmem {
@@ -719,7 +719,7 @@ struct DqSmem {
 };
 
 template <bool HALF, bool WIN, bool EXACT_Q>
-__global__ void __launch_bounds__(kQThreads, 2) bwd_dq_bf16_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(kQThreads, 1) bwd_dq_bf16_kernel(BwdArgs a) {
   __shared__ DqSmem sm;
   __shared__ int s_item;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -806,29 +806,31 @@ __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_bf16_kernel(BwdArgs a) {
     klo = (int)(lo > (1LL << 30) ? (1LL << 30) : lo);
   }
 
-  // staging: thread t moves 16-byte chunk t & 15 of rows t >> 4 and (t >> 4) + 16
-  // of a k and a v tile (16 threads per 256-byte row), through buffer
-  // descriptors whose range ends at Nk (rows past it read as zero)
+  // staging: thread t moves 16-byte chunk t & 15 of row t >> 4 of a k and a v
+  // tile (16 threads per 256-byte row; with fewer than 512 threads also rows
+  // (t >> 4) + kQThreads / 16, ...), through buffer descriptors whose range
+  // ends at Nk (rows past it read as zero)
   const __hip_bfloat16* ksrc =
       a.k_rot ? reinterpret_cast<const __hip_bfloat16*>(a.k_rot) + ((long long)b * a.Hkv + hk) * a.Nk * kD : kg;
   const int sc = tid & 15, sr = tid >> 4;
   const uint32_t soff = sr * (kD * 2) + sc * 16;
-  uint4 kb[2], vb[2];
+  constexpr int kStg = 32 / (kQThreads / 16);     // rows per thread of a 32-row tile
+  uint4 kb[kStg], vb[kStg];
   auto issue = [&](int key0) {
     const int bytes = min(32, max(0, a.Nk - key0)) * (kD * 2);
     const __amdgpu_buffer_rsrc_t rk = raw_buffer(ksrc + (long long)key0 * kD, bytes);
     const __amdgpu_buffer_rsrc_t rv = raw_buffer(vg + (long long)key0 * kD, bytes);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      kb[i] = buffer_ld16(rk, soff + i * 16 * (kD * 2));
-      vb[i] = buffer_ld16(rv, soff + i * 16 * (kD * 2));
+    for (int i = 0; i < kStg; ++i) {
+      kb[i] = buffer_ld16(rk, soff + i * (kQThreads / 16) * (kD * 2));
+      vb[i] = buffer_ld16(rv, soff + i * (kQThreads / 16) * (kD * 2));
     }
   };
   auto store = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      *reinterpret_cast<uint4*>(&sm.k[buf][prow(sr + 16 * i) * kTStr + sc * 8]) = kb[i];
-      *reinterpret_cast<uint4*>(&sm.v[buf][(sr + 16 * i) * kRStr + sc * 8]) = vb[i];
+    for (int i = 0; i < kStg; ++i) {
+      *reinterpret_cast<uint4*>(&sm.k[buf][prow(sr + (kQThreads / 16) * i) * kTStr + sc * 8]) = kb[i];
+      *reinterpret_cast<uint4*>(&sm.v[buf][(sr + (kQThreads / 16) * i) * kRStr + sc * 8]) = vb[i];
     }
   };
   const int gj = lane & 15;
@@ -987,8 +989,8 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    if (a.sched && nq > 4LL * compute_units() && nq <= kMaxLaunchItems)
-      aq.sched = a.sched + kSchedBlockWords;   // (two workgroups per CU)
+    if (a.sched && nq > 2LL * compute_units() && nq <= kMaxLaunchItems)
+      aq.sched = a.sched + kSchedBlockWords;
     pick(q_kernel);
     return hipGetLastError();
   }

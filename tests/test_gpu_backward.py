@@ -97,7 +97,8 @@ def test_backward_bf16_group_sizes(G):
 
 
 @pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
-@pytest.mark.parametrize("G,Nq", [(1, 1), (1, 32), (1, 64), (1, 96), (1, 128), (1, 160), (2, 96), (2, 160), (4, 33)])
+@pytest.mark.parametrize("G,Nq", [(1, 1), (1, 32), (1, 64), (1, 96), (1, 128), (1, 160), (2, 96), (2, 160), (4, 33),
+                                  (4, 96), (4, 161), (8, 96)])
 def test_backward_bf16_tile_counts(G, Nq, causal):
     """Every residue of the query-tile count a dk/dv workgroup walks (1 to 5
     tiles of one head, several heads), including a single query row."""
