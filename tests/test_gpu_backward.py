@@ -173,6 +173,45 @@ def test_backward_yarn_32k_full_size_sampled():
     assert worst <= 2e-2
 
 
+def test_backward_window_sinks_two_batches_sampled():
+    """A window of 512 keys with 4 sinks at GQA 32/8, two batches of 4096 (so both kernels take their items
+    through the run-time queues): dq at sampled rows of every query head of the first and last KV group of
+    each batch, dk and dv at the keys just past the sinks and at the last keys, against the oracle at those
+    entries."""
+    srt = need_gpu()
+    B, Hq, Hkv, N, D, W, S = 2, 32, 8, 4096, 128, 512, 4
+    G = Hq // Hkv
+    rope = synth.WORKLOADS["yarn_32k_bf16"].rope
+    q, k, v = qkv(B, Hq, Hkv, N, N, D, torch.bfloat16, 57)
+    do = synth.randn((B, Hq, N, D), torch.bfloat16, 57, synth.DO_ID, "cuda")
+    table, _ = device_table(srt, rope, D, N)
+    out, lse = srt.attn_prefill(q, k, v, table=table, window=W, sink=S)
+    dq, dk, dv = srt.attn_backward(q, k, v, out, do, lse, table=table, window=W, sink=S)
+    torch.cuda.synchronize()
+    th, ms, _ = oracle_freq(rope, D)
+    rng = np.random.default_rng(57)
+    rows = np.unique(np.concatenate([[0, 3, 4, 31, 32, 63, 64, W - 1, W, W + 1, W + 4, 2047, N - 2, N - 1],
+                                     rng.integers(0, N, 6)]))
+    keys = np.concatenate([np.arange(S, S + 8), np.arange(N - 16, N)])
+    worst = 0.0
+    for b in range(B):
+        for hk in (0, Hkv - 1):
+            hs = slice(hk * G, (hk + 1) * G)
+            rdq, rdk, rdv = BW.attention_backward_sampled(
+                f64(q[:, hs]), f64(k[:, hk:hk + 1]), f64(v[:, hk:hk + 1]), f64(do[:, hs]), hk=0, rows=rows,
+                keys=keys, sm_scale=1 / math.sqrt(D), theta=th, mscale=ms, window=W, sink=S, b=b)
+            got_dq = f64(dq[b, hs][:, torch.as_tensor(rows, device="cuda")])
+            got_dk = f64(dk[b, hk][torch.as_tensor(keys, device="cuda")])
+            got_dv = f64(dv[b, hk][torch.as_tensor(keys, device="cuda")])
+            for name, g, r in (("dq", got_dq, rdq), ("dk", got_dk, rdk), ("dv", got_dv, rdv)):
+                scale = max(1.0, float(np.abs(r).max())) if name == "dq" else float(np.abs(r).max())
+                e = max_abs(g, r) / scale
+                print(f"window b {b} kv head {hk} {name}: max|err| {max_abs(g, r):.3g} max|ref| {np.abs(r).max():.3g}",
+                      flush=True)
+                worst = max(worst, e)
+    assert worst <= 2e-2
+
+
 @pytest.mark.parametrize("rotate", [False, True], ids=["given", "rotated"])
 def test_backward_recomputes_the_forward_softmax(rotate):
     """With a one-key window every query sees only its own position, so the
