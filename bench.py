@@ -25,6 +25,9 @@ same line carries:
     ring device's query run, against the 8 TB/s HBM peak;
   * ``window``: the same prefill with a 4096-key sliding window and 4 sink
     tokens (flops of the kept pairs only), and its time against full causal;
+  * ``half_pairs``: the same prefill with half-split pairs (x_i, x_i+D/2)
+    for K's rotation and q's rotation on load, and its time against the
+    interleaved pairs of the headline;
   * ``backward``: dq, dk, dv of the same prefill, TFLOP/s of the five
     backward products;
   * ``gqa_8k``: the GQA 8K prefill (B=1, 32/8 heads, D=128, N=8192, base
@@ -223,7 +226,40 @@ def bench_window(srt, torch, w, window, sink, steps, warmup, full_kernel_ms):
             "kernel_ms": round(kernel_ms, 4), "alg_flops_per_launch": flops,
             "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
             "work_vs_full_causal": round(pairs / causal_pairs(w.N, w.N), 4),
-            "time_vs_full_causal": round(kernel_ms / full_kernel_ms, 4)}
+            "time_vs_full_causal": round(kernel_ms / full_kernel_ms, 4) if full_kernel_ms else None}
+
+
+def bench_half_pairs(srt, torch, w, steps, warmup, full_kernel_ms):
+    """The prefill workload with half-split pairs (x_i, x_i+D/2): K rotated once with that pairing and q
+    rotated on load with it.  The other frequency-step variants (Dynamic NTK, per-pair factor tables) only
+    change the host-built table, not what the kernels do."""
+    import synth
+    D = w.D
+    q = synth.randn((w.B, w.Hq, w.N, D), torch.bfloat16, w.seed, synth.Q_ID, "cuda")
+    k = synth.randn((w.B, w.Hkv, w.N, D), torch.bfloat16, w.seed, synth.K_ID, "cuda")
+    v = synth.randn((w.B, w.Hkv, w.N, D), torch.bfloat16, w.seed, synth.V_ID, "cuda")
+    rp = w.rope
+    th, ms, _ = srt.rope_inv_freq(rp.method, rp.base, rp.s, rp.L, rp.alpha, rp.beta, D)
+    table = srt.rope_cos_sin(th, D, ms, w.N, "cuda")
+    krot = srt.rope_apply(k, table, pairing="half")
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device="cuda")
+    kt = Timer(torch)
+    fn = lambda: srt.attn_prefill(q, krot, v, table=table, rope_flags=srt.ROTATE_Q | srt.PAIR_HALF, out=out,
+                                  lse=lse)
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        kt.run(fn)
+    torch.cuda.synchronize()
+    kernel_ms = kt.mean_ms()
+    flops = 4.0 * D * w.B * w.Hq * causal_pairs(w.N, w.N)
+    tf = flops / (kernel_ms * 1e-3) / 1e12
+    return {"workload": f"{w.name} with half-split pairs", "unit": "TFLOP/s", "value": round(tf, 2),
+            "kernel_ms": round(kernel_ms, 4), "alg_flops_per_launch": flops,
+            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "time_vs_interleaved": round(kernel_ms / full_kernel_ms, 4) if full_kernel_ms else None}
 
 
 # ----------------------------------------------------------------------------- backward
@@ -587,7 +623,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=24.0,
                     help="seconds of oracle time over all legs (split among them)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
-    ap.add_argument("--only", choices=["decode", "ring", "window", "backward", "gqa_8k", "merge"], default=None,
+    ap.add_argument("--only", choices=["decode", "ring", "window", "half_pairs", "backward", "gqa_8k", "merge"],
+                    default=None,
                     help="run one extra leg alone and print its JSON (for profiling that leg's kernels)")
     args = ap.parse_args()
 
@@ -628,7 +665,9 @@ def main():
         elif args.only == "ring":
             r = bench_ring(srt, torch, synth.WORKLOADS["ntk_128k_ring_bf16"], args.steps, args.warmup)
         elif args.only == "window":
-            r = bench_window(srt, torch, w, 4096, 4, args.steps, args.warmup, float("nan"))
+            r = bench_window(srt, torch, w, 4096, 4, args.steps, args.warmup, None)
+        elif args.only == "half_pairs":
+            r = bench_half_pairs(srt, torch, w, args.steps, args.warmup, None)
         elif args.only == "merge":
             r = bench_merge(srt, torch, synth.WORKLOADS["ntk_128k_ring_bf16"], args.steps, args.warmup)
         elif args.only == "gqa_8k":
@@ -672,6 +711,8 @@ def main():
         line["merge"] = bench_merge(srt, torch, synth.WORKLOADS["ntk_128k_ring_bf16"], args.steps, args.warmup)
         torch.cuda.empty_cache()
         line["window"] = bench_window(srt, torch, w, 4096, 4, args.steps, args.warmup, p["kernel_ms"])
+        torch.cuda.empty_cache()
+        line["half_pairs"] = bench_half_pairs(srt, torch, w, args.steps, args.warmup, p["kernel_ms"])
         torch.cuda.empty_cache()
         line["backward"] = bench_backward(srt, torch, w, max(3, args.steps // 4), 1)
         torch.cuda.empty_cache()
