@@ -75,9 +75,10 @@ def test_backward_fp32(kw):
 @pytest.mark.parametrize("kw", [dict(), dict(half=True), dict(window=100, sink=4), dict(window=70, sink=90),
                                 dict(q_pos0=300, k_pos0=340, Nq=130, Nk=257), dict(causal=False),
                                 dict(rotate=False), dict(B=2, Nq=64, Nk=64), dict(sm_scale=0.03),
-                                dict(sm_scale=0.2, rotate=False, Nq=96, Nk=96)],
+                                dict(sm_scale=0.2, rotate=False, Nq=96, Nk=96),
+                                dict(window=64, sink=5, q_pos0=200, k_pos0=0, Nq=170, Nk=370, half=True)],
                          ids=["plain", "half", "window", "wide_sink", "offsets", "noncausal", "given", "batch",
-                              "scale_small", "scale_large_given"])
+                              "scale_small", "scale_large_given", "window_offsets_half"])
 def test_backward_bf16(kw):
     srt = need_gpu()
     base = dict(Nq=300, Nk=300)
