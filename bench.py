@@ -13,7 +13,8 @@ the kernel instead).  Inputs are resident in HBM before timing starts.  The
 same line carries:
 
   * ``roofline``: the prefill kernel's algorithmic flops / its mean launch
-    time (HIP events on the launch stream) against the bf16 dense MFMA peak,
+    time (HIP events on the launch stream; the median and the fastest launch
+    beside it) against the bf16 dense MFMA peak,
     plus HBM traffic from committed rocprofv3 counters when they were taken
     on the current kernel source (else null);
   * ``decode``: 128K split-K decode (B=16, GQA 32/8, PI s=16, 64 splits):
@@ -122,8 +123,18 @@ class Timer:
         self.pairs.append((e0, e1))
         return r
 
+    def times_ms(self):
+        return sorted(a.elapsed_time(b) for a, b in self.pairs)
+
     def mean_ms(self):
         return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
+
+    def median_min_ms(self):
+        t = self.times_ms()
+        if not t:
+            return None, None
+        med = t[len(t) // 2] if len(t) % 2 else 0.5 * (t[len(t) // 2 - 1] + t[len(t) // 2])
+        return med, t[0]
 
 
 # ----------------------------------------------------------------------------- prefill (headline)
@@ -172,7 +183,9 @@ def bench_prefill(srt, torch, w, steps, warmup, prerotate_k=False):
     ms_step = (time.perf_counter() - t0) * 1e3 / steps
     flops = prefill_flops(w.B, w.Hq, w.N, w.N, D)
     kernel_ms = kt.mean_ms()
-    return {"flops": flops, "ms_per_step": ms_step, "kernel_ms": kernel_ms,
+    med, mn = kt.median_min_ms()
+    return {"flops": flops, "ms_per_step": ms_step, "kernel_ms": kernel_ms, "kernel_ms_median": med,
+            "kernel_ms_min": mn,
             "tflops_step": flops / (ms_step * 1e-3) / 1e12, "tflops_kernel": flops / (kernel_ms * 1e-3) / 1e12}
 
 
@@ -336,10 +349,12 @@ def bench_decode(srt, torch, w, steps, warmup):
     ws_bytes = w.B * w.Hq * w.splits * (D + 1) * 4.0
     alg = kv + w.B * w.Hq * D * 2 * 2 + w.B * w.Hq * 4 + 2 * ws_bytes
     kernel_ms = kt.mean_ms()
+    med, mn = kt.median_min_ms()
     gbs = alg / (kernel_ms * 1e-3) / 1e9
     del k, v
     return {"workload": w.name, "unit": "GB/s", "value": round(gbs, 1), "ms_per_step": round(ms_step, 4),
-            "kernel_ms": round(kernel_ms, 4), "alg_bytes": alg,
+            "kernel_ms": round(kernel_ms, 4), "kernel_ms_median": round(med, 4), "kernel_ms_min": round(mn, 4),
+            "alg_bytes": alg,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4)},
             "cache_build_ms": round(cache_ms, 3)}
@@ -607,6 +622,7 @@ def prefill_leg(p, w, traffic=None, mfma_util=None, traffic_note=None):
             "traffic": traffic, "traffic_note": traffic_note,
             "mfma_busy_from_counters": None if mfma_util is None else round(mfma_util, 4),
             "kernel": "prefill_bf16_kernel", "kernel_ms": round(p["kernel_ms"], 4),
+            "kernel_ms_median": round(p["kernel_ms_median"], 4), "kernel_ms_min": round(p["kernel_ms_min"], 4),
             "alg_flops_per_launch": p["flops"]}
 
 
